@@ -1,0 +1,215 @@
+"""Seeded synthetic workloads for paged decode attention.
+
+This module draws the random inputs only: context-length mixes, the order of
+the physical-block free list, and the q / K / V values. It holds none of the
+attention arithmetic and none of the block bookkeeping: block tables, slots
+and copy-on-write pairs come from whatever block manager the caller passes
+in (the library's native manager in the benchmark, the oracle's in tests), so
+both sides of every parity check read inputs from one generator.
+
+Workloads (lengths, seeds and draw order are fixed here):
+
+  tiny  fp32, 4 seqs, 8 heads (MHA), head_dim 64, contexts {1, 17, 100, 250},
+        a 64-block pool handed out in a seeded random order.        seed 0
+  7b    bf16, 64 seqs, 32/32 heads, head_dim 128, contexts U[128, 2048],
+        pool = used blocks + 10% free.                              seed 1
+  13b   bf16, 128 seqs, 40/40 heads, head_dim 128, contexts lognormal
+        (median 500, sigma 0.7 in log space) clipped to [16, 2048].  seed 2
+  gqa   bf16, 16 seqs, 64 q heads / 8 kv heads, head_dim 128, contexts
+        U[8192, 32768], 512-token partitions.                      seed 3
+  cow   bf16, 16 prompts x 8 samples, 32 heads, head_dim 128. Prompt length
+        1024 - r, r ~ U{1..15} (so the last prompt block is partly filled and
+        shared by 8 samples); each sample then gets a private tail of
+        U{1..256} tokens.                                           seed 4
+
+Draw order for a seed: lengths -> free-list permutation -> q -> K pool ->
+V pool -> new K -> new V. Values are N(0, 1) in fp32, rounded to the
+workload's element type by torch (round to nearest even for bf16).
+
+Every workload has one decode step: each sequence's last token is appended
+(through the block manager) and written with the step's new K/V, then all
+sequences attend over their full context. For `cow`, the step's appended
+tokens are the samples' whole tails, so the step carries the copy-on-write
+copies of the shared, partly filled prompt blocks.
+"""
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass
+class Spec:
+    name: str
+    dtype: str                 # "f32" | "bf16"
+    B: int                     # sequences (cow: prompts * samples)
+    Hq: int
+    Hkv: int
+    D: int
+    seed: int
+    lengths: tuple             # ("fixed", [..]) | ("uniform", lo, hi) | ("lognormal", median, sigma, lo, hi)
+    pool_blocks: int = 0       # fixed pool size; 0 = used blocks + pool_slack
+    pool_slack: float = 0.10
+    partition: int = 0         # tokens per split-context partition the benchmark uses (0 = none)
+    bs: int = 16
+    cow: dict = field(default_factory=dict)  # prompts, samples, prompt_len, r_max, tail_lo, tail_hi
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.D)
+
+
+CONFIGS = {
+    "tiny": Spec("tiny", "f32", 4, 8, 8, 64, seed=0, lengths=("fixed", [1, 17, 100, 250]),
+                 pool_blocks=64),
+    "7b": Spec("7b", "bf16", 64, 32, 32, 128, seed=1, lengths=("uniform", 128, 2048)),
+    "13b": Spec("13b", "bf16", 128, 40, 40, 128, seed=2, lengths=("lognormal", 500.0, 0.7, 16, 2048)),
+    "gqa": Spec("gqa", "bf16", 16, 64, 8, 128, seed=3, lengths=("uniform", 8192, 32768), partition=512),
+    "cow": Spec("cow", "bf16", 128, 32, 32, 128, seed=4, lengths=("cow",),
+                cow=dict(prompts=16, samples=8, prompt_len=1024, r_max=15, tail_lo=1, tail_hi=256)),
+}
+
+
+def torch_dtype(spec):
+    return torch.float32 if spec.dtype == "f32" else torch.bfloat16
+
+
+def draw_lengths(spec, rng):
+    """Final context lengths (history + the step's tokens), int64 [B].
+
+    For cow also returns (prompt_lens [prompts], tail_lens [B])."""
+    kind = spec.lengths[0]
+    if kind == "fixed":
+        ctx = np.asarray(spec.lengths[1], dtype=np.int64)
+        assert ctx.shape == (spec.B,)
+        return ctx, None
+    if kind == "uniform":
+        lo, hi = spec.lengths[1], spec.lengths[2]
+        return rng.integers(lo, hi, size=spec.B, endpoint=True).astype(np.int64), None
+    if kind == "lognormal":
+        med, sigma, lo, hi = spec.lengths[1:]
+        raw = np.exp(rng.normal(math.log(med), sigma, size=spec.B))
+        return np.clip(np.rint(raw), lo, hi).astype(np.int64), None
+    if kind == "cow":
+        c = spec.cow
+        r = rng.integers(1, c["r_max"], size=c["prompts"], endpoint=True)
+        prompt = c["prompt_len"] - r
+        tails = rng.integers(c["tail_lo"], c["tail_hi"], size=c["prompts"] * c["samples"], endpoint=True)
+        ctx = np.repeat(prompt, c["samples"]) + tails
+        return ctx.astype(np.int64), (prompt.astype(np.int64), tails.astype(np.int64))
+    raise ValueError(kind)
+
+
+def _populate(spec, bm, ctx, cow_parts):
+    """Drive a block manager through the workload's history and its step.
+
+    Returns seq ids, the step's slots, the step's (src, dst) copy pairs and
+    the per-slot token index into the step's new K/V rows.
+    """
+    seqs = []
+    step_slots = []
+    step_pairs = []
+    if cow_parts is None:
+        for s in range(spec.B):
+            sid = bm.add_seq()
+            seqs.append(sid)
+            bm.append(sid, int(ctx[s]) - 1)          # history (untimed)
+        for sid in seqs:
+            slots, pairs = bm.append(sid, 1)          # the step's token
+            step_slots.extend(slots)
+            step_pairs.extend(pairs)
+    else:
+        prompt, tails = cow_parts
+        c = spec.cow
+        for p in range(c["prompts"]):
+            parent = bm.add_seq()
+            bm.append(parent, int(prompt[p]))          # prompt prefill (untimed)
+            group = [parent] + [bm.fork(parent) for _ in range(c["samples"] - 1)]
+            seqs.extend(group)
+        for i, sid in enumerate(seqs):
+            slots, pairs = bm.append(sid, int(tails[i]))   # divergent tails
+            step_slots.extend(slots)
+            step_pairs.extend(pairs)
+    return seqs, step_slots, step_pairs
+
+
+@dataclass
+class Tables:
+    spec: Spec
+    NB: int
+    MB: int
+    free_order: np.ndarray      # int32 [NB]
+    context_lens: np.ndarray    # int32 [B]
+    block_tables: np.ndarray    # int32 [B, MB], unused = -1 (after the step)
+    positions: np.ndarray       # int32 [B], the last position of each sequence
+    slots: np.ndarray           # int32 [T], the step's slots (from the block manager)
+    pairs: np.ndarray           # int32 [n, 2], the step's copy-on-write pairs
+    seqs: list
+    bm: object
+
+
+def make_tables(spec, bm_factory):
+    """Block tables for `spec` built by `bm_factory(num_blocks, block_size, free_order)`."""
+    rng = np.random.default_rng(spec.seed)
+    ctx, cow_parts = draw_lengths(spec, rng)
+    if spec.pool_blocks:
+        NB = spec.pool_blocks
+    else:
+        # dry run in an ample pool to count the blocks the workload holds
+        big = int(sum(int(c) for c in ctx)) + spec.B + 16
+        probe = bm_factory(big, spec.bs, np.arange(big, dtype=np.int32))
+        _populate(spec, probe, ctx, cow_parts)
+        used = big - probe.num_free()
+        NB = int(math.ceil(used * (1.0 + spec.pool_slack)))
+    free_order = rng.permutation(NB).astype(np.int32)
+    bm = bm_factory(NB, spec.bs, free_order)
+    seqs, slots, pairs = _populate(spec, bm, ctx, cow_parts)
+    MB = max(len(bm.block_table(s)) for s in seqs)
+    bt = np.asarray(bm.tables_array(seqs, MB), dtype=np.int32).reshape(spec.B, MB)
+    lens = np.asarray([bm.seq_len(s) for s in seqs], dtype=np.int32)
+    return Tables(spec=spec, NB=NB, MB=MB, free_order=free_order, context_lens=lens,
+                  block_tables=bt, positions=(lens - 1).astype(np.int32),
+                  slots=np.asarray(slots, dtype=np.int32),
+                  pairs=np.asarray(pairs, dtype=np.int32).reshape(-1, 2),
+                  seqs=seqs, bm=bm)
+
+
+@dataclass
+class Values:
+    q: torch.Tensor         # [B, Hq, D]
+    k_cache: torch.Tensor   # [NB, Hkv, bs, D]
+    v_cache: torch.Tensor
+    k_new: torch.Tensor     # [T, Hkv, D]
+    v_new: torch.Tensor
+
+
+def make_values(spec, NB, T, device="cpu"):
+    """N(0,1) values in the workload's element type, drawn on `device`.
+
+    The same seed gives the same values on the CPU every time; a GPU
+    generator gives a different (still seeded) stream."""
+    g = torch.Generator(device=device)
+    g.manual_seed(spec.seed)
+    dt = torch_dtype(spec)
+
+    def draw(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(dt)
+
+    q = draw(spec.B, spec.Hq, spec.D)
+    k = draw(NB, spec.Hkv, spec.bs, spec.D)
+    v = draw(NB, spec.Hkv, spec.bs, spec.D)
+    kn = draw(T, spec.Hkv, spec.D)
+    vn = draw(T, spec.Hkv, spec.D)
+    return Values(q, k, v, kn, vn)
+
+
+def to_bits(t):
+    """A torch tensor's raw element bits as numpy (uint16 for bf16, float32 for fp32)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(t.dtype)
