@@ -1,0 +1,251 @@
+/*
+ * pa.h — paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A KV cache split into fixed-size physical blocks, a per-sequence block
+ * table from logical token positions to physical blocks, single-query decode
+ * attention that gathers K/V through that table, the write of each step's new
+ * K/V into its slot, and the copy of shared blocks before a write
+ * (copy-on-write). Sources of the method:
+ *
+ *   [P1] "Why OS Virtual Memory Paging Saved LLM Inference: The vLLM
+ *        Breakthrough" (a8q9.cn): section 2 "The PagedAttention Architecture"
+ *        (fixed-size blocks, block table, on-demand allocation, attention
+ *        kernel reading blocks through the table); section 3 "Copy-on-Write
+ *        for Prompt Sharing".
+ *   [P2] "vLLM & PagedAttention: Operating Systems Ideas for LLM Serving"
+ *        (completesystemdesign.dev): section 01 "The Problem" (decode reads
+ *        every earlier token's K and V each step and is memory-bound).
+ *   [P3] "Can OS paging techniques reduce LLM serving memory waste?"
+ *        (inquiringlines.com): mechanism paragraph (attention block by block,
+ *        non-contiguous blocks, per-request block tables, block sharing).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor argument is a DEVICE pointer owned by the caller; the
+ *    library never allocates, frees or keeps device memory and keeps no state
+ *    between calls (the block manager at the end is host-only and owns only
+ *    host memory). Tensors are dense and row-major in the shapes given.
+ *  - Cache pools: k_cache and v_cache are [NB][Hkv][bs][D] each: one
+ *    (block, kv head) tile is bs contiguous token rows of D elements.
+ *  - Element type `dt` (PA_F32 or PA_BF16) applies to q, out, the new K/V
+ *    rows and both pools alike.
+ *  - Supported: bs == 16; D in {64, 128}; Hq % Hkv == 0. Query head h reads
+ *    kv head h / (Hq / Hkv).
+ *  - Calls enqueue their kernels on `stream` (NULL = the null stream) and
+ *    return once launched; nothing synchronises. A launch failure returns
+ *    PA_EHIP. Host-side validation runs before any launch; on any error
+ *    nothing is launched and no memory is touched.
+ *  - Device-side contents are read defensively: an out-of-range block id,
+ *    slot or context length never causes an out-of-bounds access. What each
+ *    call does with such entries is stated with the call.
+ *  - Thread-safe and reentrant: no global mutable state.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,        /* null pointer, bad size, inconsistent arguments   */
+  PA_EUNSUPPORTED = -2,  /* valid request outside the compiled kernels       */
+  PA_EWORKSPACE = -3,    /* workspace missing or smaller than required       */
+  PA_EHIP = -4,          /* the HIP runtime rejected a launch                */
+  PA_ENOBLOCKS = -5      /* block manager: not enough free blocks            */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Static, human-readable text for a status code. Never NULL. */
+const char* pa_status_str(pa_status s);
+
+/*
+ * pa_slot_mapping — physical slot of logical token positions.
+ *
+ * [P1] section 2: the block table maps a sequence's logical token positions
+ * to physical blocks, as a page table maps pages. Position p lies in
+ * logical block p / bs at offset p % bs, so for token i of sequence
+ * s = seq_ids[i] at position p = positions[i]:
+ *     slot_mapping[i] = block_tables[s][p / bs] * bs + p % bs.
+ *
+ *   slot_mapping  out, int32 [T]
+ *   block_tables  int32 [B][MB]; entries may be -1 (unused)
+ *   seq_ids       int32 [T], or NULL for seq_ids[i] = i (then T must be <= B)
+ *   positions     int32 [T]
+ * A negative position, a position at or past MB * bs, a sequence index
+ * outside [0, B) or a negative table entry gives slot -1 (the "no write"
+ * marker pa_write_kv skips). T == 0 is a no-op.
+ */
+pa_status pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* seq_ids, const int32_t* positions,
+                          int32_t T, int32_t B, int32_t MB, int32_t bs,
+                          hipStream_t stream);
+
+/*
+ * pa_write_kv — write each new token's K and V rows into its slot
+ * (the reshape-and-cache step).
+ *
+ * [P1] section 2: blocks fill as tokens are generated. Row i of k_new/v_new
+ * (all Hkv heads) goes to slot s = slot_mapping[i]:
+ *     k_cache[s / bs][g][s % bs][:] = k_new[i][g][:]   for every kv head g,
+ * and likewise for V. The copy is of raw bits (NaN payloads and denormals
+ * are preserved).
+ *
+ *   k_new, v_new   [T][Hkv][D]
+ *   k_cache, v_cache [NB][Hkv][bs][D], modified in place
+ *   slot_mapping   int32 [T]; slot < 0 or slot >= NB * bs is skipped
+ * Slots must be distinct within one call (else which row lands is
+ * unspecified). T == 0 is a no-op.
+ */
+pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, const int32_t* slot_mapping, int32_t T,
+                      int32_t NB, int32_t Hkv, int32_t D, int32_t bs,
+                      pa_dtype dt, hipStream_t stream);
+
+/*
+ * pa_copy_blocks — copy-on-write block copies.
+ *
+ * [P1] section 3: branches of one request share the physical prompt blocks;
+ * a branch about to write into a shared block first gets a private copy.
+ * For each pair i: K[dst] = K[src] and V[dst] = V[src], whole blocks (all kv
+ * heads, slots and dims), raw bits.
+ *
+ *   pairs  int32 [n][2] = (src, dst), device memory
+ * Pairs with an id outside [0, NB) are skipped. Destinations must be
+ * distinct and no destination may also be a source within one call (then
+ * the parallel copy equals the in-order one). n == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                         int32_t n, int32_t NB, int32_t Hkv, int32_t D,
+                         int32_t bs, pa_dtype dt, hipStream_t stream);
+
+/*
+ * pa_decode_default_partition — split-context partition size (tokens) the
+ * library would pick for this shape on the current device: 0 (no split) when
+ * one workgroup per (sequence, kv head) already fills the GPU, else a
+ * multiple of bs. Never fails; returns 0 for invalid shapes.
+ */
+int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv,
+                                    int32_t D, int32_t max_ctx);
+
+/*
+ * pa_decode_workspace_bytes — device workspace pa_decode needs for this
+ * split: 0 when partition == 0 or max_ctx <= partition, otherwise room for
+ * per-partition partial results (fp32 running max, sum and unnormalised
+ * output row per (sequence, query head, partition)).
+ */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+                                 int32_t max_ctx, int32_t partition);
+
+/*
+ * pa_decode — single-query decode attention over the paged cache.
+ *
+ * [P1] section 2 / [P3] mechanism paragraph: for the new token, look up each
+ * logical block's physical block in the table and read K/V from it; the
+ * result equals attention over the contiguous history. [P2] section 01: the
+ * query attends over every cached token of its sequence. For sequence s,
+ * query head h, kv head g = h / (Hq / Hkv), L = context_lens[s]:
+ *     x_t   = scale * dot(q[s][h], K_t),   t = 0 .. L-1
+ *     out   = sum_t softmax(x)_t * V_t
+ * where K_t = k_cache[block_tables[s][t / bs]][g][t % bs]. L counts the
+ * tokens in the cache including the step's own token (write it with
+ * pa_write_kv first). Accumulation is fp32; bf16 output is rounded to
+ * nearest even.
+ *
+ *   out            [B][Hq][D], must not alias any input
+ *   q              [B][Hq][D]
+ *   k_cache, v_cache [NB][Hkv][bs][D]
+ *   block_tables   int32 [B][MB]; only entries t / bs < ceil(L / bs) are read
+ *   context_lens   int32 [B], device memory
+ *   max_ctx        host-side upper bound on every context_lens[s] (sizes the
+ *                  grid without a device-to-host read)
+ *   scale          fp32 logit scale (usually 1 / sqrt(D))
+ *   partition      tokens per split-context partition: 0 = no split, else a
+ *                  positive multiple of bs. With a split, every partition is
+ *                  attended independently and a second kernel merges the
+ *                  partitions of each (sequence, head) with log-sum-exp
+ *                  weights.
+ *   workspace      device buffer of at least
+ *                  pa_decode_workspace_bytes(B, Hq, D, max_ctx, partition)
+ *                  bytes, 256-byte aligned (may be NULL when that is 0)
+ * L == 0 gives an all-zero row. A sequence whose L is negative or exceeds
+ * min(max_ctx, MB * bs), or whose table holds an id outside [0, NB) at a
+ * position it reads, gets an all-NaN output row and its K/V are not read.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t B, int32_t Hq,
+                    int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                    int32_t max_ctx, float scale, int32_t partition,
+                    void* workspace, size_t workspace_bytes, pa_dtype dt,
+                    hipStream_t stream);
+
+/*
+ * Block manager — host-side bookkeeping of the physical block pool.
+ *
+ * [P1] section 2: blocks are handed out one at a time, only when a token
+ * needs a new one; each sequence has a table from logical to physical
+ * blocks. [P1] section 3 / [P3] mechanism paragraph: sequences may share
+ * blocks; a sequence about to write into a shared block gets a private copy
+ * first. Sharing is tracked with per-block reference counts. The free list
+ * hands out blocks from its front and takes freed blocks back at its front.
+ * All pointers below are HOST memory. One manager must not be used from two
+ * threads at once; distinct managers are independent.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* free_order: host int32 [num_blocks], a permutation of 0..num_blocks-1 giving
+ * the initial free-list order, or NULL for 0, 1, 2, ... */
+pa_status pa_bm_create(pa_block_manager** bm, int32_t num_blocks,
+                       int32_t block_size, const int32_t* free_order);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* A new, empty sequence; its id is written to *seq. */
+pa_status pa_bm_add_seq(pa_block_manager* bm, int32_t* seq);
+
+/* A new sequence sharing every block of `parent` (their counts go up). */
+pa_status pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t* child);
+
+/*
+ * Append n tokens to `seq`. slots: host int32 [n] receives the physical slot
+ * of each new token. At most one copy-on-write pair arises per call (only the
+ * partly filled last block can be shared); it is written to pair[0..1] as
+ * (src, dst) and *n_pairs is set to 0 or 1; the caller copies that block
+ * (pa_copy_blocks) before writing the tokens (pa_write_kv). If the free list
+ * cannot supply every block the call needs, PA_ENOBLOCKS is returned and
+ * nothing changes.
+ */
+pa_status pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t n,
+                       int32_t* slots, int32_t* pair, int32_t* n_pairs);
+
+/* Drop `seq`; blocks no other sequence holds return to the free list. */
+pa_status pa_bm_free_seq(pa_block_manager* bm, int32_t seq);
+
+pa_status pa_bm_seq_len(const pa_block_manager* bm, int32_t seq, int32_t* len);
+pa_status pa_bm_num_free(const pa_block_manager* bm, int32_t* n);
+pa_status pa_bm_refcount(const pa_block_manager* bm, int32_t block, int32_t* ref);
+
+/* The table of `seq`: up to cap ids to out (host int32), count to *n. */
+pa_status pa_bm_block_table(const pa_block_manager* bm, int32_t seq,
+                            int32_t* out, int32_t cap, int32_t* n);
+
+/*
+ * Dense tables for a batch: tables host int32 [n_seqs][MB] (unused = -1) and
+ * lens host int32 [n_seqs]. PA_EINVAL if a table is longer than MB.
+ */
+pa_status pa_bm_fill_tables(const pa_block_manager* bm, const int32_t* seqs,
+                            int32_t n_seqs, int32_t MB, int32_t* tables,
+                            int32_t* lens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

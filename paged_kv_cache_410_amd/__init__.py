@@ -1,1 +1,238 @@
-"""Paged KV-cache decode attention for MI355X (gfx950)."""
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+Python face of libpa.so (include/pa.h). Each function checks tensor shapes,
+dtypes, devices and contiguity, then calls the C function of the same name on
+torch's current stream. Every step runs in the library's HIP kernels; torch
+provides device memory and streams only.
+
+    slot_mapping(block_tables, positions)                  -> int32 [B]
+    write_kv(k_new, v_new, k_cache, v_cache, slot_mapping)    (in place)
+    copy_blocks(k_cache, v_cache, pairs)                      (in place)
+    decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx,
+           partition=None, out=None, workspace=None)     -> [B, Hq, D]
+    BlockManager(num_blocks, block_size=16, free_order=None)
+
+Pools are [num_blocks, num_kv_heads, 16, head_dim] tensors (fp32 or bf16).
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PAError, check, lib  # noqa: F401
+
+__all__ = ["slot_mapping", "write_kv", "copy_blocks", "decode", "decode_workspace_bytes",
+           "default_partition", "BlockManager", "PAError"]
+
+BLOCK_SIZE = 16
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: use float32 or bfloat16")
+
+
+def _dev(*ts):
+    dev = ts[0].device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for t in ts:
+        if t.device != dev:
+            raise ValueError("tensors must share one device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def slot_mapping(block_tables, positions, seq_ids=None, out=None):
+    """Slot of each (sequence, position): positions [T], seq_ids [T] or None (= 0..T-1)."""
+    _i32(block_tables, "block_tables")
+    _i32(positions, "positions")
+    B, MB = block_tables.shape
+    T = positions.shape[0]
+    ts = [block_tables, positions]
+    if seq_ids is not None:
+        _i32(seq_ids, "seq_ids")
+        if seq_ids.shape != (T,):
+            raise ValueError("seq_ids must match positions")
+        ts.append(seq_ids)
+    elif T > B:
+        raise ValueError("without seq_ids there is one position per sequence")
+    if out is None:
+        out = torch.empty(T, dtype=torch.int32, device=block_tables.device)
+    dev = _dev(*ts, out)
+    with torch.cuda.device(dev):
+        check(lib().pa_slot_mapping(out.data_ptr(), block_tables.data_ptr(),
+                                    seq_ids.data_ptr() if seq_ids is not None else None,
+                                    positions.data_ptr(), T, B, MB, BLOCK_SIZE, _stream(dev)),
+              "pa_slot_mapping")
+    return out
+
+
+def _pool_dims(k_cache, v_cache):
+    if k_cache.dim() != 4 or k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must be matching [NB, Hkv, 16, D] tensors")
+    NB, Hkv, bs, D = k_cache.shape
+    return NB, Hkv, bs, D
+
+
+def write_kv(k_new, v_new, k_cache, v_cache, slot_mapping):
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _i32(slot_mapping, "slot_mapping")
+    T = slot_mapping.shape[0]
+    if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D):
+        raise ValueError("k_new / v_new must be [T, Hkv, D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("new rows and pools must share a dtype")
+    dev = _dev(k_new, v_new, k_cache, v_cache, slot_mapping)
+    with torch.cuda.device(dev):
+        check(lib().pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                                v_cache.data_ptr(), slot_mapping.data_ptr(), T, NB, Hkv, D, bs,
+                                _dt(k_cache), _stream(dev)), "pa_write_kv")
+
+
+def copy_blocks(k_cache, v_cache, pairs):
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _i32(pairs, "pairs")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    dev = _dev(k_cache, v_cache, pairs)
+    with torch.cuda.device(dev):
+        check(lib().pa_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), pairs.data_ptr(),
+                                   pairs.shape[0], NB, Hkv, D, bs, _dt(k_cache), _stream(dev)),
+              "pa_copy_blocks")
+
+
+def default_partition(B, Hq, Hkv, D, max_ctx):
+    return int(lib().pa_decode_default_partition(B, Hq, Hkv, D, max_ctx))
+
+
+def decode_workspace_bytes(B, Hq, D, max_ctx, partition):
+    return int(lib().pa_decode_workspace_bytes(B, Hq, D, max_ctx, partition))
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx, partition=None,
+           out=None, workspace=None):
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    B, Hq, Dq = q.shape
+    if Dq != D or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [B, Hq, D] with the pools' dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    MB = block_tables.shape[1]
+    if partition is None:
+        with torch.cuda.device(q.device):
+            partition = default_partition(B, Hq, Hkv, D, max_ctx)
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = decode_workspace_bytes(B, Hq, D, max_ctx, partition)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    tensors = [q, k_cache, v_cache, block_tables, context_lens, out]
+    if workspace is not None:
+        tensors.append(workspace)
+    dev = _dev(*tensors)
+    with torch.cuda.device(dev):
+        check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                              block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs,
+                              NB, MB, int(max_ctx), float(scale), int(partition), ws_ptr, ws_bytes,
+                              _dt(q), _stream(dev)), "pa_decode")
+    return out
+
+
+class BlockManager:
+    """Host-side block bookkeeping in the native library (pa_bm_* in pa.h)."""
+
+    def __init__(self, num_blocks, block_size=BLOCK_SIZE, free_order=None):
+        self._h = ctypes.c_void_p()
+        fo = None
+        if free_order is not None:
+            fo = np.ascontiguousarray(free_order, dtype=np.int32)
+            if fo.shape != (num_blocks,):
+                raise ValueError("free_order must have num_blocks entries")
+        self._destroy = lib().pa_bm_destroy  # held so teardown at exit still finds it
+        check(lib().pa_bm_create(ctypes.byref(self._h), num_blocks, block_size,
+                                 fo.ctypes.data if fo is not None else None), "pa_bm_create")
+        self._fo = fo
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._destroy(h)
+            self._h = None
+
+    def add_seq(self):
+        out = ctypes.c_int32()
+        check(lib().pa_bm_add_seq(self._h, ctypes.byref(out)), "pa_bm_add_seq")
+        return out.value
+
+    def fork(self, parent):
+        out = ctypes.c_int32()
+        check(lib().pa_bm_fork(self._h, parent, ctypes.byref(out)), "pa_bm_fork")
+        return out.value
+
+    def append(self, sid, n=1):
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pair = np.empty(2, dtype=np.int32)
+        npairs = ctypes.c_int32()
+        st = lib().pa_bm_append(self._h, sid, n, slots.ctypes.data, pair.ctypes.data,
+                                ctypes.byref(npairs))
+        check(st, "pa_bm_append")
+        pairs = [(int(pair[0]), int(pair[1]))] if npairs.value else []
+        return slots[:n].tolist(), pairs
+
+    def free_seq(self, sid):
+        check(lib().pa_bm_free_seq(self._h, sid), "pa_bm_free_seq")
+
+    def seq_len(self, sid):
+        out = ctypes.c_int32()
+        check(lib().pa_bm_seq_len(self._h, sid, ctypes.byref(out)), "pa_bm_seq_len")
+        return out.value
+
+    def num_free(self):
+        out = ctypes.c_int32()
+        check(lib().pa_bm_num_free(self._h, ctypes.byref(out)), "pa_bm_num_free")
+        return out.value
+
+    def refcount(self, b):
+        out = ctypes.c_int32()
+        check(lib().pa_bm_refcount(self._h, b, ctypes.byref(out)), "pa_bm_refcount")
+        return out.value
+
+    def block_table(self, sid):
+        n = ctypes.c_int32()
+        check(lib().pa_bm_block_table(self._h, sid, None, 0, ctypes.byref(n)), "pa_bm_block_table")
+        buf = np.empty(max(n.value, 1), dtype=np.int32)
+        check(lib().pa_bm_block_table(self._h, sid, buf.ctypes.data, n.value, ctypes.byref(n)),
+              "pa_bm_block_table")
+        return buf[:n.value].tolist()
+
+    def tables_array(self, sids, max_blocks):
+        seqs = np.ascontiguousarray(sids, dtype=np.int32)
+        tables = np.empty((len(seqs), max_blocks), dtype=np.int32)
+        lens = np.empty(len(seqs), dtype=np.int32)
+        check(lib().pa_bm_fill_tables(self._h, seqs.ctypes.data, len(seqs), max_blocks,
+                                      tables.ctypes.data, lens.ctypes.data), "pa_bm_fill_tables")
+        return tables

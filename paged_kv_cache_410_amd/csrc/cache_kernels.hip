@@ -1,0 +1,107 @@
+// Block-table bookkeeping kernels: slot mapping, the cache write of new K/V
+// rows, and copy-on-write block copies. All three move integers or raw bits.
+//
+// Method: "Why OS Virtual Memory Paging Saved LLM Inference" (a8q9.cn),
+// section 2 (block table from logical positions to physical blocks; blocks
+// filled as tokens are generated) and section 3 (a branch writing into a
+// shared block first receives a private copy of it).
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+// slot = table[seq][p / 16] * 16 + p % 16, or -1 when there is no valid slot.
+__global__ void slot_mapping_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ bt,
+                                    const int32_t* __restrict__ seq_ids,
+                                    const int32_t* __restrict__ pos, int32_t T, int32_t B,
+                                    int32_t MB) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  const int32_t s = seq_ids ? seq_ids[i] : i;
+  const int32_t p = pos[i];
+  int32_t slot = -1;
+  if (s >= 0 && s < B && p >= 0 && p / kBlock < MB) {
+    const int32_t b = bt[(size_t)s * MB + p / kBlock];
+    if (b >= 0) slot = b * kBlock + p % kBlock;
+  }
+  out[i] = slot;
+}
+
+// One thread per 16-byte chunk of a (token, kv head) row; K and V together.
+// Source row (t, g) -> pool row (slot / 16, g, slot % 16).
+__global__ void write_kv_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                                uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                const int32_t* __restrict__ slots, int32_t T, int32_t Hkv,
+                                int32_t chunks_per_row, int64_t n_slots) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)T * Hkv * chunks_per_row;
+  if (i >= total) return;
+  const int32_t c = (int32_t)(i % chunks_per_row);
+  const int64_t row = i / chunks_per_row;
+  const int32_t g = (int32_t)(row % Hkv);
+  const int32_t t = (int32_t)(row / Hkv);
+  const int32_t slot = slots[t];
+  if (slot < 0 || slot >= n_slots) return;
+  const int64_t dst = (((int64_t)(slot / kBlock) * Hkv + g) * kBlock + slot % kBlock) * chunks_per_row + c;
+  k_cache[dst] = k_new[i];
+  v_cache[dst] = v_new[i];
+}
+
+// grid.y = pair, grid.z = 0 (K) / 1 (V); grid.x strides over the block's chunks.
+__global__ void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                   const int32_t* __restrict__ pairs, int32_t NB,
+                                   int64_t chunks_per_block) {
+  const int32_t src = pairs[2 * blockIdx.y];
+  const int32_t dst = pairs[2 * blockIdx.y + 1];
+  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  uint4* base = blockIdx.z ? v_cache : k_cache;
+  const uint4* from = base + (int64_t)src * chunks_per_block;
+  uint4* to = base + (int64_t)dst * chunks_per_block;
+  constexpr int kUnroll = 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < chunks_per_block; i += kUnroll * stride) {
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = from[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) to[i + u * stride] = v[u];
+  }
+  for (; i < chunks_per_block; i += stride) to[i] = from[i];
+}
+
+hipError_t launch_slot_mapping(int32_t* out, const int32_t* bt, const int32_t* seq_ids,
+                               const int32_t* pos, int32_t T, int32_t B, int32_t MB,
+                               hipStream_t stream) {
+  const int threads = 256;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((T + threads - 1) / threads), dim3(threads), 0,
+                     stream, out, bt, seq_ids, pos, T, B, MB);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* slots, int32_t T, int32_t NB, int32_t Hkv,
+                           int32_t row_bytes, hipStream_t stream) {
+  const int32_t chunks = row_bytes / 16;
+  const int64_t total = (int64_t)T * Hkv * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     (const uint4*)k_new, (const uint4*)v_new, (uint4*)k_cache, (uint4*)v_cache,
+                     slots, T, Hkv, chunks, (int64_t)NB * kBlock);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n,
+                              int32_t NB, size_t block_bytes, hipStream_t stream) {
+  const int64_t chunks = (int64_t)(block_bytes / 16);
+  const int threads = 256;
+  // about 4 chunks (64 B) per thread per pass: a 128 KiB block takes 8 workgroups
+  int64_t gx = (chunks + threads * 4 - 1) / (threads * 4);
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n, 2), dim3(threads), 0,
+                     stream, (uint4*)k_cache, (uint4*)v_cache, pairs, NB, chunks);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,102 @@
+// Split-context merge: combines the per-partition partial results of a
+// (sequence, query head) into the final output row.
+//
+// Each partition j left (m_j, l_j, O_j): its running max and softmax sum in
+// the log2 domain and its unnormalised output row. With M = max_j m_j and
+// w_j = 2^(m_j - M), the full-context result is
+//     out = (sum_j w_j O_j) / (sum_j w_j l_j),
+// the same online-softmax rescaling the decode kernels apply between blocks,
+// applied once more between partitions. (The pages describe attention run
+// block by block; partitioning long contexts across workgroups is this
+// library's way to spread one sequence over many compute units.)
+//
+// One wave per (query head, sequence). Lane j of a 64-partition chunk reads
+// (m_j, l_j); the weights are broadcast with readlane while every lane
+// accumulates its own dims of the output row.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return rows_max(x);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams P) {
+  constexpr int DPL = D / kWave;  // output dims per lane
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+
+  const int ctx = P.context_lens[s];
+  if (ctx < 0 || ctx > P.ctx_limit) return;  // the decode kernel wrote NaN already
+  const int nblk = (ctx + kBlock - 1) / kBlock;
+  const int bpp = P.partition / kBlock;
+  const int np = (nblk + bpp - 1) / bpp;
+  if (np <= 1) return;  // the decode kernel wrote the final row itself
+
+  const size_t base = ((size_t)s * P.Hq + h) * P.n_parts;
+  const float* ml = P.ws_ml + 2 * base;
+  const float* po = P.ws_o + base * D + lane * DPL;
+
+  float M = -INFINITY;
+  for (int j = lane; j < np; j += kWave) M = fmaxf(M, ml[2 * j]);
+  M = wave_max(M);
+  const float m_use = (M == -INFINITY) ? 0.0f : M;
+
+  float lpart = 0.0f;
+  float acc[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
+  for (int j0 = 0; j0 < np; j0 += kWave) {
+    const int j = j0 + lane;
+    float wj = 0.0f;
+    if (j < np) {
+      wj = exp2_fast(ml[2 * j] - m_use);
+      lpart += wj * ml[2 * j + 1];
+    }
+    const int cnt = min(kWave, np - j0);
+    for (int k = 0; k < cnt; ++k) {
+      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), k));
+      const float* src = po + (size_t)(j0 + k) * D;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) acc[d] = fmaf(wk, src[d], acc[d]);
+    }
+  }
+  const float L = group_sum<kWave>(lpart);
+  const float inv = 1.0f / L;
+  char* out = reinterpret_cast<char*>(P.out) + (((size_t)s * P.Hq + h) * D + lane * DPL) * sizeof(T);
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (DPL == 2) {
+      *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      const uint32_t pr = pack_bf16x2(acc[0] * inv, 0.0f);
+      *reinterpret_cast<uint16_t*>(out) = (uint16_t)(pr & 0xffffu);
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) reinterpret_cast<float*>(out)[d] = acc[d] * inv;
+  }
+}
+
+hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
+  const dim3 grid(p.Hq, p.B), block(kWave);
+  if (dtype == 1 && D == 128)
+    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, 128>), grid, block, 0, stream, p);
+  else if (dtype == 1 && D == 64)
+    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, 64>), grid, block, 0, stream, p);
+  else if (dtype == 0 && D == 128)
+    hipLaunchKernelGGL((decode_reduce_kernel<float, 128>), grid, block, 0, stream, p);
+  else if (dtype == 0 && D == 64)
+    hipLaunchKernelGGL((decode_reduce_kernel<float, 64>), grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,326 @@
+// Paged decode attention, vector-ALU path (one query head per workgroup).
+//
+// Method: "Why OS Virtual Memory Paging Saved LLM Inference" (a8q9.cn),
+// section 2: the attention kernel reads each logical block's physical block
+// id from the block table and fetches that block's K/V wherever it sits.
+// "Can OS paging techniques reduce LLM serving memory waste?"
+// (inquiringlines.com), mechanism paragraph: attention proceeds block by
+// block. The softmax is accumulated online over blocks (running max, running
+// sum, rescaled output), so every K/V byte is read exactly once.
+//
+// Work decomposition (gfx950, wave64):
+//   grid   = (partition p, query head h, sequence s)
+//   block  = NW waves; wave w takes blocks p0 + w, p0 + w + NW, ...
+//   A (block, kv head) tile is 16 rows of D elements, contiguous in memory.
+//   One 16-byte load per lane: LPT = D*e/16 lanes cover one token row, so a
+//   wave-wide load covers TPI = 64/LPT rows, fully coalesced; NLD = 16/TPI
+//   loads cover the tile. Lane (r = lane / LPT, c = lane % LPT) holds chunk c
+//   of row j*TPI + r for load j.
+//   QK: per-lane partial dot (v_dot2_f32_bf16 or fp32 FMA), then a DPP
+//   all-reduce over the LPT lanes of the row. Every lane of a row then holds
+//   the row's logit, so the V rows loaded in the same lane layout are
+//   accumulated without any further data movement.
+//   Each row group of lanes keeps its own online-softmax state; row groups
+//   merge at the end through lane swaps, waves through LDS.
+//   Next-block K/V loads are issued before the current block is consumed
+//   (two register buffers).
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kPerChunk = 4;
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+};
+template <>
+struct Elem<uint16_t> {  // bf16 bits
+  static constexpr int kPerChunk = 8;
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = bf16lo(u.x);
+    f[1] = bf16hi(u.x);
+    f[2] = bf16lo(u.y);
+    f[3] = bf16hi(u.y);
+    f[4] = bf16lo(u.z);
+    f[5] = bf16hi(u.z);
+    f[6] = bf16lo(u.w);
+    f[7] = bf16hi(u.w);
+  }
+};
+
+// (own, partner) for lanes OFF apart inside the wave, OFF in {8, 16, 32}.
+template <int OFF>
+__device__ __forceinline__ LanePair lane_pair(float x) {
+  if constexpr (OFF == 8) {
+    // row_ror:8 inside a row of 16 lanes: lane i sees lane i ^ 8
+    return {x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false))};
+  } else if constexpr (OFF == 16) {
+    return pair16(x);
+  } else {
+    static_assert(OFF == 32, "lane offset");
+    return pair32(x);
+  }
+}
+
+// Merge the online-softmax states of lanes OFF apart (different token rows,
+// same D chunk) so both hold the state over the union of their tokens.
+template <int OFF, int EPL>
+__device__ __forceinline__ void merge_rows(float& m, float& l, float (&o)[EPL]) {
+  const LanePair pm = lane_pair<OFF>(m);
+  const LanePair pl = lane_pair<OFF>(l);
+  const SoftmaxScales sc = merge_scales(pm.a, pm.b);
+  l = pl.a * sc.a + pl.b * sc.b;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const LanePair po = lane_pair<OFF>(o[e]);
+    o[e] = po.a * sc.a + po.b * sc.b;
+  }
+  m = sc.m;
+}
+
+template <int LPT, int EPL>
+__device__ __forceinline__ void merge_all_rows(float& m, float& l, float (&o)[EPL]) {
+  if constexpr (LPT <= 8) merge_rows<8, EPL>(m, l, o);
+  if constexpr (LPT <= 16) merge_rows<16, EPL>(m, l, o);
+  if constexpr (LPT <= 32) merge_rows<32, EPL>(m, l, o);
+}
+
+}  // namespace
+
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P) {
+  constexpr int EPL = Elem<T>::kPerChunk;  // elements per 16-byte lane chunk
+  constexpr int LPT = D / EPL;             // lanes per token row
+  constexpr int TPI = kWave / LPT;         // token rows per wave-wide load
+  constexpr int NLD = kBlock / TPI;        // wave loads per (block, head) tile
+  constexpr int kRowBytes = D * (int)sizeof(T);
+  static_assert(LPT >= 8 && LPT <= 32 && NLD >= 1, "unsupported tile shape");
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int r = lane / LPT;
+  const int c = lane % LPT;
+
+  const int p = blockIdx.x;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  const int g = h / P.G;
+
+  const int ctx = P.context_lens[s];
+  const bool bad_ctx = ctx < 0 || ctx > P.ctx_limit;
+  const int nblk = bad_ctx ? 0 : (ctx + kBlock - 1) / kBlock;
+  int blk_begin = 0, blk_end = nblk, nparts_s = nblk > 0 ? 1 : 0;
+  if (P.partition > 0) {
+    const int bpp = P.partition / kBlock;
+    nparts_s = (nblk + bpp - 1) / bpp;
+    blk_begin = p * bpp;
+    blk_end = min(nblk, blk_begin + bpp);
+  }
+  if (p >= max(nparts_s, 1)) return;  // partition past this sequence's end
+
+  const size_t row_qo = ((size_t)s * P.Hq + h) * D;
+
+  // Query chunk c of this head.
+  const uint4 qraw = ld16(reinterpret_cast<const char*>(P.q) + row_qo * sizeof(T) + c * 16);
+  float qf[EPL];
+  Elem<T>::unpack(qraw, qf);
+
+  float m = -INFINITY, l = 0.0f;
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+  bool bad = bad_ctx;
+
+  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
+  const char* kbase = reinterpret_cast<const char*>(P.k_cache);
+  const char* vbase = reinterpret_cast<const char*>(P.v_cache);
+  const size_t lane_off = (size_t)r * kRowBytes + c * 16;
+  const size_t head_off = (size_t)g * kBlock * kRowBytes;
+  const size_t block_stride = (size_t)P.Hkv * kBlock * kRowBytes;
+
+  // Load tile `blk` into (kb, vb); false if its block id is out of range.
+  auto load = [&](uint4 (&kb)[NLD], uint4 (&vb)[NLD], int blk) -> bool {
+    const int b = bt_row[blk];
+    if (b < 0 || b >= P.NB) return false;
+    const size_t off = (size_t)b * block_stride + head_off + lane_off;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) kb[j] = ld16(kbase + off + (size_t)j * TPI * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) vb[j] = ld16(vbase + off + (size_t)j * TPI * kRowBytes);
+    return true;
+  };
+
+  // Consume one tile: logits, online-softmax update, V accumulation.
+  auto consume = [&](const uint4 (&kb)[NLD], const uint4 (&vb)[NLD], int blk, bool ok) {
+    if (!ok) {
+      bad = true;
+      return;
+    }
+    float x[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      float acc = 0.0f;
+      if constexpr (sizeof(T) == 2) {
+        acc = dot2_bf16(qraw.x, kb[j].x, acc);
+        acc = dot2_bf16(qraw.y, kb[j].y, acc);
+        acc = dot2_bf16(qraw.z, kb[j].z, acc);
+        acc = dot2_bf16(qraw.w, kb[j].w, acc);
+      } else {
+        float kf[EPL];
+        Elem<T>::unpack(kb[j], kf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qf[e], kf[e], acc);
+      }
+      x[j] = group_sum<LPT>(acc) * P.qscale;
+    }
+    const int tok0 = blk * kBlock;
+    const bool partial = tok0 + kBlock > ctx;  // same for the whole wave
+    if (partial) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        if (tok0 + j * TPI + r >= ctx) x[j] = -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int j = 1; j < NLD; ++j) mx = fmaxf(mx, x[j]);
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = exp2_fast(m - m_use);
+    float pj[NLD];
+    float psum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      pj[j] = exp2_fast(x[j] - m_use);
+      psum += pj[j];
+    }
+    l = l * alpha + psum;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      float vf[EPL];
+      Elem<T>::unpack(vb[j], vf);
+      // rows past the context may hold anything (even NaN): select, not multiply
+      const bool valid = !partial || (tok0 + j * TPI + r < ctx);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pj[j], valid ? vf[e] : 0.0f, o[e]);
+    }
+    m = m_new;
+  };
+
+  // Two-deep software pipeline over this wave's blocks.
+  {
+    uint4 ka[NLD], va[NLD], kb2[NLD], vb2[NLD];
+    int i0 = blk_begin + w;
+    bool ok_a = false, ok_b = false;
+    if (i0 < blk_end) ok_a = load(ka, va, i0);
+    while (i0 < blk_end) {
+      const int i1 = i0 + NW;
+      if (i1 < blk_end) ok_b = load(kb2, vb2, i1);
+      consume(ka, va, i0, ok_a);
+      if (i1 >= blk_end) break;
+      const int i2 = i1 + NW;
+      if (i2 < blk_end) ok_a = load(ka, va, i2);
+      consume(kb2, vb2, i1, ok_b);
+      i0 = i2;
+    }
+  }
+
+  // Row groups of this wave -> one state per D chunk (all rows agree).
+  merge_all_rows<LPT, EPL>(m, l, o);
+
+  float outv[EPL];
+  float M = m, L = l;
+  if constexpr (NW > 1) {
+    __shared__ float sm_o[NW][D];
+    __shared__ float sm_m[NW], sm_l[NW];
+    __shared__ int sm_bad[NW];
+    if (r == 0) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_o[w][c * EPL + e] = o[e];
+      if (c == 0) {
+        sm_m[w] = m;
+        sm_l[w] = l;
+        sm_bad[w] = bad ? 1 : 0;
+      }
+    }
+    __syncthreads();
+    if (w != 0 || r != 0) return;
+    M = sm_m[0];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) M = fmaxf(M, sm_m[v]);
+    const float m_use = (M == -INFINITY) ? 0.0f : M;
+    L = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) outv[e] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float sc = exp2_fast(sm_m[v] - m_use);
+      L += sm_l[v] * sc;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) outv[e] += sm_o[v][c * EPL + e] * sc;
+      bad |= sm_bad[v] != 0;
+    }
+  } else {
+    if (r != 0) return;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) outv[e] = o[e];
+  }
+
+  // Lanes 0 .. LPT-1 of wave 0 hold the result for chunk c.
+  if (P.partition > 0 && nparts_s > 1) {
+    const size_t part = ((size_t)s * P.Hq + h) * P.n_parts + p;
+    float* dst = P.ws_o + part * D + c * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = bad ? __builtin_nanf("") : outv[e];
+    if (c == 0) {
+      P.ws_ml[2 * part] = bad ? 0.0f : M;
+      P.ws_ml[2 * part + 1] = bad ? __builtin_nanf("") : L;
+    }
+    return;
+  }
+  float res[EPL];
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // empty context -> zeros
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) res[e] = bad ? __builtin_nanf("") : outv[e] * inv;
+  char* out = reinterpret_cast<char*>(P.out) + row_qo * sizeof(T) + c * 16;
+  if constexpr (sizeof(T) == 2) {
+    uint4 u;
+    u.x = pack_bf16x2(res[0], res[1]);
+    u.y = pack_bf16x2(res[2], res[3]);
+    u.z = pack_bf16x2(res[4], res[5]);
+    u.w = pack_bf16x2(res[6], res[7]);
+    st16(out, u);
+  } else {
+    st16(out, make_uint4(__float_as_uint(res[0]), __float_as_uint(res[1]),
+                         __float_as_uint(res[2]), __float_as_uint(res[3])));
+  }
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
+  constexpr int NW = 4;
+  const dim3 grid(p.n_parts, p.Hq, p.B), block(NW * kWave);
+  if (dtype == 1 && D == 128)
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW>), grid, block, 0, stream, p);
+  else if (dtype == 1 && D == 64)
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW>), grid, block, 0, stream, p);
+  else if (dtype == 0 && D == 128)
+    hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW>), grid, block, 0, stream, p);
+  else if (dtype == 0 && D == 64)
+    hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW>), grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

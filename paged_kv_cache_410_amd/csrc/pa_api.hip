@@ -1,0 +1,178 @@
+// C ABI of the paged decode attention library: argument validation, kernel
+// choice, grid and workspace layout. Every check here runs on the host before
+// anything is launched; a failed check launches nothing.
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int32_t kBs = 16;
+constexpr int32_t kMaxGridYZ = 65535;
+constexpr size_t kAlign = 256;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int32_t elem_bytes(pa_dtype dt) { return dt == PA_F32 ? 4 : 2; }
+bool dtype_ok(pa_dtype dt) { return dt == PA_F32 || dt == PA_BF16; }
+
+// Partitions the grid covers for a split of `partition` tokens (1 = no split).
+int64_t grid_parts(int32_t max_ctx, int32_t partition) {
+  if (partition <= 0 || max_ctx <= partition) return 1;
+  return ((int64_t)max_ctx + partition - 1) / partition;
+}
+
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EUNSUPPORTED: return "unsupported configuration";
+    case PA_EWORKSPACE: return "workspace missing or too small";
+    case PA_EHIP: return "HIP launch failure";
+    case PA_ENOBLOCKS: return "not enough free KV blocks";
+  }
+  return "unknown status";
+}
+
+pa_status pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* seq_ids, const int32_t* positions, int32_t T, int32_t B,
+                          int32_t MB, int32_t bs, hipStream_t stream) {
+  if (T < 0 || B < 0 || MB < 0) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (!seq_ids && T > B) return PA_EINVAL;
+  if (T == 0) return PA_OK;
+  if (!slot_mapping || !positions || (B > 0 && MB > 0 && !block_tables)) return PA_EINVAL;
+  return pa::launch_slot_mapping(slot_mapping, block_tables, seq_ids, positions, T, B, MB,
+                                 stream) == hipSuccess
+             ? PA_OK
+             : PA_EHIP;
+}
+
+pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* slot_mapping, int32_t T, int32_t NB, int32_t Hkv, int32_t D,
+                      int32_t bs, pa_dtype dt, hipStream_t stream) {
+  if (T < 0 || NB < 0 || Hkv <= 0 || D <= 0 || !dtype_ok(dt)) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (D != 64 && D != 128) return PA_EUNSUPPORTED;
+  if (T == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  if ((int64_t)T * Hkv * D * elem_bytes(dt) / 16 > (int64_t)INT32_MAX * 256) return PA_EUNSUPPORTED;
+  return pa::launch_write_kv(k_new, v_new, k_cache, v_cache, slot_mapping, T, NB, Hkv,
+                             D * elem_bytes(dt), stream) == hipSuccess
+             ? PA_OK
+             : PA_EHIP;
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n, int32_t NB,
+                         int32_t Hkv, int32_t D, int32_t bs, pa_dtype dt, hipStream_t stream) {
+  if (n < 0 || NB < 0 || Hkv <= 0 || D <= 0 || !dtype_ok(dt)) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (D != 64 && D != 128) return PA_EUNSUPPORTED;
+  if (n == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return PA_EINVAL;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_EINVAL;
+  const size_t block_bytes = (size_t)Hkv * kBs * D * elem_bytes(dt);
+  for (int32_t done = 0; done < n; done += kMaxGridYZ) {
+    const int32_t cnt = n - done < kMaxGridYZ ? n - done : kMaxGridYZ;
+    if (pa::launch_copy_blocks(k_cache, v_cache, pairs + 2 * (size_t)done, cnt, NB, block_bytes,
+                               stream) != hipSuccess)
+      return PA_EHIP;
+  }
+  return PA_OK;
+}
+
+int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int32_t max_ctx) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || max_ctx <= 0) return 0;
+  const int32_t G = Hq / Hkv;
+  const int64_t units = (int64_t)B * (G >= 2 ? (int64_t)Hkv * pa::mfma_q_groups(G) : Hq);
+  const int64_t cus = device_cus();
+  // Enough (sequence, head) workgroups to keep every CU busy: no split.
+  if (units >= 8 * cus || max_ctx <= 512) return 0;
+  return 512;
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_ctx,
+                                 int32_t partition) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || max_ctx <= 0 || partition <= 0) return 0;
+  const int64_t parts = grid_parts(max_ctx, partition);
+  if (parts <= 1) return 0;
+  const size_t rows = (size_t)B * Hq * (size_t)parts;
+  return align_up(rows * 2 * sizeof(float)) + rows * (size_t)D * sizeof(float);
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                    int32_t max_ctx, float scale, int32_t partition, void* workspace,
+                    size_t workspace_bytes, pa_dtype dt, hipStream_t stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || NB < 0 || MB < 0 || max_ctx < 0 || !dtype_ok(dt))
+    return PA_EINVAL;
+  if (Hq % Hkv != 0) return PA_EINVAL;
+  if (partition < 0 || partition % kBs != 0) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (D != 64 && D != 128) return PA_EUNSUPPORTED;
+  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return PA_EUNSUPPORTED;
+  if (B == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !context_lens || (MB > 0 && !block_tables))
+    return PA_EINVAL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+
+  const int64_t parts = grid_parts(max_ctx, partition);
+  const size_t need = pa_decode_workspace_bytes(B, Hq, D, max_ctx, partition);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
+  if (need > 0 && ((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
+  if (parts > INT32_MAX) return PA_EUNSUPPORTED;
+
+  pa::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = Hq / Hkv;
+  p.NB = NB;
+  p.MB = MB;
+  const int64_t cap = (int64_t)MB * kBs;
+  p.ctx_limit = (int32_t)(cap < max_ctx ? cap : max_ctx);
+  p.partition = parts > 1 ? partition : 0;
+  p.n_parts = (int32_t)parts;
+  p.qscale = scale * 1.4426950408889634f;
+  if (parts > 1) {
+    const size_t rows = (size_t)B * Hq * (size_t)parts;
+    p.ws_ml = static_cast<float*>(workspace);
+    p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * 2 * sizeof(float)));
+  }
+
+  const bool mfma = dt == PA_BF16 && D == 128 && p.G >= 2;
+  if (mfma && (int64_t)Hkv * pa::mfma_q_groups(p.G) > kMaxGridYZ) return PA_EUNSUPPORTED;
+  hipError_t err = mfma ? pa::launch_decode_mfma(p, stream) : pa::launch_decode_valu(p, dt, D, stream);
+  if (err != hipSuccess) return PA_EHIP;
+  if (parts > 1) {
+    err = pa::launch_decode_reduce(p, dt, D, stream);
+    if (err != hipSuccess) return PA_EHIP;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device-side building blocks shared by the decode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 16;  // tokens per KV block
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 bits
+// bf16 -> fp32 is exact: the 16 stored bits are the high half of a binary32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------- cross-lane
+// DPP lane permutations inside a row of 16 lanes.
+enum : int {
+  kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+  kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+  kDppHalfMirror = 0x141, // lane i <-> 7-i within each half-row of 8
+  kDppMirror = 0x140,     // lane i <-> 15-i within each row of 16
+};
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+
+// The gfx950 permlane swaps exchange rows (16 lanes) between two registers.
+// Fed the same value twice they return, in some order, a lane's own value and
+// that of its partner lane l ^ 16 (permlane16) or l ^ 32 (permlane32). Every
+// use below combines the two symmetrically (sum, max, softmax merge), so which
+// of the pair is "own" never matters.
+struct LanePair {
+  float a, b;
+};
+__device__ __forceinline__ LanePair pair16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ LanePair pair32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
+// Sum over aligned groups of N consecutive lanes (N in 4, 8, 16, 32, 64); every lane gets it.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (N >= 32) {
+    LanePair p = pair16(x);
+    x = p.a + p.b;
+  }
+  if constexpr (N >= 64) {
+    LanePair p = pair32(x);
+    x = p.a + p.b;
+  }
+  return x;
+}
+
+// Max over the 4 rows of the wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float rows_max(float x) {
+  LanePair p = pair16(x);
+  x = fmaxf(p.a, p.b);
+  p = pair32(x);
+  return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  LanePair p = pair16(x);
+  x = p.a + p.b;
+  p = pair32(x);
+  return p.a + p.b;
+}
+
+// fast 2^x (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax merge of two partial states over disjoint token sets, in the
+// log2 domain: (m, l, o) with o unnormalised. Empty states carry m = -inf.
+struct SoftmaxScales {
+  float a, b, m;
+};
+__device__ __forceinline__ SoftmaxScales merge_scales(float m_a, float m_b) {
+  const float m = fmaxf(m_a, m_b);
+  const float m_use = (m == -INFINITY) ? 0.0f : m;
+  return {exp2_fast(m_a - m_use), exp2_fast(m_b - m_use), m};
+}
+
+// Non-temporal-free plain 16-byte global load/store helpers.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace pa

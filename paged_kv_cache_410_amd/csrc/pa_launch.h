@@ -1,0 +1,44 @@
+// Host-side launch interface between the C ABI (pa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything a decode kernel reads. Lengths are in elements unless noted.
+struct DecodeParams {
+  void* out;                    // [B][Hq][D] I/O dtype
+  const void* q;                // [B][Hq][D]
+  const void* k_cache;          // [NB][Hkv][16][D]
+  const void* v_cache;
+  const int32_t* block_tables;  // [B][MB]
+  const int32_t* context_lens;  // [B]
+  float* ws_ml;                 // split only: [B][Hq][n_parts][2] = (m, l), log2 domain
+  float* ws_o;                  // split only: [B][Hq][n_parts][D], unnormalised
+  int32_t B, Hq, Hkv, G, NB, MB;
+  int32_t ctx_limit;            // min(max_ctx, MB * 16): larger contexts are rejected
+  int32_t partition;            // tokens per partition; 0 = one partition per sequence
+  int32_t n_parts;              // grid extent over partitions
+  float qscale;                 // scale * log2(e): logits are kept in the log2 domain
+};
+
+hipError_t launch_slot_mapping(int32_t* out, const int32_t* bt, const int32_t* seq_ids,
+                               const int32_t* pos, int32_t T, int32_t B, int32_t MB,
+                               hipStream_t stream);
+hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                           const int32_t* slots, int32_t T, int32_t NB, int32_t Hkv,
+                           int32_t row_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n,
+                              int32_t NB, size_t block_bytes, hipStream_t stream);
+
+// dtype: 0 = fp32, 1 = bf16 (pa_dtype values)
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream);
+
+// Query-head groups of up to 16 handled by one MFMA workgroup.
+__host__ __device__ inline int mfma_q_groups(int G) { return (G + 15) / 16; }
+
+}  // namespace pa

@@ -105,21 +105,30 @@ def draw_lengths(spec, rng):
 def _populate(spec, bm, ctx, cow_parts):
     """Drive a block manager through the workload's history and its step.
 
-    Returns seq ids, the step's slots, the step's (src, dst) copy pairs and
-    the per-slot token index into the step's new K/V rows.
+    Returns seq ids, the step's slots, the step's (src, dst) copy pairs, and
+    for every step token its batch index and logical position.
     """
     seqs = []
     step_slots = []
     step_pairs = []
+    step_seq = []
+    step_pos = []
+
+    def step(i, sid, n):
+        start = bm.seq_len(sid)
+        slots, pairs = bm.append(sid, n)
+        step_slots.extend(slots)
+        step_pairs.extend(pairs)
+        step_seq.extend([i] * n)
+        step_pos.extend(range(start, start + n))
+
     if cow_parts is None:
         for s in range(spec.B):
             sid = bm.add_seq()
             seqs.append(sid)
             bm.append(sid, int(ctx[s]) - 1)          # history (untimed)
-        for sid in seqs:
-            slots, pairs = bm.append(sid, 1)          # the step's token
-            step_slots.extend(slots)
-            step_pairs.extend(pairs)
+        for i, sid in enumerate(seqs):
+            step(i, sid, 1)                           # the step's token
     else:
         prompt, tails = cow_parts
         c = spec.cow
@@ -129,10 +138,8 @@ def _populate(spec, bm, ctx, cow_parts):
             group = [parent] + [bm.fork(parent) for _ in range(c["samples"] - 1)]
             seqs.extend(group)
         for i, sid in enumerate(seqs):
-            slots, pairs = bm.append(sid, int(tails[i]))   # divergent tails
-            step_slots.extend(slots)
-            step_pairs.extend(pairs)
-    return seqs, step_slots, step_pairs
+            step(i, sid, int(tails[i]))                # divergent tails
+    return seqs, step_slots, step_pairs, step_seq, step_pos
 
 
 @dataclass
@@ -145,6 +152,8 @@ class Tables:
     block_tables: np.ndarray    # int32 [B, MB], unused = -1 (after the step)
     positions: np.ndarray       # int32 [B], the last position of each sequence
     slots: np.ndarray           # int32 [T], the step's slots (from the block manager)
+    step_seq: np.ndarray        # int32 [T], batch index of each step token
+    step_pos: np.ndarray        # int32 [T], logical position of each step token
     pairs: np.ndarray           # int32 [n, 2], the step's copy-on-write pairs
     seqs: list
     bm: object
@@ -165,13 +174,15 @@ def make_tables(spec, bm_factory):
         NB = int(math.ceil(used * (1.0 + spec.pool_slack)))
     free_order = rng.permutation(NB).astype(np.int32)
     bm = bm_factory(NB, spec.bs, free_order)
-    seqs, slots, pairs = _populate(spec, bm, ctx, cow_parts)
+    seqs, slots, pairs, step_seq, step_pos = _populate(spec, bm, ctx, cow_parts)
     MB = max(len(bm.block_table(s)) for s in seqs)
     bt = np.asarray(bm.tables_array(seqs, MB), dtype=np.int32).reshape(spec.B, MB)
     lens = np.asarray([bm.seq_len(s) for s in seqs], dtype=np.int32)
     return Tables(spec=spec, NB=NB, MB=MB, free_order=free_order, context_lens=lens,
                   block_tables=bt, positions=(lens - 1).astype(np.int32),
                   slots=np.asarray(slots, dtype=np.int32),
+                  step_seq=np.asarray(step_seq, dtype=np.int32),
+                  step_pos=np.asarray(step_pos, dtype=np.int32),
                   pairs=np.asarray(pairs, dtype=np.int32).reshape(-1, 2),
                   seqs=seqs, bm=bm)
 

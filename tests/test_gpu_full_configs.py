@@ -1,0 +1,61 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times: whole-pool bit-exact cache bookkeeping, and attention outputs
+on sampled (sequence, head) rows the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_410_amd import workloads
+
+from gpu_cases import TOL, Step, host_bits, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_410_amd as m
+    return m
+
+
+def bench_partition(pa, spec, max_ctx):
+    if spec.partition:
+        return spec.partition
+    return pa.default_partition(spec.B, spec.Hq, spec.Hkv, spec.D, max_ctx)
+
+
+def sample_rows(tb, Hq, n, seed):
+    rng = np.random.default_rng(seed)
+    cl = tb.context_lens
+    seqs = [int(np.argmax(cl)), int(np.argmin(cl))] + rng.integers(0, len(cl), n - 2).tolist()
+    heads = [0, Hq - 1] + rng.integers(0, Hq, n - 2).tolist()
+    return list(zip(seqs, heads))
+
+
+@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "cow"])
+def test_full_config(pa, name):
+    spec = workloads.CONFIGS[name]
+    say(f"[full config] {name}: building inputs")
+    st = Step(spec, values_device="cuda", oracle_full=False)
+    part = bench_partition(pa, spec, st.max_ctx)
+    say(f"[full config] {name}: NB={st.tb.NB} MB={st.tb.MB} T={len(st.tb.slots)} "
+        f"pairs={len(st.tb.pairs)} partition={part}")
+    slots = st.run_cache_ops(pa)
+    out = st.decode(pa, partition=part)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), st.tb.slots)
+    assert np.array_equal(host_bits(st.k_cache), st.k_after)
+    assert np.array_equal(host_bits(st.v_cache), st.v_after)
+    rows = sample_rows(st.tb, spec.Hq, 40, seed=123)
+    expect = st.oracle_decode(pairs=rows)
+    got = out.float().cpu().numpy()
+    err = max(float(np.max(np.abs(got[s, h] - expect[i]))) for i, (s, h) in enumerate(rows))
+    say(f"    sampled max abs err {err:.3e} (tol {TOL[spec.dtype]})")
+    assert err <= TOL[spec.dtype]
+    # properties at every row: finite, and a convex combination of V rows
+    assert np.all(np.isfinite(got))
+    assert np.abs(got).max() <= 8.0
