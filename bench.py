@@ -1,0 +1,324 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 13b]
+
+A step is one pass of the whole path over one batch of seeded synthetic
+input, all of it already resident in HBM:
+  copy-on-write block copies (workloads that have any) -> slot mapping ->
+  cache write of the step's new K/V -> decode attention over every sequence.
+W untimed steps, then exactly K timed steps between two device
+synchronisations. HIP events on the launch stream bracket each decode call
+inside the timed region, so the decode kernel's average duration (and from it
+its achieved HBM bandwidth against the 8 TB/s peak) is measured live.
+
+Printed: one JSON line. `value` is the step's algorithmic HBM bytes over the
+step time (GB/s); `decode_tokens_per_s` is sequences / step time. The
+`roofline` object covers the decode kernel; its `traffic` comes from the
+committed rocprofv3 counter summary for that kernel and workload, or is null
+when the kernel sources have changed since those counters were taken. The
+`cpu_baseline` object is the fp64 CPU oracle on the same inputs, on this
+host's cores (test infrastructure, timed for reference only).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+# Sources the decode kernels are built from: counters taken on another
+# version of these no longer describe the kernel that runs.
+DECODE_SOURCES = ["paged_kv_cache_410_amd/csrc/decode_valu.hip",
+                  "paged_kv_cache_410_amd/csrc/decode_mfma.hip",
+                  "paged_kv_cache_410_amd/csrc/decode_reduce.hip",
+                  "paged_kv_cache_410_amd/csrc/pa_device.h",
+                  "paged_kv_cache_410_amd/csrc/pa_launch.h",
+                  "paged_kv_cache_410_amd/csrc/pa_api.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_sources_sha():
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, or None."""
+    path = os.path.join(PROFILES, f"pa_decode_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    text = open(path).read()
+    m_sha = re.search(r"^decode_sources_sha:\s*(\w+)", text, re.M)
+    m_tr = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_sha or not m_tr:
+        return None, "counter summary unreadable"
+    if m_sha.group(1) != decode_sources_sha():
+        return None, "decode sources changed since the counters were taken"
+    return float(m_tr.group(1)), "ok"
+
+
+def algorithmic_bytes(spec, tb):
+    """Bytes the method must move, each element once (not what a kernel moves)."""
+    e = 4 if spec.dtype == "f32" else 2
+    ctx = tb.context_lens.astype("int64")
+    kv = int(ctx.sum()) * spec.Hkv * spec.D * 2 * e                # every K and V row once
+    qo = 2 * spec.B * spec.Hq * spec.D * e                         # q in, out
+    meta = 4 * (int(((ctx + 15) // 16).sum()) + spec.B)            # table entries + lengths
+    decode = kv + qo + meta
+    T = len(tb.slots)
+    write = 2 * 2 * T * spec.Hkv * spec.D * e                      # K, V rows: read + write
+    slots = 4 * 4 * T                                              # seq, pos, table entry, slot
+    copy = 2 * 2 * len(tb.pairs) * spec.Hkv * 16 * spec.D * e      # K, V blocks: read + write
+    return dict(decode=decode, write=write, slots=slots, copy=copy,
+                step=decode + write + slots + copy, flops=4 * int(ctx.sum()) * spec.Hq * spec.D)
+
+
+def unique_decode_bytes(spec, tb):
+    """For shared blocks: K/V bytes of each distinct (physical block, token) read."""
+    e = 4 if spec.dtype == "f32" else 2
+    # a shared block is read by each of its sharers; count its used rows once
+    last_rows = {}
+    for s in range(spec.B):
+        L = int(tb.context_lens[s])
+        for j in range((L + 15) // 16):
+            b = int(tb.block_tables[s, j])
+            last_rows[b] = max(last_rows.get(b, 0), min(16, L - 16 * j))
+    rows = sum(last_rows.values())
+    return rows * spec.Hkv * spec.D * 2 * e + 2 * spec.B * spec.Hq * spec.D * e
+
+
+def cpu_baseline(st_inputs, spec, tb, bytes_decode, budget_s):
+    """The fp64 oracle on the host, on the same inputs: whole decode step, repeated
+    until about `budget_s` seconds of CPU time have been spent (at least once)."""
+    import oracle
+    q, k, v = st_inputs
+    oracle.build()
+    threads = oracle.max_threads()
+    times = []
+    out = None
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        out = oracle.decode(q, k, v, tb.block_tables, tb.context_lens, spec.scale)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= budget_s or len(times) >= 20:
+            break
+    t = sorted(times)[len(times) // 2]
+    return out, dict(value=round(bytes_decode / t / 1e9, 3), unit="GB/s", cores=threads,
+                     kind="oracle",
+                     sample=f"the whole {spec.name} decode step ({spec.B} sequences x {spec.Hq} "
+                            f"heads, fp64 oracle, OpenMP over (sequence, head)), median of "
+                            f"{len(times)} runs",
+                     seconds_per_step=round(t, 4),
+                     decode_tokens_per_s=round(spec.B / t, 2))
+
+
+def host_bits(t):
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="13b", choices=["tiny", "7b", "13b", "gqa", "cow"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-context partition in tokens (default: the library's choice, "
+                         "or the workload's own)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (e.g. under a counter profiler)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-controls", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sequences or kv heads would shard with no exchange, but no multi-GPU run is "
+              "built here)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_410_amd as pa
+    from paged_kv_cache_410_amd import _lib, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(_lib.LIB_PATH):
+        print("bench.py: libpa.so is not built (python -m paged_kv_cache_410_amd.build)",
+              file=sys.stderr)
+        sys.exit(1)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = workloads.CONFIGS[args.workload]
+    log(f"[bench] workload {spec.name}: building tables with the native block manager")
+    tb = workloads.make_tables(spec, pa.BlockManager)
+    T = len(tb.slots)
+    vals = workloads.make_values(spec, tb.NB, T, device="cuda")
+    k_cache, v_cache = vals.k_cache, vals.v_cache
+    q, k_new, v_new = vals.q, vals.k_new, vals.v_new
+    bt = torch.from_numpy(tb.block_tables).to(dev)
+    cl = torch.from_numpy(tb.context_lens).to(dev)
+    step_seq = torch.from_numpy(tb.step_seq).to(dev)
+    step_pos = torch.from_numpy(tb.step_pos).to(dev)
+    pairs = torch.from_numpy(np.ascontiguousarray(tb.pairs)).to(dev)
+    max_ctx = int(tb.context_lens.max())
+    partition = args.partition
+    if partition is None:
+        partition = spec.partition or pa.default_partition(spec.B, spec.Hq, spec.Hkv, spec.D,
+                                                           max_ctx)
+    ws_bytes = pa.decode_workspace_bytes(spec.B, spec.Hq, spec.D, max_ctx, partition)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    slots = torch.empty(T, dtype=torch.int32, device=dev)
+    nbytes = algorithmic_bytes(spec, tb)
+    log(f"[bench] NB={tb.NB} MB={tb.MB} T={T} pairs={len(tb.pairs)} max_ctx={max_ctx} "
+        f"partition={partition} decode bytes={nbytes['decode'] / 1e9:.4f} GB")
+
+    # The copy-on-write copies read blocks the step's writes then change, so a
+    # repeated step starts from pools saved before the first one.
+    if len(tb.pairs):
+        dst = torch.from_numpy(tb.pairs[:, 1].astype(np.int64)).to(dev)
+        k_saved, v_saved = k_cache[dst].clone(), v_cache[dst].clone()
+
+    def step(ev=None):
+        if len(tb.pairs):
+            pa.copy_blocks(k_cache, v_cache, pairs)
+        pa.slot_mapping(bt, step_pos, seq_ids=step_seq, out=slots)
+        pa.write_kv(k_new, v_new, k_cache, v_cache, slots)
+        if ev is not None:
+            ev[0].record()
+        pa.decode(q, k_cache, v_cache, bt, cl, spec.scale, max_ctx, partition=partition,
+                  out=out, workspace=workspace)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_step = wall * 1e3 / args.steps
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    dec_med_ms = sorted(dec_ms)[len(dec_ms) // 2]
+    log(f"[bench] step {ms_step * 1e3:.1f} us, decode avg {dec_avg_ms * 1e3:.1f} us "
+        f"(median {dec_med_ms * 1e3:.1f})")
+
+    controls = {}
+    if not args.no_controls:
+        # A plain device-to-device copy of the decode's K/V byte count: the
+        # bandwidth a streaming kernel reaches here (and the reference the HBM
+        # counters are scaled by).
+        n = nbytes["decode"] // 2 // 16 * 16
+        a = torch.empty(n // 2, dtype=torch.int16, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
+        controls["d2d_copy"] = dict(bytes_read=n, bytes_written=n, us=round(cms * 1e3, 2),
+                                    GBps=round(2 * n / (cms * 1e-3) / 1e9, 1))
+        del a, b
+
+    if len(tb.pairs):
+        k_cache[dst], v_cache[dst] = k_saved, v_saved
+        step()
+        torch.cuda.synchronize()
+
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        log("[bench] oracle on the host (cpu_baseline)")
+        inputs = (host_bits(q), host_bits(k_cache), host_bits(v_cache))
+        if spec.dtype == "f32":
+            inputs = tuple(x.view(np.float32) for x in inputs)
+        expect, cpu = cpu_baseline(inputs, spec, tb, nbytes["decode"], args.cpu_seconds)
+        got = out.float().cpu().numpy().astype(np.float64)
+        parity = float(np.max(np.abs(got - expect)))
+        log(f"[bench] oracle {cpu['seconds_per_step']} s/step on {cpu['cores']} threads; "
+            f"max abs err vs oracle {parity:.3e}")
+
+    traffic, why = read_traffic(spec.name)
+    achieved = nbytes["decode"] / (dec_avg_ms * 1e-3) / 1e9
+    value = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    line = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) + decode tokens/sec",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded; no dataset or weights)",
+        "config": {"workload": f"{spec.name}: B={spec.B} Hq={spec.Hq} Hkv={spec.Hkv} "
+                               f"D={spec.D} block_size=16 {spec.dtype}",
+                   "batch": spec.B, "num_q_heads": spec.Hq, "num_kv_heads": spec.Hkv,
+                   "head_dim": spec.D, "block_size": 16, "partition": partition,
+                   "max_ctx": max_ctx, "mean_ctx": round(float(tb.context_lens.mean()), 1),
+                   "pool_blocks": tb.NB, "new_tokens": T, "cow_pairs": len(tb.pairs),
+                   "parallelism": "none (one GPU)"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s": round(spec.B / (ms_step * 1e-3), 1),
+        "decode_us": round(dec_avg_ms * 1e3, 2),
+        "decode_us_median": round(dec_med_ms * 1e3, 2),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode (one launch per step"
+                     + (", plus the partition merge)" if ws_bytes else ")"),
+                     "traffic_note": why},
+        "cpu_baseline": cpu,
+        "parity_max_abs_err_vs_oracle": parity,
+        "controls": controls,
+    }
+    if spec.name == "cow":
+        ub = unique_decode_bytes(spec, tb)
+        line["unique_decode_bytes"] = ub
+        line["roofline_unique_GBps"] = round(ub / (dec_avg_ms * 1e-3) / 1e9, 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,6 +30,14 @@
 #include "pa_device.h"
 #include "pa_launch.h"
 
+// Waves per workgroup and K/V tiles in flight per wave.
+#ifndef PA_MFMA_WAVES
+#define PA_MFMA_WAVES 2
+#endif
+#ifndef PA_MFMA_DEPTH
+#define PA_MFMA_DEPTH 2
+#endif
+
 namespace pa {
 
 namespace {
@@ -46,22 +54,23 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int k) {
 
 }  // namespace
 
-template <int NW>
+template <int NW, int DEPTH>
 __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P) {
   constexpr int D = 128;
   constexpr int kRowBytes = D * 2;
   constexpr int kPad = 4;  // LDS row padding (floats) against bank conflicts
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  const int w = wave_id();
   const int col = lane & 15;
   const int rg = lane >> 4;
 
-  const int p = blockIdx.x;
+  const GridPos gp = grid_pos();
+  const int p = gp.y;
   const int QG = mfma_q_groups(P.G);
-  const int g = blockIdx.y / QG;
-  const int sub = blockIdx.y % QG;
-  const int s = blockIdx.z;
+  const int g = gp.x / QG;
+  const int sub = gp.x % QG;
+  const int s = gp.z;
   const int q0 = g * P.G + sub * 16;           // first query head of this group
   const int gsub = min(16, P.G - sub * 16);     // real heads in the group
 
@@ -101,25 +110,26 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
   const size_t head_off = (size_t)g * kBlock * kRowBytes;
   const size_t block_stride = (size_t)P.Hkv * kBlock * kRowBytes;
-  const size_t k_lane = (size_t)col * kRowBytes + 8 * rg * 2;       // + 64 B per kk
-  const size_t v_lane = (size_t)(4 * rg) * kRowBytes + 8 * col * 2;  // + 1 row per j
+  const int k_lane = col * kRowBytes + 8 * rg * 2;       // + 64 B per kk
+  const int v_lane = (4 * rg) * kRowBytes + 8 * col * 2;  // + 1 row per j
 
-  auto load = [&](uint4 (&kb)[4], uint4 (&vb)[4], int blk) -> bool {
-    const int b = bt_row[blk];
-    if (b < 0 || b >= P.NB) return false;
-    const size_t off = (size_t)b * block_stride + head_off;
+  // Issue the loads of physical block b's tile into (kb, vb). An id outside
+  // the pool marks the group bad and loads nothing; so does a block that does
+  // not exist (an empty ring refill).
+  auto load = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, bool exists) {
+    const bool valid = b >= 0 && b < P.NB;
+    bad |= exists && !valid;
+    const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
+    const int bytes = exists && valid ? kBlock * kRowBytes : 0;
+    const rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kb[kk] = ld16(kbase + off + k_lane + kk * 64);
+    for (int kk = 0; kk < 4; ++kk) kb[kk] = ld16(rk, k_lane + kk * 64);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vb[j] = ld16(vbase + off + v_lane + (size_t)j * kRowBytes);
-    return true;
+    for (int j = 0; j < 4; ++j) vb[j] = ld16(rv, v_lane + j * kRowBytes);
   };
 
-  auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk, bool ok) {
-    if (!ok) {
-      bad = true;
-      return;
-    }
+  auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
     f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -165,22 +175,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
     }
   };
 
+  // This wave's blocks: first + k * NW, k < nk, through a ring of DEPTH tiles.
   {
-    uint4 ka[4], va[4], kb2[4], vb2[4];
-    int i0 = blk_begin + w;
-    bool ok_a = false, ok_b = false;
-    if (i0 < blk_end) ok_a = load(ka, va, i0);
-    while (i0 < blk_end) {
-      const int i1 = i0 + NW;
-      if (i1 < blk_end) ok_b = load(kb2, vb2, i1);
-      consume(ka, va, i0, ok_a);
-      if (i1 >= blk_end) break;
-      const int i2 = i1 + NW;
-      if (i2 < blk_end) ok_a = load(ka, va, i2);
-      consume(kb2, vb2, i1, ok_b);
-      i0 = i2;
-    }
+    const int first = blk_begin + w;
+    const int nk = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
+    uint4 kb[DEPTH][4], vb[DEPTH][4];
+    block_pipeline<DEPTH>(
+        bt_row, first, NW, nk, lane,
+        [&](int d, int b, bool exists) { load(kb[d], vb[d], b, exists); },
+        [&](int d, int k) { consume(kb[d], vb[d], first + k * NW); });
   }
+
 
   lsum = rows_sum(lsum);  // per query head: sum over the 4 row groups
 
@@ -250,9 +255,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  constexpr int NW = 4;
-  const dim3 grid(p.n_parts, p.Hkv * mfma_q_groups(p.G), p.B), block(NW * kWave);
-  hipLaunchKernelGGL((decode_mfma_kernel<NW>), grid, block, 0, stream, p);
+  constexpr int NW = PA_MFMA_WAVES;
+  constexpr int DEPTH = PA_MFMA_DEPTH;
+  const dim3 grid(p.Hkv * mfma_q_groups(p.G), p.n_parts, p.B), block(NW * kWave);
+  hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

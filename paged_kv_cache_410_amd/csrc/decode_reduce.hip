@@ -10,13 +10,18 @@
 // block by block; partitioning long contexts across workgroups is this
 // library's way to spread one sequence over many compute units.)
 //
-// One wave per (query head, sequence). Lane j of a 64-partition chunk reads
-// (m_j, l_j); the weights are broadcast with readlane while every lane
-// accumulates its own dims of the output row.
+// One workgroup of RW waves per (query head, sequence). Every wave finds M
+// over all partitions; wave w then accumulates partitions w, w + RW, ...,
+// reading kUnroll partial rows per round trip (lane i holds w_j for the i-th
+// partition of the wave's current chunk, broadcast with readlane, while every
+// lane accumulates its own dims of the output row); the waves' sums are
+// combined through LDS.
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
+
+constexpr int kReduceWaves = 4;
 
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<kDppXor1>(x));
@@ -27,9 +32,12 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(DecodeParams P) {
+  constexpr int RW = kReduceWaves;
   constexpr int DPL = D / kWave;  // output dims per lane
-  const int lane = threadIdx.x;
+  constexpr int kUnroll = 8;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = wave_id();
   const int h = blockIdx.x;
   const int s = blockIdx.y;
 
@@ -49,26 +57,59 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams P) {
   M = wave_max(M);
   const float m_use = (M == -INFINITY) ? 0.0f : M;
 
+  // this wave's partitions: j = w + RW * i, i < nw
+  const int nw = w < np ? (np - w + RW - 1) / RW : 0;
   float lpart = 0.0f;
   float acc[DPL];
 #pragma unroll
   for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
-  for (int j0 = 0; j0 < np; j0 += kWave) {
-    const int j = j0 + lane;
+  for (int i0 = 0; i0 < nw; i0 += kWave) {
+    const int i = i0 + lane;
     float wj = 0.0f;
-    if (j < np) {
+    if (i < nw) {
+      const int j = w + RW * i;
       wj = exp2_fast(ml[2 * j] - m_use);
       lpart += wj * ml[2 * j + 1];
     }
-    const int cnt = min(kWave, np - j0);
-    for (int k = 0; k < cnt; ++k) {
-      const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), k));
-      const float* src = po + (size_t)(j0 + k) * D;
+    const int cnt = min(kWave, nw - i0);
+    for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
+      float v[kUnroll][DPL];
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) acc[d] = fmaf(wk, src[d], acc[d]);
+      for (int u = 0; u < kUnroll; ++u) {
+        const int k = min(k0 + u, cnt - 1);  // repeats are weighted by 0 below
+        const float* src = po + (size_t)(w + RW * (i0 + k)) * D;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) v[u][d] = src[d];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float wk = k0 + u < cnt
+                             ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), k0 + u))
+                             : 0.0f;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[d] = fmaf(wk, v[u][d], acc[d]);
+      }
     }
   }
-  const float L = group_sum<kWave>(lpart);
+
+  __shared__ float sm_acc[RW][D];
+  __shared__ float sm_l[RW];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) sm_acc[w][lane * DPL + d] = acc[d];
+  const float lw = group_sum<kWave>(lpart);
+  if (lane == 0) sm_l[w] = lw;
+  __syncthreads();
+  if (w != 0) return;
+  float L = 0.0f;
+#pragma unroll
+  for (int v = 0; v < RW; ++v) L += sm_l[v];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) {
+    float t = 0.0f;
+#pragma unroll
+    for (int v = 0; v < RW; ++v) t += sm_acc[v][lane * DPL + d];
+    acc[d] = t;
+  }
   const float inv = 1.0f / L;
   char* out = reinterpret_cast<char*>(P.out) + (((size_t)s * P.Hq + h) * D + lane * DPL) * sizeof(T);
   if constexpr (sizeof(T) == 2) {
@@ -85,7 +126,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams P) {
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
-  const dim3 grid(p.Hq, p.B), block(kWave);
+  const dim3 grid(p.Hq, p.B), block(kReduceWaves * kWave);
   if (dtype == 1 && D == 128)
     hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, 128>), grid, block, 0, stream, p);
   else if (dtype == 1 && D == 64)

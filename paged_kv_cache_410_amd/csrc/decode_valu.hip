@@ -9,7 +9,9 @@
 // sum, rescaled output), so every K/V byte is read exactly once.
 //
 // Work decomposition (gfx950, wave64):
-//   grid   = (partition p, query head h, sequence s)
+//   grid   = (query head h, partition p, sequence s): the heads of one
+//            sequence are dispatched together, so the tiles of one physical
+//            block (all heads, contiguous in the pool) are read close in time.
 //   block  = NW waves; wave w takes blocks p0 + w, p0 + w + NW, ...
 //   A (block, kv head) tile is 16 rows of D elements, contiguous in memory.
 //   One 16-byte load per lane: LPT = D*e/16 lanes cover one token row, so a
@@ -22,10 +24,19 @@
 //   accumulated without any further data movement.
 //   Each row group of lanes keeps its own online-softmax state; row groups
 //   merge at the end through lane swaps, waves through LDS.
-//   Next-block K/V loads are issued before the current block is consumed
-//   (two register buffers).
+//   K/V tiles are prefetched DEPTH - 1 blocks ahead through a ring of
+//   register buffers; the wave's block ids come from the table 64 at a time
+//   (block_pipeline), so no table read sits between two tile prefetches.
 #include "pa_device.h"
 #include "pa_launch.h"
+
+// Waves per workgroup and K/V tiles in flight per wave.
+#ifndef PA_VALU_WAVES
+#define PA_VALU_WAVES 8
+#endif
+#ifndef PA_VALU_DEPTH
+#define PA_VALU_DEPTH 3
+#endif
 
 namespace pa {
 
@@ -97,7 +108,7 @@ __device__ __forceinline__ void merge_all_rows(float& m, float& l, float (&o)[EP
 
 }  // namespace
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P) {
   constexpr int EPL = Elem<T>::kPerChunk;  // elements per 16-byte lane chunk
   constexpr int LPT = D / EPL;             // lanes per token row
@@ -107,13 +118,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   static_assert(LPT >= 8 && LPT <= 32 && NLD >= 1, "unsupported tile shape");
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  const int w = wave_id();
   const int r = lane / LPT;
   const int c = lane % LPT;
 
-  const int p = blockIdx.x;
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
+  const GridPos gp = grid_pos();
+  const int h = gp.x;
+  const int p = gp.y;
+  const int s = gp.z;
   const int g = h / P.G;
 
   const int ctx = P.context_lens[s];
@@ -144,28 +156,28 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
   const char* kbase = reinterpret_cast<const char*>(P.k_cache);
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
-  const size_t lane_off = (size_t)r * kRowBytes + c * 16;
+  const int lane_off = r * kRowBytes + c * 16;
   const size_t head_off = (size_t)g * kBlock * kRowBytes;
   const size_t block_stride = (size_t)P.Hkv * kBlock * kRowBytes;
 
-  // Load tile `blk` into (kb, vb); false if its block id is out of range.
-  auto load = [&](uint4 (&kb)[NLD], uint4 (&vb)[NLD], int blk) -> bool {
-    const int b = bt_row[blk];
-    if (b < 0 || b >= P.NB) return false;
-    const size_t off = (size_t)b * block_stride + head_off + lane_off;
+  // Issue the loads of physical block b's tile into (kb, vb). An id outside
+  // the pool marks the row bad and loads nothing; so does a block that does
+  // not exist (an empty ring refill).
+  auto load = [&](uint4 (&kb)[NLD], uint4 (&vb)[NLD], int b, bool exists) {
+    const bool valid = b >= 0 && b < P.NB;
+    bad |= exists && !valid;
+    const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
+    const int bytes = exists && valid ? kBlock * kRowBytes : 0;
+    const rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) kb[j] = ld16(kbase + off + (size_t)j * TPI * kRowBytes);
+    for (int j = 0; j < NLD; ++j) kb[j] = ld16(rk, lane_off + j * TPI * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) vb[j] = ld16(vbase + off + (size_t)j * TPI * kRowBytes);
-    return true;
+    for (int j = 0; j < NLD; ++j) vb[j] = ld16(rv, lane_off + j * TPI * kRowBytes);
   };
 
   // Consume one tile: logits, online-softmax update, V accumulation.
-  auto consume = [&](const uint4 (&kb)[NLD], const uint4 (&vb)[NLD], int blk, bool ok) {
-    if (!ok) {
-      bad = true;
-      return;
-    }
+  auto consume = [&](const uint4 (&kb)[NLD], const uint4 (&vb)[NLD], int blk) {
     float x[NLD];
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
@@ -218,23 +230,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
     m = m_new;
   };
 
-  // Two-deep software pipeline over this wave's blocks.
+  // This wave's blocks: first + k * NW, k < nk, through a ring of DEPTH tiles.
   {
-    uint4 ka[NLD], va[NLD], kb2[NLD], vb2[NLD];
-    int i0 = blk_begin + w;
-    bool ok_a = false, ok_b = false;
-    if (i0 < blk_end) ok_a = load(ka, va, i0);
-    while (i0 < blk_end) {
-      const int i1 = i0 + NW;
-      if (i1 < blk_end) ok_b = load(kb2, vb2, i1);
-      consume(ka, va, i0, ok_a);
-      if (i1 >= blk_end) break;
-      const int i2 = i1 + NW;
-      if (i2 < blk_end) ok_a = load(ka, va, i2);
-      consume(kb2, vb2, i1, ok_b);
-      i0 = i2;
-    }
+    const int first = blk_begin + w;
+    const int nk = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
+    uint4 kb[DEPTH][NLD], vb[DEPTH][NLD];
+    block_pipeline<DEPTH>(
+        bt_row, first, NW, nk, lane,
+        [&](int d, int b, bool exists) { load(kb[d], vb[d], b, exists); },
+        [&](int d, int k) { consume(kb[d], vb[d], first + k * NW); });
   }
+
 
   // Row groups of this wave -> one state per D chunk (all rows agree).
   merge_all_rows<LPT, EPL>(m, l, o);
@@ -308,16 +314,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
 }
 
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
-  constexpr int NW = 4;
-  const dim3 grid(p.n_parts, p.Hq, p.B), block(NW * kWave);
+  constexpr int NW = PA_VALU_WAVES;
+  constexpr int DEPTH = PA_VALU_DEPTH;
+  const dim3 grid(p.Hq, p.n_parts, p.B), block(NW * kWave);
   if (dtype == 1 && D == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW, DEPTH>), grid, block, 0, stream, p);
   else if (dtype == 1 && D == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW, DEPTH>), grid, block, 0, stream, p);
   else if (dtype == 0 && D == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW, DEPTH>), grid, block, 0, stream, p);
   else if (dtype == 0 && D == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW, DEPTH>), grid, block, 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -127,7 +127,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (partition < 0 || partition % kBs != 0) return PA_EINVAL;
   if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
   if (D != 64 && D != 128) return PA_EUNSUPPORTED;
-  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return PA_EUNSUPPORTED;
+  if (B > kMaxGridYZ) return PA_EUNSUPPORTED;  // grid z
   if (B == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (MB > 0 && !block_tables))
     return PA_EINVAL;
@@ -138,7 +138,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const size_t need = pa_decode_workspace_bytes(B, Hq, D, max_ctx, partition);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
   if (need > 0 && ((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
-  if (parts > INT32_MAX) return PA_EUNSUPPORTED;
+  if (parts > kMaxGridYZ) return PA_EUNSUPPORTED;  // grid y
 
   pa::DecodeParams p{};
   p.out = out;
@@ -165,7 +165,6 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   }
 
   const bool mfma = dt == PA_BF16 && D == 128 && p.G >= 2;
-  if (mfma && (int64_t)Hkv * pa::mfma_q_groups(p.G) > kMaxGridYZ) return PA_EUNSUPPORTED;
   hipError_t err = mfma ? pa::launch_decode_mfma(p, stream) : pa::launch_decode_valu(p, dt, D, stream);
   if (err != hipSuccess) return PA_EHIP;
   if (parts > 1) {

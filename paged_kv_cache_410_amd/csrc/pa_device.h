@@ -113,4 +113,88 @@ __device__ __forceinline__ SoftmaxScales merge_scales(float m_a, float m_b) {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// The index of this thread's wave in its workgroup, as a wave-uniform value
+// (so branches on it stay scalar and the compiler can count loads in flight
+// exactly instead of draining them at every join).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+// ------------------------------------------------------- workgroup mapping
+// Workgroups of one dispatch go round-robin to the 8 XCDs (workgroup L runs on
+// XCD L % 8). With PA_XCD_SWIZZLE the grid's coordinates are taken from a
+// remapped linear id so that each XCD runs one contiguous range of work items
+// (its own sequences, all their heads) instead of every eighth one.
+#ifndef PA_XCD_SWIZZLE
+#define PA_XCD_SWIZZLE 0
+#endif
+constexpr int kXcds = 8;
+struct GridPos {
+  int x, y, z;
+};
+__device__ __forceinline__ GridPos grid_pos() {
+  if constexpr (PA_XCD_SWIZZLE == 0) {
+    return {(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+  } else {
+    const uint32_t X = gridDim.x, Y = gridDim.y;
+    const uint32_t n = X * Y * gridDim.z;
+    const uint32_t L = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+    const uint32_t xcd = L % kXcds, j = L / kXcds, q = n / kXcds, r = n % kXcds;
+    const uint32_t w = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + j;
+    return {(int)(w % X), (int)((w / X) % Y), (int)(w / (X * Y))};
+  }
+}
+
+// ---------------------------------------------------------------- tile loads
+// A buffer resource over `bytes` bytes at `base` (raw buffer, no stride; the
+// word-3 value is the gfx9-family one for untyped dword loads). A load whose
+// offset falls outside [0, bytes) is dropped by the hardware range check and
+// returns zeros without touching memory, so a resource of 0 bytes turns a
+// tile load into a no-op that still counts as one issued load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Cache-policy bits of the K/V tile loads (0 = default caching).
+#ifndef PA_TILE_AUX
+#define PA_TILE_AUX 2
+#endif
+__device__ __forceinline__ uint4 ld16(rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PA_TILE_AUX));
+}
+
+// Software pipeline over the blocks one wave reads: logical blocks
+// first + k * stride, k = 0 .. n-1, of one block-table row.
+//   load(slot, b, exists)   issue the K/V tile loads of physical block b into
+//                           ring slot `slot`; exists == false asks for an
+//                           empty load (past the wave's last block)
+//   consume(slot, k)        use ring slot `slot` for the wave's k-th block
+// Every step refills one slot unconditionally and only the compute is
+// branched on, so the compiler sees the same loads in flight on every path
+// and waits for exactly the slot it consumes (loads complete in order).
+// Block ids are read from the table 64 at a time (lane j holds the id of the
+// chunk's j-th block, broadcast with readlane): no table read sits between
+// two tile prefetches, where it would drain the ring. Tiles are prefetched
+// DEPTH - 1 blocks ahead; the ring drains once per 64 blocks.
+template <int DEPTH, typename Load, typename Consume>
+__device__ __forceinline__ void block_pipeline(const int32_t* row, int first, int stride, int n,
+                                               int lane, Load&& load, Consume&& consume) {
+  for (int c0 = 0; c0 < n; c0 += kWave) {
+    const int cn = min(kWave, n - c0);
+    const int ids = lane < cn ? row[first + (c0 + lane) * stride] : -1;
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+      load(d, __builtin_amdgcn_readlane(ids, d), d < cn);
+    for (int k0 = 0; k0 < cn; k0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int k = k0 + d;
+        const int kl = k + DEPTH - 1;
+        load((d + DEPTH - 1) % DEPTH, __builtin_amdgcn_readlane(ids, min(kl, kWave - 1)), kl < cn);
+        if (k < cn) consume(d, c0 + k);
+      }
+    }
+  }
+}
+
 }  // namespace pa
