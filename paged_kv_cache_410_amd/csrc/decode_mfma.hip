@@ -37,6 +37,10 @@
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 2
 #endif
+// Minimum waves per SIMD the register allocation must allow.
+#ifndef PA_MFMA_MIN_WAVES
+#define PA_MFMA_MIN_WAVES 3
+#endif
 
 namespace pa {
 
@@ -55,7 +59,8 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int k) {
 }  // namespace
 
 template <int NW, int DEPTH>
-__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P) {
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES)))
+void decode_mfma_kernel(DecodeParams P) {
   constexpr int D = 128;
   constexpr int kRowBytes = D * 2;
   constexpr int kPad = 4;  // LDS row padding (floats) against bank conflicts
@@ -74,18 +79,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
   const int q0 = g * P.G + sub * 16;           // first query head of this group
   const int gsub = min(16, P.G - sub * 16);     // real heads in the group
 
-  const int ctx = P.context_lens[s];
-  const bool bad_ctx = ctx < 0 || ctx > P.ctx_limit;
-  const int nblk = bad_ctx ? 0 : (ctx + kBlock - 1) / kBlock;
-  int blk_begin = 0, blk_end = nblk, nparts_s = nblk > 0 ? 1 : 0;
-  if (P.partition > 0) {
-    const int bpp = P.partition / kBlock;
-    nparts_s = (nblk + bpp - 1) / bpp;
-    blk_begin = p * bpp;
-    blk_end = min(nblk, blk_begin + bpp);
-  }
-  if (p >= max(nparts_s, 1)) return;
+  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
+  const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
+  const int blk_begin = p * bpp;
+  const int first = blk_begin + w;       // this wave's blocks: first, first + NW, ...
 
+  // Start-up loads, issued together before anything waits on them: the query
+  // group, the wave's first 64 block ids (bounded by the partition's table
+  // range, as the context length is not known yet) and the context length.
   // B operand of S^T: Q[q0 + col][32 kk + 8 rg ..], zero for padded heads.
   bf16x8_t qop[4];
   {
@@ -98,6 +99,15 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
       qop[kk] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
+  const int ids0 = first_chunk_ids(bt_row, first, NW, bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB,
+                                   lane);
+  const int ctx = P.context_lens[s];
+
+  const bool bad_ctx = ctx < 0 || ctx > P.ctx_limit;
+  const int nblk = bad_ctx ? 0 : (ctx + kBlock - 1) / kBlock;
+  const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
+  const int nparts_s = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
+  if (p >= max(nparts_s, 1)) return;  // partition past this sequence's end
 
   float m = -INFINITY, lsum = 0.0f;
   f32x4_t acc[8];
@@ -105,7 +115,6 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
   for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   bool bad = bad_ctx;
 
-  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
   const char* kbase = reinterpret_cast<const char*>(P.k_cache);
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
   const size_t head_off = (size_t)g * kBlock * kRowBytes;
@@ -113,14 +122,16 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
   const int k_lane = col * kRowBytes + 8 * rg * 2;       // + 64 B per kk
   const int v_lane = (4 * rg) * kRowBytes + 8 * col * 2;  // + 1 row per j
 
-  // Issue the loads of physical block b's tile into (kb, vb). An id outside
-  // the pool marks the group bad and loads nothing; so does a block that does
-  // not exist (an empty ring refill).
-  auto load = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, bool exists) {
+  // Issue the loads of physical block b's tile (logical block blk) into
+  // (kb, vb). An id outside the pool marks the group bad and loads nothing;
+  // so does a block that does not exist (an empty ring refill).
+  auto load = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, int blk, bool exists) {
     const bool valid = b >= 0 && b < P.NB;
     bad |= exists && !valid;
     const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
-    const int bytes = exists && valid ? kBlock * kRowBytes : 0;
+    // only the block's rows inside the context are fetched (the rest read as 0)
+    const int rows = min(kBlock, ctx - blk * kBlock);
+    const int bytes = exists && valid ? rows * kRowBytes : 0;
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
@@ -177,12 +188,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams P)
 
   // This wave's blocks: first + k * NW, k < nk, through a ring of DEPTH tiles.
   {
-    const int first = blk_begin + w;
     const int nk = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
     uint4 kb[DEPTH][4], vb[DEPTH][4];
     block_pipeline<DEPTH>(
-        bt_row, first, NW, nk, lane,
-        [&](int d, int b, bool exists) { load(kb[d], vb[d], b, exists); },
+        bt_row, first, NW, nk, lane, ids0,
+        [&](int d, int b, int k, bool exists) { load(kb[d], vb[d], b, first + k * NW, exists); },
         [&](int d, int k) { consume(kb[d], vb[d], first + k * NW); });
   }
 

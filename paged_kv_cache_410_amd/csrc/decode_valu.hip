@@ -128,22 +128,26 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const int s = gp.z;
   const int g = h / P.G;
 
+  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
+  const size_t row_qo = ((size_t)s * P.Hq + h) * D;
+  const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
+  const int blk_begin = p * bpp;
+  const int first = blk_begin + w;       // this wave's blocks: first, first + NW, ...
+
+  // Start-up loads, issued together before anything waits on them: the query
+  // chunk, the wave's first 64 block ids (bounded by the partition's table
+  // range, as the context length is not known yet) and the context length.
+  const uint4 qraw = ld16(reinterpret_cast<const char*>(P.q) + row_qo * sizeof(T) + c * 16);
+  const int ids0 = first_chunk_ids(bt_row, first, NW, bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB,
+                                   lane);
   const int ctx = P.context_lens[s];
+
   const bool bad_ctx = ctx < 0 || ctx > P.ctx_limit;
   const int nblk = bad_ctx ? 0 : (ctx + kBlock - 1) / kBlock;
-  int blk_begin = 0, blk_end = nblk, nparts_s = nblk > 0 ? 1 : 0;
-  if (P.partition > 0) {
-    const int bpp = P.partition / kBlock;
-    nparts_s = (nblk + bpp - 1) / bpp;
-    blk_begin = p * bpp;
-    blk_end = min(nblk, blk_begin + bpp);
-  }
+  const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
+  const int nparts_s = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
   if (p >= max(nparts_s, 1)) return;  // partition past this sequence's end
 
-  const size_t row_qo = ((size_t)s * P.Hq + h) * D;
-
-  // Query chunk c of this head.
-  const uint4 qraw = ld16(reinterpret_cast<const char*>(P.q) + row_qo * sizeof(T) + c * 16);
   float qf[EPL];
   Elem<T>::unpack(qraw, qf);
 
@@ -153,21 +157,22 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
   bool bad = bad_ctx;
 
-  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
   const char* kbase = reinterpret_cast<const char*>(P.k_cache);
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
   const int lane_off = r * kRowBytes + c * 16;
   const size_t head_off = (size_t)g * kBlock * kRowBytes;
   const size_t block_stride = (size_t)P.Hkv * kBlock * kRowBytes;
 
-  // Issue the loads of physical block b's tile into (kb, vb). An id outside
-  // the pool marks the row bad and loads nothing; so does a block that does
-  // not exist (an empty ring refill).
-  auto load = [&](uint4 (&kb)[NLD], uint4 (&vb)[NLD], int b, bool exists) {
+  // Issue the loads of physical block b's tile (logical block blk) into
+  // (kb, vb). An id outside the pool marks the row bad and loads nothing;
+  // so does a block that does not exist (an empty ring refill).
+  auto load = [&](uint4 (&kb)[NLD], uint4 (&vb)[NLD], int b, int blk, bool exists) {
     const bool valid = b >= 0 && b < P.NB;
     bad |= exists && !valid;
     const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
-    const int bytes = exists && valid ? kBlock * kRowBytes : 0;
+    // only the block's rows inside the context are fetched (the rest read as 0)
+    const int rows = min(kBlock, ctx - blk * kBlock);
+    const int bytes = exists && valid ? rows * kRowBytes : 0;
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
@@ -232,12 +237,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
 
   // This wave's blocks: first + k * NW, k < nk, through a ring of DEPTH tiles.
   {
-    const int first = blk_begin + w;
     const int nk = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
     uint4 kb[DEPTH][NLD], vb[DEPTH][NLD];
     block_pipeline<DEPTH>(
-        bt_row, first, NW, nk, lane,
-        [&](int d, int b, bool exists) { load(kb[d], vb[d], b, exists); },
+        bt_row, first, NW, nk, lane, ids0,
+        [&](int d, int b, int k, bool exists) { load(kb[d], vb[d], b, first + k * NW, exists); },
         [&](int d, int k) { consume(kb[d], vb[d], first + k * NW); });
   }
 

@@ -165,9 +165,10 @@ __device__ __forceinline__ uint4 ld16(rsrc_t r, int off) {
 
 // Software pipeline over the blocks one wave reads: logical blocks
 // first + k * stride, k = 0 .. n-1, of one block-table row.
-//   load(slot, b, exists)   issue the K/V tile loads of physical block b into
-//                           ring slot `slot`; exists == false asks for an
-//                           empty load (past the wave's last block)
+//   load(slot, b, k, exists) issue the K/V tile loads of physical block b,
+//                           the wave's k-th block, into ring slot `slot`;
+//                           exists == false asks for an empty load (past the
+//                           wave's last block; k is then meaningless)
 //   consume(slot, k)        use ring slot `slot` for the wave's k-th block
 // Every step refills one slot unconditionally and only the compute is
 // branched on, so the compiler sees the same loads in flight on every path
@@ -176,21 +177,32 @@ __device__ __forceinline__ uint4 ld16(rsrc_t r, int off) {
 // chunk's j-th block, broadcast with readlane): no table read sits between
 // two tile prefetches, where it would drain the ring. Tiles are prefetched
 // DEPTH - 1 blocks ahead; the ring drains once per 64 blocks.
+//
+// ids0 is the first chunk's ids, loaded by the caller (first_chunk_ids) before
+// it waits on anything else, so the table read overlaps the kernel's other
+// start-up loads.
+__device__ __forceinline__ int first_chunk_ids(const int32_t* row, int first, int stride, int lim,
+                                               int lane) {
+  const int i = first + lane * stride;
+  return i < lim ? row[i] : -1;
+}
+
 template <int DEPTH, typename Load, typename Consume>
 __device__ __forceinline__ void block_pipeline(const int32_t* row, int first, int stride, int n,
-                                               int lane, Load&& load, Consume&& consume) {
+                                               int lane, int ids0, Load&& load, Consume&& consume) {
   for (int c0 = 0; c0 < n; c0 += kWave) {
     const int cn = min(kWave, n - c0);
-    const int ids = lane < cn ? row[first + (c0 + lane) * stride] : -1;
+    const int ids = c0 == 0 ? ids0 : (lane < cn ? row[first + (c0 + lane) * stride] : -1);
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d)
-      load(d, __builtin_amdgcn_readlane(ids, d), d < cn);
+      load(d, __builtin_amdgcn_readlane(ids, d), c0 + d, d < cn);
     for (int k0 = 0; k0 < cn; k0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
         const int k = k0 + d;
         const int kl = k + DEPTH - 1;
-        load((d + DEPTH - 1) % DEPTH, __builtin_amdgcn_readlane(ids, min(kl, kWave - 1)), kl < cn);
+        load((d + DEPTH - 1) % DEPTH, __builtin_amdgcn_readlane(ids, min(kl, kWave - 1)), c0 + kl,
+             kl < cn);
         if (k < cn) consume(d, c0 + k);
       }
     }

@@ -40,6 +40,10 @@ SMALL = {
     "gqa_bf16_d64": Spec("gqa_bf16_d64", "bf16", 3, 8, 2, 64, seed=19, lengths=("uniform", 1, 300)),
     "exact_blocks": Spec("exact_blocks", "bf16", 4, 2, 2, 128, seed=20,
                          lengths=("fixed", [16, 32, 48, 512])),
+    # unsplit contexts longer than one 64-block id chunk per wave (8 waves x 64 x 16 tokens)
+    "long_mha": Spec("long_mha", "bf16", 2, 2, 2, 128, seed=23, lengths=("fixed", [9000, 20000])),
+    "long_f32": Spec("long_f32", "f32", 2, 2, 2, 64, seed=24, lengths=("fixed", [8200, 17000])),
+    "long_gqa": Spec("long_gqa", "bf16", 2, 16, 2, 128, seed=25, lengths=("fixed", [2100, 5000])),
     "cow_small": Spec("cow_small", "bf16", 8, 4, 4, 128, seed=21, lengths=("cow",),
                       cow=dict(prompts=2, samples=4, prompt_len=96, r_max=15, tail_lo=1,
                                tail_hi=40)),
