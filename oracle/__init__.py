@@ -7,6 +7,7 @@ oracle never imports the library.
 
 Contents
   decode(...)        fp64 paged attention, C (pa_oracle.c -> liboracle.so)
+  multi_query(...)   fp64 causal attention of several new tokens per sequence
   cache_ops          slot mapping, cache write, block copy (numpy bit moves)
   blockmgr           free list / block tables / refcounts / copy-on-write
   dense              textbook contiguous attention (pins the C decode)
@@ -58,6 +59,13 @@ def _load():
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64,
             ctypes.c_int32]
+        lib.oracle_multi_query.restype = ctypes.c_int
+        lib.oracle_multi_query.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_float, ctypes.c_int32, ctypes.c_int32]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -116,4 +124,41 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, pairs=None, n
                            pr_ptr, n, int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_decode failed ({rc}): bad argument or block id out of range")
+    return out
+
+
+def multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                n_threads=0):
+    """fp64 causal attention of several new tokens per sequence.
+
+    q [Tq, Hq, D]; sequence s owns rows query_start[s] .. query_start[s+1]-1,
+    the last n_s tokens of its context (row i at position ctx_s - n_s + i,
+    attending to positions 0 .. ctx_s - n_s + i). Element types as decode().
+    Returns float64 [Tq, Hq, D].
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q)
+    k_cache = np.ascontiguousarray(k_cache)
+    v_cache = np.ascontiguousarray(v_cache)
+    dt = _dtype_code(q)
+    if _dtype_code(k_cache) != dt or _dtype_code(v_cache) != dt:
+        raise TypeError("q, k_cache and v_cache must share one element type")
+    Tq, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    if v_cache.shape != k_cache.shape or Dk != D:
+        raise ValueError("shape mismatch")
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    B = cl.shape[0]
+    if bt.ndim != 2 or bt.shape[0] != B or qs.shape != (B + 1,):
+        raise ValueError("block_tables / query_start shape mismatch")
+    out = np.empty((Tq, Hq, D), dtype=np.float64)
+    rc = lib.oracle_multi_query(out.ctypes.data, q.ctypes.data, k_cache.ctypes.data,
+                                v_cache.ctypes.data, bt.ctypes.data, cl.ctypes.data,
+                                qs.ctypes.data, B, Tq, Hq, Hkv, D, bs, NB, bt.shape[1],
+                                float(np.float32(scale)), dt, int(n_threads))
+    if rc != 0:
+        raise ValueError(f"oracle_multi_query failed ({rc}): bad argument, a chunk longer "
+                         "than its context, or a block id out of range")
     return out

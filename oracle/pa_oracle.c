@@ -40,6 +40,12 @@
  * The pool layout is [num_blocks][num_kv_heads][bs][head_dim], row-major, for
  * both K and V (the pages fix no layout; this is the reading taken).
  *
+ * Several new tokens per sequence (oracle_multi_query): each new token is a
+ * query of its own, at its logical position, and attends to every position up
+ * to and including its own (the same look-back rule the decode step applies
+ * to its single new token, applied token by token), as when a prompt is
+ * processed in chunks or several drafted tokens are checked in one pass.
+ *
  * Everything is accumulated in double. bf16 inputs are widened exactly
  * (the 16 stored bits are the top half of an IEEE binary32). The softmax is
  * the two-pass textbook form (all logits first, then the max, then the
@@ -68,21 +74,18 @@ static double widen(const void* base, size_t idx, int dtype) {
   return (double)f;
 }
 
-/* One (sequence s, query head h) output row, written to out[0 .. D-1].
- * Returns 0 on success, -1 if a block id read from the table is out of range
- * (the oracle checks what the GPU library takes as a precondition). */
-static int decode_one(double* out, const void* q, const void* k_cache,
-                      const void* v_cache, const int32_t* block_tables,
-                      const int32_t* context_lens, int32_t s, int32_t h,
-                      int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
-                      int32_t NB, int32_t MB, double scale, int dtype) {
-  const int32_t L = context_lens[s];
+/* Attention of one query row over the first L logical tokens of table row s,
+ * kv head g: the row q[q_off .. q_off + D - 1] against K/V rows t = 0 .. L-1,
+ * written to out[0 .. D-1]. Returns 0 on success, -1 if a block id read from
+ * the table is out of range (the oracle checks what the GPU library takes as
+ * a precondition), -2 if out of memory. */
+static int attend(double* out, const void* q, size_t q_off, int32_t L,
+                  const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, int32_t s, int32_t g,
+                  int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                  double scale, int dtype) {
   for (int32_t d = 0; d < D; ++d) out[d] = 0.0;
   if (L <= 0) return 0; /* empty context: output defined as zeros */
-
-  const int32_t G = Hq / Hkv;
-  const int32_t g = h / G;
-  const size_t q_off = ((size_t)s * Hq + h) * D;
 
   double* x = (double*)malloc(sizeof(double) * (size_t)L);
   if (!x) return -2;
@@ -122,6 +125,19 @@ static int decode_one(double* out, const void* q, const void* k_cache,
   for (int32_t d = 0; d < D; ++d) out[d] /= Z;
   free(x);
   return 0;
+}
+
+/* One (sequence s, query head h) decode row: the sequence's single query
+ * attends over all context_lens[s] cached tokens. */
+static int decode_one(double* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t s, int32_t h,
+                      int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+                      int32_t NB, int32_t MB, double scale, int dtype) {
+  const int32_t G = Hq / Hkv;
+  return attend(out, q, ((size_t)s * Hq + h) * D, context_lens[s], k_cache,
+                v_cache, block_tables, s, h / G, Hkv, D, bs, NB, MB, scale,
+                dtype);
 }
 
 /*
@@ -173,6 +189,65 @@ int oracle_decode(double* out, const void* q, const void* k_cache,
                        context_lens, s, h, Hq, Hkv, D, bs, NB, MB,
                        (double)scale, dtype);
     if (r < err) err = r;
+  }
+  (void)n_threads;
+  return err;
+}
+
+/*
+ * oracle_multi_query — several new query tokens per sequence, causal.
+ *
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1 (n_s rows);
+ * they are the last n_s tokens of its context, so row i (0-based) sits at
+ * logical position ctx_s - n_s + i and attends to positions 0 .. ctx_s - n_s
+ * + i, its own included: the decode rule applied to each new token in turn
+ * (chunked prefill, or checking several drafted tokens at once). With
+ * n_s = 1 for every s this is oracle_decode.
+ *
+ *   out          double [Tq][Hq][D]
+ *   q            [Tq][Hq][D]            dtype-tagged
+ *   query_start  int32 [B+1], non-decreasing, query_start[0] = 0,
+ *                query_start[B] = Tq
+ * A sequence with n_s > ctx_s is an error (-1).
+ */
+int oracle_multi_query(double* out, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* query_start,
+                       int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                       float scale, int32_t dtype, int32_t n_threads) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
+      !query_start)
+    return -1;
+  if (B < 0 || Tq < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || MB < 0 ||
+      NB < 0)
+    return -1;
+  if (Hq % Hkv != 0) return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  if (query_start[0] != 0 || query_start[B] != Tq) return -1;
+  for (int32_t s = 0; s < B; ++s) {
+    const int32_t n = query_start[s + 1] - query_start[s];
+    if (n < 0 || n > context_lens[s]) return -1;
+  }
+  const int32_t G = Hq / Hkv;
+  const int64_t n_rows = (int64_t)Tq * Hq;
+  int err = 0;
+#ifdef _OPENMP
+  if (n_threads <= 0) n_threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads) reduction(min : err)
+#endif
+  for (int64_t r = 0; r < n_rows; ++r) {
+    const int32_t j = (int32_t)(r / Hq);
+    const int32_t h = (int32_t)(r % Hq);
+    int32_t s = 0;
+    while (query_start[s + 1] <= j) ++s; /* the sequence owning row j */
+    const int32_t n = query_start[s + 1] - query_start[s];
+    const int32_t i = j - query_start[s];
+    const int32_t L = context_lens[s] - n + i + 1;
+    int rc = attend(out + (size_t)r * D, q, ((size_t)j * Hq + h) * D, L,
+                    k_cache, v_cache, block_tables, s, h / G, Hkv, D, bs, NB,
+                    MB, (double)scale, dtype);
+    if (rc < err) err = rc;
   }
   (void)n_threads;
   return err;
