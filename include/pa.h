@@ -136,12 +136,13 @@ int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv,
                                     int32_t D, int32_t max_ctx);
 
 /*
- * pa_decode_workspace_bytes — device workspace pa_decode needs for this
- * split: 0 when partition == 0 or max_ctx <= partition, otherwise room for
- * per-partition partial results (fp32 running max, sum and unnormalised
- * output row per (sequence, query head, partition)).
+ * pa_decode_workspace_bytes — device workspace pa_decode (rows = B) or
+ * pa_multi_query (rows = Tq) needs for this split: 0 when partition == 0 or
+ * max_ctx <= partition, otherwise room for per-partition partial results
+ * (fp32 running max, sum and unnormalised output row per (query row, query
+ * head, partition)).
  */
-size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+size_t pa_decode_workspace_bytes(int32_t rows, int32_t Hq, int32_t D,
                                  int32_t max_ctx, int32_t partition);
 
 /*
@@ -186,6 +187,45 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
                     int32_t max_ctx, float scale, int32_t partition,
                     void* workspace, size_t workspace_bytes, pa_dtype dt,
                     hipStream_t stream);
+
+/*
+ * pa_multi_query — causal attention of several new tokens per sequence over
+ * the paged cache (a prompt processed in chunks, or several drafted tokens
+ * checked in one pass).
+ *
+ * "vLLM & PagedAttention" (completesystemdesign.dev), section 01: a new
+ * token attends over the keys and values of every earlier token; here each
+ * new token of a chunk does so in turn, its own and the chunk's earlier
+ * tokens included. [P1] section 2: K/V are read through the block table.
+ * Sequence s owns query rows query_start[s] .. query_start[s+1]-1 (n_s rows),
+ * the last n_s tokens of its context (write their K/V with pa_write_kv
+ * first). Row i (0-based) sits at position ctx_s - n_s + i and, for query head
+ * h and kv head g = h / (Hq / Hkv):
+ *     out[row][h] = sum_t softmax(x)_t V_t,  x_t = scale * dot(q[row][h], K_t),
+ *     t = 0 .. ctx_s - n_s + i.
+ * With every n_s = 1 this is pa_decode. Accumulation is fp32; bf16 output is
+ * rounded to nearest even.
+ *
+ *   out, q         [Tq][Hq][D]; out must not alias any input
+ *   query_start    int32 [B + 1], device memory, non-decreasing, with
+ *                  query_start[0] = 0 and query_start[B] = Tq
+ *   max_q          host-side upper bound on every n_s (sizes the grid)
+ *   workspace      at least pa_decode_workspace_bytes(Tq, Hq, D, max_ctx,
+ *                  partition) bytes, 256-byte aligned
+ * Other arguments as pa_decode. A sequence whose n_s exceeds its context
+ * length or max_q, or whose context length is invalid, gets all-NaN rows
+ * (those among its first max_q); a sequence whose rows fall outside
+ * [0, Tq) gets none written. B == 0 or Tq == 0 is a no-op.
+ */
+pa_status pa_multi_query(void* out, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens,
+                         const int32_t* query_start, int32_t B, int32_t Tq,
+                         int32_t max_q, int32_t Hq, int32_t Hkv, int32_t D,
+                         int32_t bs, int32_t NB, int32_t MB, int32_t max_ctx,
+                         float scale, int32_t partition, void* workspace,
+                         size_t workspace_bytes, pa_dtype dt,
+                         hipStream_t stream);
 
 /*
  * Block manager — host-side bookkeeping of the physical block pool.

@@ -10,6 +10,8 @@ provides device memory and streams only.
     copy_blocks(k_cache, v_cache, pairs)                      (in place)
     decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx,
            partition=None, out=None, workspace=None)     -> [B, Hq, D]
+    multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                scale, max_ctx, max_q, partition=None)   -> [Tq, Hq, D]
     BlockManager(num_blocks, block_size=16, free_order=None)
 
 Pools are [num_blocks, num_kv_heads, 16, head_dim] tensors (fp32 or bf16).
@@ -22,7 +24,8 @@ import torch
 
 from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PAError, check, lib  # noqa: F401
 
-__all__ = ["slot_mapping", "write_kv", "copy_blocks", "decode", "decode_workspace_bytes",
+__all__ = ["slot_mapping", "write_kv", "copy_blocks", "decode", "multi_query",
+           "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError"]
 
 BLOCK_SIZE = 16
@@ -157,6 +160,50 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx, part
                               block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs,
                               NB, MB, int(max_ctx), float(scale), int(partition), ws_ptr, ws_bytes,
                               _dt(q), _stream(dev)), "pa_decode")
+    return out
+
+
+def multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, max_ctx,
+                max_q, partition=None, out=None, workspace=None):
+    """Causal attention of several new tokens per sequence (pa_multi_query).
+
+    q [Tq, Hq, D]; query_start int32 [B + 1]: sequence s owns rows
+    query_start[s] .. query_start[s+1]-1, the last tokens of its context.
+    max_q bounds the rows per sequence."""
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    _i32(query_start, "query_start")
+    Tq, Hq, Dq = q.shape
+    if Dq != D or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [Tq, Hq, D] with the pools' dtype")
+    B = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start.shape != (B + 1,):
+        raise ValueError("block_tables must be [B, MB] and query_start [B + 1]")
+    MB = block_tables.shape[1]
+    if partition is None:
+        with torch.cuda.device(q.device):
+            partition = default_partition(max(Tq, 1), Hq, Hkv, D, max_ctx)
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = decode_workspace_bytes(Tq, Hq, D, max_ctx, partition)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    tensors = [q, k_cache, v_cache, block_tables, context_lens, query_start, out]
+    if workspace is not None:
+        tensors.append(workspace)
+    dev = _dev(*tensors)
+    with torch.cuda.device(dev):
+        check(lib().pa_multi_query(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                   v_cache.data_ptr(), block_tables.data_ptr(),
+                                   context_lens.data_ptr(), query_start.data_ptr(), B, Tq,
+                                   int(max_q), Hq, Hkv, D, bs, NB, MB, int(max_ctx), float(scale),
+                                   int(partition), ws_ptr, ws_bytes, _dt(q), _stream(dev)),
+              "pa_multi_query")
     return out
 
 

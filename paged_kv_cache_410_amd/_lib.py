@@ -24,6 +24,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_i32, c_vp]),
+    "pa_multi_query": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
+                               c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32,
+                               c_vp, c_sz, c_i32, c_vp]),
     "pa_bm_create": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_i32, c_vp]),
     "pa_bm_destroy": (None, [c_vp]),
     "pa_bm_add_seq": (c_i32, [c_vp, c_i32p]),

@@ -1,32 +1,39 @@
-// Paged decode attention for grouped query heads, matrix-core path
-// (bf16, head_dim 128, G = Hq / Hkv query heads per kv head).
+// Paged attention on the matrix cores (bf16, head_dim 128): grouped query
+// heads, and several new query tokens per sequence.
 //
 // Method: as the vector path ("Why OS Virtual Memory Paging Saved LLM
 // Inference" (a8q9.cn), section 2: K/V gathered block by block through the
-// block table; online softmax over blocks). With G query heads sharing one
-// kv head, each 16-token K tile meets a G x 128 query block: a small, real
-// contraction, done on the MFMA units so that every K/V byte is read once
-// for all G heads.
+// block table; online softmax over blocks). A kv head serves the G query
+// heads of its group and, with several new tokens per sequence, every new
+// token's row: each 16-token K tile meets up to 16 such (row, head) columns,
+// a small real contraction done on the MFMA units, so that every K/V byte is
+// read once per 16 columns instead of once per column.
+//
+// Columns: the n x G (query row, head of the group) pairs of a sequence and
+// kv head, row-major, cut into tiles of 16; one workgroup per (tile,
+// partition, sequence). Column (i, q) attends over its row's causal prefix
+// (ctx - n + i + 1 tokens): a per-column limit masks the logits. The decode
+// step is n = 1: the columns are the G heads.
 //
 // Layouts (wave64; lane = 16 * rg + col, rg = lane / 16, col = lane % 16):
 //   S^T = K Q^T with v_mfma_f32_16x16x32_bf16, 4 steps over D (kk = 0..3):
 //     A (16 tokens x 32 dims): lane holds K[t = col][32 kk + 8 rg + 0..7]
-//     B (32 dims x 16 heads):  lane holds Q[q = col][32 kk + 8 rg + 0..7]
+//     B (32 dims x 16 cols):   lane holds Q[q = col][32 kk + 8 rg + 0..7]
 //     result: lane holds S^T[t = 4 rg + i][q = col], i = 0..3
-//   So every lane owns one query head (col) and 4 tokens: the softmax max is
-//   an in-lane max plus a max over the 4 row groups.
+//   So every lane owns one column (col) and 4 tokens: the softmax max is an
+//   in-lane max plus a max over the 4 row groups.
 //   O^T = V^T P^T with v_mfma_f32_16x16x16_bf16 (K dimension = 16 tokens):
 //     V is loaded row-wise: lane holds V[t = 4 rg + j][8 col + 0..7], j = 0..3
 //     (each load instruction reads 4 whole 256-byte rows).
 //     For output tile e (e = 0..7) the A operand (16 "dims" x 16 tokens) is
 //     {V[4 rg + j][8 col + e]}_j, i.e. row m = col stands for dim 8 m + e;
 //     it is assembled from the loaded registers with byte permutes.
-//     B (16 tokens x 16 heads): lane holds P^T[t = 4 rg + j][q = col] = the
+//     B (16 tokens x 16 cols): lane holds P^T[t = 4 rg + j][q = col] = the
 //     lane's own 4 probabilities, rounded to bf16.
 //     result tile e: lane holds O^T[d = 8 (4 rg + i) + e][q = col].
-//   Every accumulator a lane holds belongs to its own query head, so the
+//   Every accumulator a lane holds belongs to its own column, so the
 //   online-softmax rescale is a per-lane multiply.
-// Heads past G in a 16-wide group are zero-padded and never written.
+// Columns past the last real one are zero-padded and never written.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -72,42 +79,55 @@ void decode_mfma_kernel(DecodeParams P) {
 
   const GridPos gp = grid_pos();
   const int p = gp.y;
-  const int QG = mfma_q_groups(P.G);
-  const int g = gp.x / QG;
-  const int sub = gp.x % QG;
+  const int g = gp.x / P.n_tiles;     // kv head
+  const int tile = gp.x % P.n_tiles;  // 16-column tile of this kv head's (row, head) pairs
   const int s = gp.z;
-  const int q0 = g * P.G + sub * 16;           // first query head of this group
-  const int gsub = min(16, P.G - sub * 16);     // real heads in the group
 
   const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
   const int blk_begin = p * bpp;
   const int first = blk_begin + w;       // this wave's blocks: first, first + NW, ...
 
-  // Start-up loads, issued together before anything waits on them: the query
-  // group, the wave's first 64 block ids (bounded by the partition's table
-  // range, as the context length is not known yet) and the context length.
-  // B operand of S^T: Q[q0 + col][32 kk + 8 rg ..], zero for padded heads.
+  // Start-up loads, issued before anything waits on them: the wave's first 64
+  // block ids (bounded by the partition's table range, as the context length
+  // is not known yet), the sequence's rows and context length, the queries.
+  const int ids0 = first_chunk_ids(bt_row, first, NW, bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB,
+                                   lane);
+  const SeqRows sr = seq_rows(P, s);
+  // Columns of this tile: global column gc = 16 tile + col of the n x G grid
+  // of (query row, head of the group), row-major; gc >= n G is padding.
+  const int ncols = min(sr.n, P.max_q) * P.G;
+  const int c_begin = 16 * tile;
+  if (c_begin >= ncols) return;  // no real column
+  const int c_end = min(ncols, c_begin + 16);
+  const int gc = c_begin + col;
+  const bool col_ok = gc < c_end;
+  const int gcl = col_ok ? gc : c_end - 1;  // padded lanes shadow a real column
+  const int qi = gcl / P.G;                 // this lane's query row
+  const int qh = g * P.G + gcl % P.G;       // and query head
+  const int qrow = sr.first + qi;
+
+  // B operand of S^T: Q[column col][32 kk + 8 rg ..], zero for padded columns.
   bf16x8_t qop[4];
   {
-    const char* qrow = reinterpret_cast<const char*>(P.q) +
-                       ((size_t)s * P.Hq + q0 + min(col, gsub - 1)) * kRowBytes;
+    const char* qp = reinterpret_cast<const char*>(P.q) + ((size_t)qrow * P.Hq + qh) * kRowBytes;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      uint4 u = ld16(qrow + (32 * kk + 8 * rg) * 2);
-      if (col >= gsub) u = make_uint4(0, 0, 0, 0);
+      uint4 u = ld16(qp + (32 * kk + 8 * rg) * 2);
+      if (!col_ok) u = make_uint4(0, 0, 0, 0);
       qop[kk] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
-  const int ids0 = first_chunk_ids(bt_row, first, NW, bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB,
-                                   lane);
-  const int ctx = P.context_lens[s];
 
-  const bool bad_ctx = ctx < 0 || ctx > P.ctx_limit;
-  const int nblk = bad_ctx ? 0 : (ctx + kBlock - 1) / kBlock;
+  // Context of each column (its row's causal prefix) and of the whole tile.
+  const int ctx_col = sr.row_ctx(qi);                       // this lane's column
+  const int ctx_min = sr.row_ctx(c_begin / P.G);            // first column's row
+  const int ctx = sr.row_ctx((c_end - 1) / P.G);            // last column's row: the longest
+  const bool bad_ctx = sr.bad;
+  const int nblk = (ctx + kBlock - 1) / kBlock;
   const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
   const int nparts_s = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
-  if (p >= max(nparts_s, 1)) return;  // partition past this sequence's end
+  if (p >= max(nparts_s, 1)) return;  // partition past the tile's longest context
 
   float m = -INFINITY, lsum = 0.0f;
   f32x4_t acc[8];
@@ -147,20 +167,17 @@ void decode_mfma_kernel(DecodeParams P) {
       st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[kk]), qop[kk],
                                                   st, 0, 0, 0);
     const int tok0 = blk * kBlock + 4 * rg;
-    const bool partial = blk * kBlock + kBlock > ctx;  // wave-uniform
+    // Some column masks some row of this block (wave-uniform).
+    const bool partial = blk * kBlock + kBlock > ctx_min;
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = st[i] * P.qscale;
-      if (partial && tok0 + i >= ctx) x[i] = -INFINITY;
+      if (partial && tok0 + i >= ctx_col) x[i] = -INFINITY;
     }
-    uint4 vb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      vb[j] = vbin[j];
-      // rows past the context may hold anything (even NaN): select, not multiply
-      if (partial && tok0 + j >= ctx) vb[j] = make_uint4(0, 0, 0, 0);
-    }
+    // Rows at or past the tile's longest context were not fetched (the tile's
+    // buffer range ends there) and read as zeros, never as stale or NaN data.
+    const uint4 (&vb)[4] = vbin;
     const float mx = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
@@ -220,11 +237,18 @@ void decode_mfma_kernel(DecodeParams P) {
   bool any_bad = false;
 #pragma unroll
   for (int v = 0; v < NW; ++v) any_bad |= sm_bad[v] != 0;
-  const bool split_out = P.partition > 0 && nparts_s > 1;
-  // thread -> (head qq, 8-dim chunk ch)
+  // thread -> (column qq, 8-dim chunk ch)
   for (int t = threadIdx.x; t < 16 * 16; t += NW * kWave) {
     const int qq = t >> 4, ch = t & 15;
-    if (qq >= gsub) continue;
+    const int c = c_begin + qq;
+    if (c >= c_end) continue;
+    const int i = c / P.G;
+    const int h = g * P.G + c % P.G;
+    // Partitions of this column's own context: with one, partition 0 writes
+    // the final row; with several, each writes its partial.
+    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
+    const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
+    if (np <= 1 ? p != 0 : p >= np) continue;
     float M = sm_m[0][qq];
 #pragma unroll
     for (int v = 1; v < NW; ++v) M = fmaxf(M, sm_m[v][qq]);
@@ -239,9 +263,9 @@ void decode_mfma_kernel(DecodeParams P) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ov[e] += sm_o[v][qq][8 * ch + e] * sc;
     }
-    const int h = q0 + qq;
-    if (split_out) {
-      const size_t part = ((size_t)s * P.Hq + h) * P.n_parts + p;
+    const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
+    if (np > 1) {
+      const size_t part = orow * P.n_parts + p;
       float* dst = P.ws_o + part * D + 8 * ch;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[e] = any_bad ? __builtin_nanf("") : ov[e];
@@ -259,7 +283,7 @@ void decode_mfma_kernel(DecodeParams P) {
       u.y = pack_bf16x2(res[2], res[3]);
       u.z = pack_bf16x2(res[4], res[5]);
       u.w = pack_bf16x2(res[6], res[7]);
-      st16(reinterpret_cast<char*>(P.out) + (((size_t)s * P.Hq + h) * D + 8 * ch) * 2, u);
+      st16(reinterpret_cast<char*>(P.out) + (orow * D + 8 * ch) * 2, u);
     }
   }
 }
@@ -267,7 +291,7 @@ void decode_mfma_kernel(DecodeParams P) {
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
   constexpr int DEPTH = PA_MFMA_DEPTH;
-  const dim3 grid(p.Hkv * mfma_q_groups(p.G), p.n_parts, p.B), block(NW * kWave);
+  const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B), block(NW * kWave);
   hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH>), grid, block, 0, stream, p);
   return hipGetLastError();
 }

@@ -10,7 +10,7 @@
 // block by block; partitioning long contexts across workgroups is this
 // library's way to spread one sequence over many compute units.)
 //
-// One workgroup of RW waves per (query head, sequence). Every wave finds M
+// One workgroup of RW waves per (query head, query row). Every wave finds M
 // over all partitions; wave w then accumulates partitions w, w + RW, ...,
 // reading kUnroll partial rows per round trip (lane i holds w_j for the i-th
 // partition of the wave's current chunk, broadcast with readlane, while every
@@ -39,16 +39,18 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   const int lane = threadIdx.x & (kWave - 1);
   const int w = wave_id();
   const int h = blockIdx.x;
-  const int s = blockIdx.y;
+  const int i = blockIdx.y;  // query row of the sequence (0 for decode)
+  const int s = blockIdx.z;
 
-  const int ctx = P.context_lens[s];
-  if (ctx < 0 || ctx > P.ctx_limit) return;  // the decode kernel wrote NaN already
-  const int nblk = (ctx + kBlock - 1) / kBlock;
+  const SeqRows sr = seq_rows(P, s);
+  if (i >= min(sr.n, P.max_q) || sr.bad) return;  // no row, or NaN written already
+  const int nblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
   const int bpp = P.partition / kBlock;
   const int np = (nblk + bpp - 1) / bpp;
-  if (np <= 1) return;  // the decode kernel wrote the final row itself
+  if (np <= 1) return;  // the attention kernel wrote the final row itself
 
-  const size_t base = ((size_t)s * P.Hq + h) * P.n_parts;
+  const int row = sr.first + i;
+  const size_t base = ((size_t)row * P.Hq + h) * P.n_parts;
   const float* ml = P.ws_ml + 2 * base;
   const float* po = P.ws_o + base * D + lane * DPL;
 
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
     acc[d] = t;
   }
   const float inv = 1.0f / L;
-  char* out = reinterpret_cast<char*>(P.out) + (((size_t)s * P.Hq + h) * D + lane * DPL) * sizeof(T);
+  char* out = reinterpret_cast<char*>(P.out) + (((size_t)row * P.Hq + h) * D + lane * DPL) * sizeof(T);
   if constexpr (sizeof(T) == 2) {
     if constexpr (DPL == 2) {
       *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
-  const dim3 grid(p.Hq, p.B), block(kReduceWaves * kWave);
+  const dim3 grid(p.Hq, p.max_q, p.B), block(kReduceWaves * kWave);
   if (dtype == 1 && D == 128)
     hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, 128>), grid, block, 0, stream, p);
   else if (dtype == 1 && D == 64)

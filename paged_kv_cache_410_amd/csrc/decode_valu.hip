@@ -1,4 +1,4 @@
-// Paged decode attention, vector-ALU path (one query head per workgroup).
+// Paged decode attention, vector-ALU path (one query row and head per workgroup).
 //
 // Method: "Why OS Virtual Memory Paging Saved LLM Inference" (a8q9.cn),
 // section 2: the attention kernel reads each logical block's physical block
@@ -9,9 +9,12 @@
 // sum, rescaled output), so every K/V byte is read exactly once.
 //
 // Work decomposition (gfx950, wave64):
-//   grid   = (query head h, partition p, sequence s): the heads of one
-//            sequence are dispatched together, so the tiles of one physical
-//            block (all heads, contiguous in the pool) are read close in time.
+//   grid   = (query head h + Hq * query row i, partition p, sequence s): the
+//            heads of one sequence are dispatched together, so the tiles of
+//            one physical block (all heads, contiguous in the pool) are read
+//            close in time. A decode step has one query row per sequence;
+//            with several new tokens per sequence (query_start) each row is
+//            its own workgroup and attends over its causal prefix.
 //   block  = NW waves; wave w takes blocks p0 + w, p0 + w + NW, ...
 //   A (block, kv head) tile is 16 rows of D elements, contiguous in memory.
 //   One 16-byte load per lane: LPT = D*e/16 lanes cover one token row, so a
@@ -123,30 +126,34 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const int c = lane % LPT;
 
   const GridPos gp = grid_pos();
-  const int h = gp.x;
+  const int h = gp.x % P.Hq;
+  const int i = gp.x / P.Hq;  // query row of the sequence (0 for decode)
   const int p = gp.y;
   const int s = gp.z;
   const int g = h / P.G;
 
   const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
-  const size_t row_qo = ((size_t)s * P.Hq + h) * D;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
   const int blk_begin = p * bpp;
   const int first = blk_begin + w;       // this wave's blocks: first, first + NW, ...
 
-  // Start-up loads, issued together before anything waits on them: the query
-  // chunk, the wave's first 64 block ids (bounded by the partition's table
-  // range, as the context length is not known yet) and the context length.
-  const uint4 qraw = ld16(reinterpret_cast<const char*>(P.q) + row_qo * sizeof(T) + c * 16);
+  // Start-up loads, issued before anything waits on them: the wave's first 64
+  // block ids (bounded by the partition's table range, as the context length
+  // is not known yet), the sequence's rows and context length, the query.
   const int ids0 = first_chunk_ids(bt_row, first, NW, bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB,
                                    lane);
-  const int ctx = P.context_lens[s];
+  const SeqRows sr = seq_rows(P, s);
+  if (i >= min(sr.n, P.max_q)) return;  // no such row
+  const int row = sr.first + i;
+  const size_t row_qo = ((size_t)row * P.Hq + h) * D;
+  const uint4 qraw = ld16(reinterpret_cast<const char*>(P.q) + row_qo * sizeof(T) + c * 16);
 
-  const bool bad_ctx = ctx < 0 || ctx > P.ctx_limit;
-  const int nblk = bad_ctx ? 0 : (ctx + kBlock - 1) / kBlock;
+  const int ctx = sr.row_ctx(i);         // tokens this row attends over
+  const bool bad_ctx = sr.bad;
+  const int nblk = (ctx + kBlock - 1) / kBlock;
   const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
   const int nparts_s = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
-  if (p >= max(nparts_s, 1)) return;  // partition past this sequence's end
+  if (p >= max(nparts_s, 1)) return;  // partition past this row's context
 
   float qf[EPL];
   Elem<T>::unpack(qraw, qf);
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
 
   // Lanes 0 .. LPT-1 of wave 0 hold the result for chunk c.
   if (P.partition > 0 && nparts_s > 1) {
-    const size_t part = ((size_t)s * P.Hq + h) * P.n_parts + p;
+    const size_t part = ((size_t)row * P.Hq + h) * P.n_parts + p;
     float* dst = P.ws_o + part * D + c * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dst[e] = bad ? __builtin_nanf("") : outv[e];
@@ -320,7 +327,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
   constexpr int NW = PA_VALU_WAVES;
   constexpr int DEPTH = PA_VALU_DEPTH;
-  const dim3 grid(p.Hq, p.n_parts, p.B), block(NW * kWave);
+  const dim3 grid(p.Hq * p.max_q, p.n_parts, p.B), block(NW * kWave);
   if (dtype == 1 && D == 128)
     hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW, DEPTH>), grid, block, 0, stream, p);
   else if (dtype == 1 && D == 64)

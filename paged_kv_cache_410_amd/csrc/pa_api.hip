@@ -116,26 +116,35 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_c
   return align_up(rows * 2 * sizeof(float)) + rows * (size_t)D * sizeof(float);
 }
 
-pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
-                    int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
-                    int32_t max_ctx, float scale, int32_t partition, void* workspace,
-                    size_t workspace_bytes, pa_dtype dt, hipStream_t stream) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || NB < 0 || MB < 0 || max_ctx < 0 || !dtype_ok(dt))
+}  // extern "C"
+
+namespace {
+
+// Shared body of pa_decode (query_start == NULL: one query row per sequence)
+// and pa_multi_query (rows query_start[s] .. query_start[s+1]-1 of sequence s).
+pa_status attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* query_start, int32_t B, int32_t rows, int32_t max_q, int32_t Hq,
+                    int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB, int32_t max_ctx,
+                    float scale, int32_t partition, void* workspace, size_t workspace_bytes,
+                    pa_dtype dt, hipStream_t stream) {
+  if (B < 0 || rows < 0 || max_q < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || NB < 0 || MB < 0 ||
+      max_ctx < 0 || !dtype_ok(dt))
     return PA_EINVAL;
   if (Hq % Hkv != 0) return PA_EINVAL;
   if (partition < 0 || partition % kBs != 0) return PA_EINVAL;
   if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
   if (D != 64 && D != 128) return PA_EUNSUPPORTED;
-  if (B > kMaxGridYZ) return PA_EUNSUPPORTED;  // grid z
-  if (B == 0) return PA_OK;
+  if (B > kMaxGridYZ || max_q > kMaxGridYZ) return PA_EUNSUPPORTED;  // grid z / merge grid y
+  if ((int64_t)Hq * max_q > INT32_MAX) return PA_EUNSUPPORTED;      // grid x
+  if (B == 0 || rows == 0 || max_q == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !context_lens || (MB > 0 && !block_tables))
     return PA_EINVAL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_EINVAL;
 
   const int64_t parts = grid_parts(max_ctx, partition);
-  const size_t need = pa_decode_workspace_bytes(B, Hq, D, max_ctx, partition);
+  const size_t need = pa_decode_workspace_bytes(rows, Hq, D, max_ctx, partition);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
   if (need > 0 && ((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
   if (parts > kMaxGridYZ) return PA_EUNSUPPORTED;  // grid y
@@ -147,6 +156,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.query_start = query_start;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
@@ -157,14 +167,21 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   p.ctx_limit = (int32_t)(cap < max_ctx ? cap : max_ctx);
   p.partition = parts > 1 ? partition : 0;
   p.n_parts = (int32_t)parts;
+  p.max_q = max_q;
+  p.rows = rows;
+  p.n_tiles = (int32_t)(((int64_t)max_q * p.G + 15) / 16);
   p.qscale = scale * 1.4426950408889634f;
   if (parts > 1) {
-    const size_t rows = (size_t)B * Hq * (size_t)parts;
+    const size_t nrows = (size_t)rows * Hq * (size_t)parts;
     p.ws_ml = static_cast<float*>(workspace);
-    p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(rows * 2 * sizeof(float)));
+    p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(nrows * 2 * sizeof(float)));
   }
 
-  const bool mfma = dt == PA_BF16 && D == 128 && p.G >= 2;
+  // The matrix-core kernel serves a kv head's columns (query rows x group
+  // heads) 16 at a time; a single column per kv head (one query head, one
+  // row) goes to the vector kernel.
+  const bool mfma = dt == PA_BF16 && D == 128 && (p.G >= 2 || max_q >= 2);
+  if (mfma && (int64_t)Hkv * p.n_tiles > INT32_MAX) return PA_EUNSUPPORTED;
   hipError_t err = mfma ? pa::launch_decode_mfma(p, stream) : pa::launch_decode_valu(p, dt, D, stream);
   if (err != hipSuccess) return PA_EHIP;
   if (parts > 1) {
@@ -172,6 +189,32 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     if (err != hipSuccess) return PA_EHIP;
   }
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                    int32_t max_ctx, float scale, int32_t partition, void* workspace,
+                    size_t workspace_bytes, pa_dtype dt, hipStream_t stream) {
+  return attention(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, B, B, 1, Hq, Hkv,
+                   D, bs, NB, MB, max_ctx, scale, partition, workspace, workspace_bytes, dt,
+                   stream);
+}
+
+pa_status pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start, int32_t B, int32_t Tq, int32_t max_q,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                         int32_t max_ctx, float scale, int32_t partition, void* workspace,
+                         size_t workspace_bytes, pa_dtype dt, hipStream_t stream) {
+  if (B > 0 && Tq > 0 && !query_start) return PA_EINVAL;
+  return attention(out, q, k_cache, v_cache, block_tables, context_lens, query_start, B, Tq,
+                   max_q, Hq, Hkv, D, bs, NB, MB, max_ctx, scale, partition, workspace,
+                   workspace_bytes, dt, stream);
 }
 
 }  // extern "C"

@@ -30,7 +30,11 @@ Every workload has one decode step: each sequence's last token is appended
 (through the block manager) and written with the step's new K/V, then all
 sequences attend over their full context. For `cow`, the step's appended
 tokens are the samples' whole tails, so the step carries the copy-on-write
-copies of the shared, partly filled prompt blocks.
+copies of the shared, partly filled prompt blocks. A chunk workload
+(spec.chunk) appends several new tokens per sequence (the last n_s tokens of
+its context, n_s drawn after the lengths) and has one query row per new
+token; its draw order is lengths -> new-token counts -> free-list
+permutation -> q -> K pool -> V pool -> new K -> new V.
 """
 
 import math
@@ -55,6 +59,7 @@ class Spec:
     partition: int = 0         # tokens per split-context partition the benchmark uses (0 = none)
     bs: int = 16
     cow: dict = field(default_factory=dict)  # prompts, samples, prompt_len, r_max, tail_lo, tail_hi
+    chunk: tuple = ()          # several new tokens per sequence: ("uniform", lo, hi) | ("all",)
 
     @property
     def scale(self):
@@ -102,7 +107,7 @@ def draw_lengths(spec, rng):
     raise ValueError(kind)
 
 
-def _populate(spec, bm, ctx, cow_parts):
+def _populate(spec, bm, ctx, cow_parts, n_new):
     """Drive a block manager through the workload's history and its step.
 
     Returns seq ids, the step's slots, the step's (src, dst) copy pairs, and
@@ -126,9 +131,9 @@ def _populate(spec, bm, ctx, cow_parts):
         for s in range(spec.B):
             sid = bm.add_seq()
             seqs.append(sid)
-            bm.append(sid, int(ctx[s]) - 1)          # history (untimed)
+            bm.append(sid, int(ctx[s]) - int(n_new[s]))   # history (untimed)
         for i, sid in enumerate(seqs):
-            step(i, sid, 1)                           # the step's token
+            step(i, sid, int(n_new[i]))                    # the step's tokens
     else:
         prompt, tails = cow_parts
         c = spec.cow
@@ -155,26 +160,39 @@ class Tables:
     step_seq: np.ndarray        # int32 [T], batch index of each step token
     step_pos: np.ndarray        # int32 [T], logical position of each step token
     pairs: np.ndarray           # int32 [n, 2], the step's copy-on-write pairs
+    query_start: np.ndarray     # int32 [B + 1], the step's new tokens per sequence (prefix sums)
     seqs: list
     bm: object
+
+
+def draw_new_tokens(spec, ctx, rng):
+    """New tokens per sequence in the step: 1 for a decode step; for a chunk
+    workload U{lo..hi} clipped to the context, or the whole context ("all")."""
+    if not spec.chunk:
+        return np.ones(len(ctx), dtype=np.int64)
+    if spec.chunk[0] == "all":
+        return ctx.copy()
+    lo, hi = spec.chunk[1], spec.chunk[2]
+    return np.minimum(rng.integers(lo, hi, size=len(ctx), endpoint=True), ctx).astype(np.int64)
 
 
 def make_tables(spec, bm_factory):
     """Block tables for `spec` built by `bm_factory(num_blocks, block_size, free_order)`."""
     rng = np.random.default_rng(spec.seed)
     ctx, cow_parts = draw_lengths(spec, rng)
+    n_new = draw_new_tokens(spec, ctx, rng)
     if spec.pool_blocks:
         NB = spec.pool_blocks
     else:
         # dry run in an ample pool to count the blocks the workload holds
         big = int(sum(int(c) for c in ctx)) + spec.B + 16
         probe = bm_factory(big, spec.bs, np.arange(big, dtype=np.int32))
-        _populate(spec, probe, ctx, cow_parts)
+        _populate(spec, probe, ctx, cow_parts, n_new)
         used = big - probe.num_free()
         NB = int(math.ceil(used * (1.0 + spec.pool_slack)))
     free_order = rng.permutation(NB).astype(np.int32)
     bm = bm_factory(NB, spec.bs, free_order)
-    seqs, slots, pairs, step_seq, step_pos = _populate(spec, bm, ctx, cow_parts)
+    seqs, slots, pairs, step_seq, step_pos = _populate(spec, bm, ctx, cow_parts, n_new)
     MB = max(len(bm.block_table(s)) for s in seqs)
     bt = np.asarray(bm.tables_array(seqs, MB), dtype=np.int32).reshape(spec.B, MB)
     lens = np.asarray([bm.seq_len(s) for s in seqs], dtype=np.int32)
@@ -184,12 +202,13 @@ def make_tables(spec, bm_factory):
                   step_seq=np.asarray(step_seq, dtype=np.int32),
                   step_pos=np.asarray(step_pos, dtype=np.int32),
                   pairs=np.asarray(pairs, dtype=np.int32).reshape(-1, 2),
+                  query_start=np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32),
                   seqs=seqs, bm=bm)
 
 
 @dataclass
 class Values:
-    q: torch.Tensor         # [B, Hq, D]
+    q: torch.Tensor         # [B, Hq, D]; chunk workloads: [T, Hq, D], one row per new token
     k_cache: torch.Tensor   # [NB, Hkv, bs, D]
     v_cache: torch.Tensor
     k_new: torch.Tensor     # [T, Hkv, D]
@@ -208,7 +227,7 @@ def make_values(spec, NB, T, device="cpu"):
     def draw(*shape):
         return torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(dt)
 
-    q = draw(spec.B, spec.Hq, spec.D)
+    q = draw(T if spec.chunk else spec.B, spec.Hq, spec.D)
     k = draw(NB, spec.Hkv, spec.bs, spec.D)
     v = draw(NB, spec.Hkv, spec.bs, spec.D)
     kn = draw(T, spec.Hkv, spec.D)

@@ -80,7 +80,7 @@ class Step:
         NB, Hkv, D = tb.NB, spec.Hkv, spec.D
         self.k_cache = to_dev(self.k0, (NB, Hkv, 16, D))
         self.v_cache = to_dev(self.v0, (NB, Hkv, 16, D))
-        self.q = to_dev(self.q_bits, (spec.B, spec.Hq, D))
+        self.q = to_dev(self.q_bits, self.q_bits.shape)
         T = len(tb.slots)
         self.k_new = to_dev(self.kn_bits, (T, Hkv, D))
         self.v_new = to_dev(self.vn_bits, (T, Hkv, D))
@@ -89,6 +89,8 @@ class Step:
         self.pairs = torch.from_numpy(np.ascontiguousarray(tb.pairs)).to(dev)
         self.step_seq = torch.from_numpy(tb.step_seq).to(dev)
         self.step_pos = torch.from_numpy(tb.step_pos).to(dev)
+        self.query_start = torch.from_numpy(tb.query_start).to(dev)
+        self.max_q = int(np.diff(tb.query_start).max()) if spec.B else 0
         self.max_ctx = int(tb.context_lens.max()) if spec.B else 0
 
         # oracle: copy -> write on host copies
@@ -103,6 +105,10 @@ class Step:
             self.expect = self.oracle_decode()
 
     def oracle_decode(self, pairs=None):
+        if self.spec.chunk:
+            return oracle.multi_query(oracle_view(self.q_bits), oracle_view(self.k_after),
+                                      oracle_view(self.v_after), self.tb.block_tables,
+                                      self.tb.context_lens, self.tb.query_start, self.spec.scale)
         return oracle.decode(oracle_view(self.q_bits), oracle_view(self.k_after),
                              oracle_view(self.v_after), self.tb.block_tables,
                              self.tb.context_lens, self.spec.scale, pairs=pairs)
@@ -114,6 +120,11 @@ class Step:
         slots = pa.slot_mapping(self.block_tables, self.step_pos, seq_ids=self.step_seq)
         pa.write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, slots)
         return slots
+
+    def multi(self, pa, partition=None):
+        return pa.multi_query(self.q, self.k_cache, self.v_cache, self.block_tables,
+                              self.context_lens, self.query_start, self.spec.scale, self.max_ctx,
+                              self.max_q, partition=partition)
 
     def decode(self, pa, partition=None):
         return pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,

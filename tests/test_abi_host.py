@@ -91,6 +91,34 @@ def test_decode_empty_batch_is_a_noop(palib):
     assert palib.lib().pa_decode(*decode_args(B=0, q=None, out=None)) == 0
 
 
+def multi_args(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, B=2, Tq=6, max_q=4,
+             Hq=8, Hkv=2, D=128, bs=16, NB=10, MB=4, max_ctx=64, scale=0.1, partition=0,
+             ws=None, ws_bytes=0, dt=1, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "k", "v", "bt", "cl", "qs", "B", "Tq", "max_q", "Hq",
+                           "Hkv", "D", "bs", "NB", "MB", "max_ctx", "scale", "partition", "ws",
+                           "ws_bytes", "dt", "stream")]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), -1), (dict(q=None), -1), (dict(Tq=-1), -1), (dict(max_q=-2), -1),
+    (dict(Hq=6, Hkv=4), -1), (dict(partition=8), -1), (dict(D=80), -2), (dict(bs=32), -2),
+    (dict(max_q=70000), -2), (dict(B=70000), -2),
+    (dict(partition=16, max_ctx=64), -3),
+    (dict(out=FAKE + 4), -1),
+])
+def test_multi_query_rejects_bad_arguments(palib, kw, status):
+    assert palib.lib().pa_multi_query(*multi_args(**kw)) == status
+
+
+def test_multi_query_empty_is_a_noop(palib):
+    lib = palib.lib()
+    assert lib.pa_multi_query(*multi_args(Tq=0, q=None, out=None, qs=None)) == 0
+    assert lib.pa_multi_query(*multi_args(B=0, qs=None)) == 0
+    assert lib.pa_multi_query(*multi_args(max_q=0)) == 0
+
+
 def test_workspace_sizing(palib):
     lib = palib.lib()
     assert lib.pa_decode_workspace_bytes(4, 8, 128, 1000, 0) == 0
