@@ -12,8 +12,10 @@ inside the timed region, so the decode kernel's average duration (and from it
 its achieved HBM bandwidth against the 8 TB/s peak) is measured live.
 
 Printed: one JSON line. `value` is the step's algorithmic HBM bytes over the
-step time (GB/s); `decode_tokens_per_s` is sequences / step time. The
-`roofline` object covers the decode kernel; its `traffic` comes from the
+step time (GB/s); `decode_tokens_per_s` is the step's new tokens / step time
+(one per sequence for a decode step). The `roofline` object covers the
+attention kernel (bound: HBM, or the matrix peak for a chunk workload whose
+arithmetic intensity passes the ridge); its `traffic` comes from the
 committed rocprofv3 counter summary for that kernel and workload, or is null
 when the kernel sources have changed since those counters were taken. The
 `cpu_baseline` object is the fp64 CPU oracle on the same inputs, on this
@@ -34,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix peak (fp32: vector peak)
 PROFILES = os.path.join(ROOT, "profiles")
 # Sources the decode kernels are built from: counters taken on another
 # version of these no longer describe the kernel that runs.
@@ -73,19 +76,28 @@ def read_traffic(workload):
 
 
 def algorithmic_bytes(spec, tb):
-    """Bytes the method must move, each element once (not what a kernel moves)."""
+    """Bytes the method must move, each element once (not what a kernel moves),
+    and its flops (QK and PV, two per multiply-add)."""
     e = 4 if spec.dtype == "f32" else 2
     ctx = tb.context_lens.astype("int64")
+    n = (tb.query_start[1:] - tb.query_start[:-1]).astype("int64")
+    rows = int(n.sum()) if spec.chunk else spec.B
     kv = int(ctx.sum()) * spec.Hkv * spec.D * 2 * e                # every K and V row once
-    qo = 2 * spec.B * spec.Hq * spec.D * e                         # q in, out
+    qo = 2 * rows * spec.Hq * spec.D * e                           # q in, out
     meta = 4 * (int(((ctx + 15) // 16).sum()) + spec.B)            # table entries + lengths
+    if spec.chunk:
+        meta += 4 * (spec.B + 1)                                   # query_start
+        # row i of a chunk of n attends over ctx - n + i + 1 tokens
+        attended = int((n * (ctx - n) + n * (n + 1) // 2).sum())
+    else:
+        attended = int(ctx.sum())
     decode = kv + qo + meta
     T = len(tb.slots)
     write = 2 * 2 * T * spec.Hkv * spec.D * e                      # K, V rows: read + write
     slots = 4 * 4 * T                                              # seq, pos, table entry, slot
     copy = 2 * 2 * len(tb.pairs) * spec.Hkv * 16 * spec.D * e      # K, V blocks: read + write
     return dict(decode=decode, write=write, slots=slots, copy=copy,
-                step=decode + write + slots + copy, flops=4 * int(ctx.sum()) * spec.Hq * spec.D)
+                step=decode + write + slots + copy, flops=4 * attended * spec.Hq * spec.D)
 
 
 def unique_decode_bytes(spec, tb):
@@ -102,30 +114,56 @@ def unique_decode_bytes(spec, tb):
     return rows * spec.Hkv * spec.D * 2 * e + 2 * spec.B * spec.Hq * spec.D * e
 
 
-def cpu_baseline(st_inputs, spec, tb, bytes_decode, budget_s):
-    """The fp64 oracle on the host, on the same inputs: whole decode step, repeated
-    until about `budget_s` seconds of CPU time have been spent (at least once)."""
+# Oracle work is bounded to about this many (row, token, dim) products per run
+# (roughly 10-20 s on 16 host threads).
+ORACLE_WORK_CAP = 1.5e11
+
+
+def cpu_baseline(st_inputs, spec, tb, budget_s):
+    """The fp64 oracle on the host, on the same inputs. The sample is the whole
+    step when its work fits ORACLE_WORK_CAP, else the first k sequences that do;
+    it is repeated until about `budget_s` seconds have been spent (at least
+    once). Returns (sample rows' oracle output, row slice, the baseline object)."""
+    import numpy as np
+
     import oracle
     q, k, v = st_inputs
     oracle.build()
     threads = oracle.max_threads()
+    ctx = tb.context_lens.astype(np.int64)
+    n = (tb.query_start[1:] - tb.query_start[:-1]).astype(np.int64)
+    if spec.chunk:
+        work = (n * (ctx - n) + n * (n + 1) // 2) * spec.Hq * spec.D * 2
+    else:
+        work = ctx * spec.Hq * spec.D * 2
+    k_seq = max(1, int(np.searchsorted(np.cumsum(work), ORACLE_WORK_CAP, side="right")))
+    k_seq = min(k_seq, spec.B)
+    sub = type(tb)(**{**tb.__dict__, "context_lens": tb.context_lens[:k_seq],
+                      "block_tables": tb.block_tables[:k_seq],
+                      "query_start": tb.query_start[:k_seq + 1]})
+    rows = slice(0, int(tb.query_start[k_seq])) if spec.chunk else slice(0, k_seq)
+    sample_bytes = algorithmic_bytes(type(spec)(**{**spec.__dict__, "B": k_seq}), sub)["decode"]
     times = []
     out = None
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        out = oracle.decode(q, k, v, tb.block_tables, tb.context_lens, spec.scale)
+        if spec.chunk:
+            out = oracle.multi_query(q[rows], k, v, sub.block_tables, sub.context_lens,
+                                     sub.query_start, spec.scale)
+        else:
+            out = oracle.decode(q[rows], k, v, sub.block_tables, sub.context_lens, spec.scale)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start >= budget_s or len(times) >= 20:
             break
     t = sorted(times)[len(times) // 2]
-    return out, dict(value=round(bytes_decode / t / 1e9, 3), unit="GB/s", cores=threads,
-                     kind="oracle",
-                     sample=f"the whole {spec.name} decode step ({spec.B} sequences x {spec.Hq} "
-                            f"heads, fp64 oracle, OpenMP over (sequence, head)), median of "
-                            f"{len(times)} runs",
-                     seconds_per_step=round(t, 4),
-                     decode_tokens_per_s=round(spec.B / t, 2))
+    what = "the whole" if k_seq == spec.B else f"the first {k_seq} of {spec.B} sequences of the"
+    return out, rows, dict(
+        value=round(sample_bytes / t / 1e9, 3), unit="GB/s", cores=threads, kind="oracle",
+        sample=f"{what} {spec.name} step's attention ({spec.Hq} heads; fp64 oracle, OpenMP over "
+               f"(query row, head)), median of {len(times)} runs; GB/s on that sample's "
+               f"algorithmic bytes",
+        seconds_per_run=round(t, 4), tokens_per_s=round((rows.stop - rows.start) / t, 2))
 
 
 def host_bits(t):
@@ -142,7 +180,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="13b", choices=["tiny", "7b", "13b", "gqa", "cow"])
+    ap.add_argument("--workload", default="13b",
+                    choices=["tiny", "7b", "13b", "gqa", "cow", "13b_verify4", "gqa_chunk512"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-context partition in tokens (default: the library's choice, "
                          "or the workload's own)")
@@ -187,11 +226,14 @@ def main():
     step_pos = torch.from_numpy(tb.step_pos).to(dev)
     pairs = torch.from_numpy(np.ascontiguousarray(tb.pairs)).to(dev)
     max_ctx = int(tb.context_lens.max())
+    rows = q.shape[0]                       # query rows: B, or every new token of a chunk
+    qs = torch.from_numpy(tb.query_start).to(dev)
+    max_q = int(np.diff(tb.query_start).max())
     partition = args.partition
     if partition is None:
-        partition = spec.partition or pa.default_partition(spec.B, spec.Hq, spec.Hkv, spec.D,
+        partition = spec.partition or pa.default_partition(rows, spec.Hq, spec.Hkv, spec.D,
                                                            max_ctx)
-    ws_bytes = pa.decode_workspace_bytes(spec.B, spec.Hq, spec.D, max_ctx, partition)
+    ws_bytes = pa.decode_workspace_bytes(rows, spec.Hq, spec.D, max_ctx, partition)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     slots = torch.empty(T, dtype=torch.int32, device=dev)
@@ -212,8 +254,12 @@ def main():
         pa.write_kv(k_new, v_new, k_cache, v_cache, slots)
         if ev is not None:
             ev[0].record()
-        pa.decode(q, k_cache, v_cache, bt, cl, spec.scale, max_ctx, partition=partition,
-                  out=out, workspace=workspace)
+        if spec.chunk:
+            pa.multi_query(q, k_cache, v_cache, bt, cl, qs, spec.scale, max_ctx, max_q,
+                           partition=partition, out=out, workspace=workspace)
+        else:
+            pa.decode(q, k_cache, v_cache, bt, cl, spec.scale, max_ctx, partition=partition,
+                      out=out, workspace=workspace)
         if ev is not None:
             ev[1].record()
 
@@ -270,15 +316,24 @@ def main():
         inputs = (host_bits(q), host_bits(k_cache), host_bits(v_cache))
         if spec.dtype == "f32":
             inputs = tuple(x.view(np.float32) for x in inputs)
-        expect, cpu = cpu_baseline(inputs, spec, tb, nbytes["decode"], args.cpu_seconds)
-        got = out.float().cpu().numpy().astype(np.float64)
+        expect, sample_rows, cpu = cpu_baseline(inputs, spec, tb, args.cpu_seconds)
+        got = out[sample_rows].float().cpu().numpy().astype(np.float64)
         parity = float(np.max(np.abs(got - expect)))
-        log(f"[bench] oracle {cpu['seconds_per_step']} s/step on {cpu['cores']} threads; "
+        log(f"[bench] oracle {cpu['seconds_per_run']} s/run on {cpu['cores']} threads; "
             f"max abs err vs oracle {parity:.3e}")
 
     traffic, why = read_traffic(spec.name)
-    achieved = nbytes["decode"] / (dec_avg_ms * 1e-3) / 1e9
     value = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    # The attention kernel's bound: HBM unless its arithmetic intensity passes
+    # the ridge of the matrix peak over the HBM peak.
+    mpeak = MFMA_PEAK_TFLOPS[spec.dtype]
+    intensity = nbytes["flops"] / nbytes["decode"]
+    if intensity > mpeak * 1e12 / (HBM_PEAK_GBPS * 1e9):
+        bound, unit, peak = ("mfma" if spec.dtype == "bf16" else "alu"), "TFLOP/s", mpeak
+        achieved = nbytes["flops"] / (dec_avg_ms * 1e-3) / 1e12
+    else:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBPS
+        achieved = nbytes["decode"] / (dec_avg_ms * 1e-3) / 1e9
     line = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + decode tokens/sec",
         "value": round(value, 1),
@@ -297,18 +352,20 @@ def main():
                    "batch": spec.B, "num_q_heads": spec.Hq, "num_kv_heads": spec.Hkv,
                    "head_dim": spec.D, "block_size": 16, "partition": partition,
                    "max_ctx": max_ctx, "mean_ctx": round(float(tb.context_lens.mean()), 1),
-                   "pool_blocks": tb.NB, "new_tokens": T, "cow_pairs": len(tb.pairs),
+                   "pool_blocks": tb.NB, "new_tokens": T, "query_rows": rows,
+                   "cow_pairs": len(tb.pairs),
                    "parallelism": "none (one GPU)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "decode_tokens_per_s": round(spec.B / (ms_step * 1e-3), 1),
+        "decode_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "attention_TFLOPs": round(nbytes["flops"] / (dec_avg_ms * 1e-3) / 1e12, 2),
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_median": round(dec_med_ms * 1e3, 2),
         "algorithmic_bytes": nbytes,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": "decode (one launch per step"
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": traffic, "kernel": "attention (one launch per step"
                      + (", plus the partition merge)" if ws_bytes else ")"),
-                     "traffic_note": why},
+                     "traffic_note": why, "intensity_flop_per_byte": round(intensity, 2)},
         "cpu_baseline": cpu,
         "parity_max_abs_err_vs_oracle": parity,
         "controls": controls,

@@ -65,7 +65,7 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-            ctypes.c_float, ctypes.c_int32, ctypes.c_int32]
+            ctypes.c_float, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -128,13 +128,14 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, pairs=None, n
 
 
 def multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
-                n_threads=0):
+                pairs=None, n_threads=0):
     """fp64 causal attention of several new tokens per sequence.
 
     q [Tq, Hq, D]; sequence s owns rows query_start[s] .. query_start[s+1]-1,
     the last n_s tokens of its context (row i at position ctx_s - n_s + i,
     attending to positions 0 .. ctx_s - n_s + i). Element types as decode().
-    Returns float64 [Tq, Hq, D].
+    pairs: optional [(row, head), ...] -> output [n, D]. Returns float64
+    [Tq, Hq, D] otherwise.
     """
     lib = _load()
     q = np.ascontiguousarray(q)
@@ -153,11 +154,17 @@ def multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start, sc
     B = cl.shape[0]
     if bt.ndim != 2 or bt.shape[0] != B or qs.shape != (B + 1,):
         raise ValueError("block_tables / query_start shape mismatch")
-    out = np.empty((Tq, Hq, D), dtype=np.float64)
+    if pairs is not None:
+        pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        out = np.empty((pr.shape[0], D), dtype=np.float64)
+        pr_ptr, n_pr = pr.ctypes.data, pr.shape[0]
+    else:
+        out = np.empty((Tq, Hq, D), dtype=np.float64)
+        pr_ptr, n_pr = None, 0
     rc = lib.oracle_multi_query(out.ctypes.data, q.ctypes.data, k_cache.ctypes.data,
                                 v_cache.ctypes.data, bt.ctypes.data, cl.ctypes.data,
                                 qs.ctypes.data, B, Tq, Hq, Hkv, D, bs, NB, bt.shape[1],
-                                float(np.float32(scale)), dt, int(n_threads))
+                                float(np.float32(scale)), dt, pr_ptr, n_pr, int(n_threads))
     if rc != 0:
         raise ValueError(f"oracle_multi_query failed ({rc}): bad argument, a chunk longer "
                          "than its context, or a block id out of range")

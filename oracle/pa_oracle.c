@@ -204,10 +204,11 @@ int oracle_decode(double* out, const void* q, const void* k_cache,
  * (chunked prefill, or checking several drafted tokens at once). With
  * n_s = 1 for every s this is oracle_decode.
  *
- *   out          double [Tq][Hq][D]
+ *   out          double; [Tq][Hq][D] when pairs == NULL, else [n_pairs][D]
  *   q            [Tq][Hq][D]            dtype-tagged
  *   query_start  int32 [B+1], non-decreasing, query_start[0] = 0,
  *                query_start[B] = Tq
+ *   pairs        optional int32 [n_pairs][2] = (row, head) outputs to compute
  * A sequence with n_s > ctx_s is an error (-1).
  */
 int oracle_multi_query(double* out, const void* q, const void* k_cache,
@@ -215,7 +216,8 @@ int oracle_multi_query(double* out, const void* q, const void* k_cache,
                        const int32_t* context_lens, const int32_t* query_start,
                        int32_t B, int32_t Tq, int32_t Hq, int32_t Hkv,
                        int32_t D, int32_t bs, int32_t NB, int32_t MB,
-                       float scale, int32_t dtype, int32_t n_threads) {
+                       float scale, int32_t dtype, const int32_t* pairs,
+                       int64_t n_pairs, int32_t n_threads) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
       !query_start)
     return -1;
@@ -230,15 +232,19 @@ int oracle_multi_query(double* out, const void* q, const void* k_cache,
     if (n < 0 || n > context_lens[s]) return -1;
   }
   const int32_t G = Hq / Hkv;
-  const int64_t n_rows = (int64_t)Tq * Hq;
+  const int64_t n_rows = pairs ? n_pairs : (int64_t)Tq * Hq;
   int err = 0;
 #ifdef _OPENMP
   if (n_threads <= 0) n_threads = omp_get_max_threads();
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads) reduction(min : err)
 #endif
   for (int64_t r = 0; r < n_rows; ++r) {
-    const int32_t j = (int32_t)(r / Hq);
-    const int32_t h = (int32_t)(r % Hq);
+    const int32_t j = pairs ? pairs[2 * r] : (int32_t)(r / Hq);
+    const int32_t h = pairs ? pairs[2 * r + 1] : (int32_t)(r % Hq);
+    if (j < 0 || j >= Tq || h < 0 || h >= Hq) {
+      err = -1;
+      continue;
+    }
     int32_t s = 0;
     while (query_start[s + 1] <= j) ++s; /* the sequence owning row j */
     const int32_t n = query_start[s + 1] - query_start[s];

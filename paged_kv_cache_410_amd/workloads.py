@@ -21,6 +21,11 @@ Workloads (lengths, seeds and draw order are fixed here):
         1024 - r, r ~ U{1..15} (so the last prompt block is partly filled and
         shared by 8 samples); each sample then gets a private tail of
         U{1..256} tokens.                                           seed 4
+  13b_verify4   the 13b shapes and length mix with 4 new tokens per
+        sequence (several drafted tokens checked in one pass).      seed 5
+  gqa_chunk512  bf16, 16 seqs, 64/8 heads, head_dim 128, contexts
+        U[1024, 8192] whose last 512 tokens are the step's chunk (a prompt
+        processed in 512-token chunks).                             seed 6
 
 Draw order for a seed: lengths -> free-list permutation -> q -> K pool ->
 V pool -> new K -> new V. Values are N(0, 1) in fp32, rounded to the
@@ -74,6 +79,11 @@ CONFIGS = {
     "gqa": Spec("gqa", "bf16", 16, 64, 8, 128, seed=3, lengths=("uniform", 8192, 32768), partition=512),
     "cow": Spec("cow", "bf16", 128, 32, 32, 128, seed=4, lengths=("cow",),
                 cow=dict(prompts=16, samples=8, prompt_len=1024, r_max=15, tail_lo=1, tail_hi=256)),
+    # several new tokens per sequence (multi-query attention, causal within the chunk)
+    "13b_verify4": Spec("13b_verify4", "bf16", 128, 40, 40, 128, seed=5,
+                        lengths=("lognormal", 500.0, 0.7, 16, 2048), chunk=("uniform", 4, 4)),
+    "gqa_chunk512": Spec("gqa_chunk512", "bf16", 16, 64, 8, 128, seed=6,
+                         lengths=("uniform", 1024, 8192), chunk=("uniform", 512, 512)),
 }
 
 

@@ -108,7 +108,8 @@ class Step:
         if self.spec.chunk:
             return oracle.multi_query(oracle_view(self.q_bits), oracle_view(self.k_after),
                                       oracle_view(self.v_after), self.tb.block_tables,
-                                      self.tb.context_lens, self.tb.query_start, self.spec.scale)
+                                      self.tb.context_lens, self.tb.query_start, self.spec.scale,
+                                      pairs=pairs)
         return oracle.decode(oracle_view(self.q_bits), oracle_view(self.k_after),
                              oracle_view(self.v_after), self.tb.block_tables,
                              self.tb.context_lens, self.spec.scale, pairs=pairs)

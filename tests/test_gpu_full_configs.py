@@ -22,30 +22,35 @@ def pa():
     return m
 
 
-def bench_partition(pa, spec, max_ctx):
+def bench_partition(pa, spec, rows, max_ctx):
     if spec.partition:
         return spec.partition
-    return pa.default_partition(spec.B, spec.Hq, spec.Hkv, spec.D, max_ctx)
+    return pa.default_partition(rows, spec.Hq, spec.Hkv, spec.D, max_ctx)
 
 
 def sample_rows(tb, Hq, n, seed):
+    """(query row, head) pairs: the longest and shortest sequences' last rows,
+    the first row of a chunk, and random ones."""
     rng = np.random.default_rng(seed)
     cl = tb.context_lens
-    seqs = [int(np.argmax(cl)), int(np.argmin(cl))] + rng.integers(0, len(cl), n - 2).tolist()
-    heads = [0, Hq - 1] + rng.integers(0, Hq, n - 2).tolist()
-    return list(zip(seqs, heads))
+    qs = tb.query_start
+    last = lambda s: int(qs[s + 1]) - 1  # noqa: E731
+    rows = [last(int(np.argmax(cl))), last(int(np.argmin(cl))), int(qs[0])]
+    rows += rng.integers(0, int(qs[-1]), n - 3).tolist()
+    heads = [0, Hq - 1, Hq // 2] + rng.integers(0, Hq, n - 3).tolist()
+    return list(zip(rows, heads))
 
 
-@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "cow"])
+@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "cow", "13b_verify4", "gqa_chunk512"])
 def test_full_config(pa, name):
     spec = workloads.CONFIGS[name]
     say(f"[full config] {name}: building inputs")
     st = Step(spec, values_device="cuda", oracle_full=False)
-    part = bench_partition(pa, spec, st.max_ctx)
+    part = bench_partition(pa, spec, st.q.shape[0], st.max_ctx)
     say(f"[full config] {name}: NB={st.tb.NB} MB={st.tb.MB} T={len(st.tb.slots)} "
         f"pairs={len(st.tb.pairs)} partition={part}")
     slots = st.run_cache_ops(pa)
-    out = st.decode(pa, partition=part)
+    out = st.multi(pa, partition=part) if spec.chunk else st.decode(pa, partition=part)
     torch.cuda.synchronize()
     assert np.array_equal(slots.cpu().numpy(), st.tb.slots)
     assert np.array_equal(host_bits(st.k_cache), st.k_after)

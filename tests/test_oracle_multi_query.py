@@ -141,3 +141,13 @@ def test_one_token_chunks_match_decode(oracle_mod):
     a = oracle.multi_query(q, kp, vp, bt, cl, qs, 0.125)
     b = oracle.decode(q, kp, vp, bt, cl, 0.125)
     assert np.array_equal(a, b)
+
+
+def test_sampled_pairs_match_full(oracle_mod):
+    lens = [40, 90]
+    q, kp, vp, bt, cl, qs, n, _ = make_case(17, lens, 4, 2, 64, "f32", max_new=10)
+    full = oracle.multi_query(q, kp, vp, bt, cl, qs, 0.125)
+    pairs = [(int(qs[-1]) - 1, 3), (0, 0), (int(qs[1]), 1)]
+    part = oracle.multi_query(q, kp, vp, bt, cl, qs, 0.125, pairs=pairs)
+    for i, (j, h) in enumerate(pairs):
+        assert np.array_equal(part[i], full[j, h])
