@@ -17,7 +17,10 @@
 //
 // Layouts (wave64; lane = 16 * rg + col, rg = lane / 16, col = lane % 16):
 //   S^T = K Q^T with v_mfma_f32_16x16x32_bf16, 4 steps over D (kk = 0..3):
-//     A (16 tokens x 32 dims): lane holds K[t = col][32 kk + 8 rg + 0..7]
+//     A (16 tokens x 32 dims): lane holds K[t = col][32 kk + 8 rg + 0..7].
+//     K is loaded like V (4 whole rows per load instruction, which streams
+//     faster than 16 row segments) and transposed into this layout through
+//     a per-wave LDS stage.
 //     B (32 dims x 16 cols):   lane holds Q[q = col][32 kk + 8 rg + 0..7]
 //     result: lane holds S^T[t = 4 rg + i][q = col], i = 0..3
 //   So every lane owns one column (col) and 4 tokens: the softmax max is an
@@ -39,7 +42,7 @@
 
 // Waves per workgroup and K/V tiles in flight per wave.
 #ifndef PA_MFMA_WAVES
-#define PA_MFMA_WAVES 2
+#define PA_MFMA_WAVES 4
 #endif
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 2
@@ -71,6 +74,8 @@ void decode_mfma_kernel(DecodeParams P) {
   constexpr int D = 128;
   constexpr int kRowBytes = D * 2;
   constexpr int kPad = 4;  // LDS row padding (floats) against bank conflicts
+  constexpr int kStageRow = kRowBytes + 16;  // LDS stride of a staged K row
+  static_assert(kBlock * kStageRow <= 16 * (D + kPad) * 4, "K stage must fit a merge region");
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = wave_id();
@@ -109,6 +114,13 @@ void decode_mfma_kernel(DecodeParams P) {
 
   // B operand of S^T: Q[column col][32 kk + 8 rg ..], zero for padded columns.
   bf16x8_t qop[4];
+  // LDS, one region per wave: while the wave streams its blocks, the first
+  // kStageBytes hold the K tile it is transposing (below); at the end the
+  // region holds the wave's merge rows (16 columns x D floats, padded). The
+  // wave overwrites its stage only after its last read of it, and a wave's
+  // LDS accesses complete in order, so no barrier guards either use.
+  __shared__ float sm_o[NW][16][D + kPad];
+  char* const stage = reinterpret_cast<char*>(&sm_o[w][0][0]);
   {
     const char* qp = reinterpret_cast<const char*>(P.q) + ((size_t)qrow * P.Hq + qh) * kRowBytes;
 #pragma unroll
@@ -139,8 +151,9 @@ void decode_mfma_kernel(DecodeParams P) {
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
   const size_t head_off = (size_t)g * kBlock * kRowBytes;
   const size_t block_stride = (size_t)P.Hkv * kBlock * kRowBytes;
-  const int k_lane = col * kRowBytes + 8 * rg * 2;       // + 64 B per kk
-  const int v_lane = (4 * rg) * kRowBytes + 8 * col * 2;  // + 1 row per j
+  // K and V tiles are loaded alike, whole 256-byte rows per load: lane holds
+  // chunk col (dims 8 col .. 8 col + 7) of row 4 rg + j in register j.
+  const int row_lane = (4 * rg) * kRowBytes + 8 * col * 2;  // + 1 row per j
 
   // Issue the loads of physical block b's tile (logical block blk) into
   // (kb, vb). An id outside the pool marks the group bad and loads nothing;
@@ -155,17 +168,27 @@ void decode_mfma_kernel(DecodeParams P) {
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kb[kk] = ld16(rk, k_lane + kk * 64);
+    for (int j = 0; j < 4; ++j) kb[j] = ld16(rk, row_lane + j * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vb[j] = ld16(rv, v_lane + j * kRowBytes);
+    for (int j = 0; j < 4; ++j) vb[j] = ld16(rv, row_lane + j * kRowBytes);
   };
 
   auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
+    // Transpose K through the wave's LDS stage into the A operand layout:
+    // step kk needs, in lane (rg, col), dims 32 kk + 8 rg .. + 7 (chunk
+    // 4 kk + rg) of row t = col. Rows are kStageRow apart (256 B + 16 B of
+    // padding), so both the row writes and the strided reads are free of
+    // bank conflicts.
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint4*>(stage + (4 * rg + j) * kStageRow + col * 16) = kb[j];
     f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[kk]), qop[kk],
-                                                  st, 0, 0, 0);
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 ka = *reinterpret_cast<const uint4*>(stage + col * kStageRow + (4 * kk + rg) * 16);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
+                                                  0, 0, 0);
+    }
     const int tok0 = blk * kBlock + 4 * rg;
     // Some column masks some row of this block (wave-uniform).
     const bool partial = blk * kBlock + kBlock > ctx_min;
@@ -217,7 +240,6 @@ void decode_mfma_kernel(DecodeParams P) {
   lsum = rows_sum(lsum);  // per query head: sum over the 4 row groups
 
   // Waves -> LDS -> one merged state per (head, dim).
-  __shared__ float sm_o[NW][16][D + kPad];
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ int sm_bad[NW];
 #pragma unroll
