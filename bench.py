@@ -181,7 +181,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="13b",
-                    choices=["tiny", "7b", "13b", "gqa", "cow", "13b_verify4", "gqa_chunk512"])
+                    choices=["tiny", "7b", "13b", "gqa", "cow", "prefix", "13b_verify4",
+                             "gqa_chunk512"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-context partition in tokens (default: the library's choice, "
                          "or the workload's own)")
@@ -237,6 +238,7 @@ def main():
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     slots = torch.empty(T, dtype=torch.int32, device=dev)
+    shared_kv = pa.shares_blocks(tb.block_tables)  # the caller's manager knows; so do the tables
     nbytes = algorithmic_bytes(spec, tb)
     log(f"[bench] NB={tb.NB} MB={tb.MB} T={T} pairs={len(tb.pairs)} max_ctx={max_ctx} "
         f"partition={partition} decode bytes={nbytes['decode'] / 1e9:.4f} GB")
@@ -256,10 +258,10 @@ def main():
             ev[0].record()
         if spec.chunk:
             pa.multi_query(q, k_cache, v_cache, bt, cl, qs, spec.scale, max_ctx, max_q,
-                           partition=partition, out=out, workspace=workspace)
+                           partition=partition, out=out, workspace=workspace, shared_kv=shared_kv)
         else:
             pa.decode(q, k_cache, v_cache, bt, cl, spec.scale, max_ctx, partition=partition,
-                      out=out, workspace=workspace)
+                      out=out, workspace=workspace, shared_kv=shared_kv)
         if ev is not None:
             ev[1].record()
 
@@ -353,7 +355,7 @@ def main():
                    "head_dim": spec.D, "block_size": 16, "partition": partition,
                    "max_ctx": max_ctx, "mean_ctx": round(float(tb.context_lens.mean()), 1),
                    "pool_blocks": tb.NB, "new_tokens": T, "query_rows": rows,
-                   "cow_pairs": len(tb.pairs),
+                   "cow_pairs": len(tb.pairs), "shared_kv": shared_kv,
                    "parallelism": "none (one GPU)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(T / (ms_step * 1e-3), 1),
@@ -370,7 +372,8 @@ def main():
         "parity_max_abs_err_vs_oracle": parity,
         "controls": controls,
     }
-    if spec.name == "cow":
+    if shared_kv:
+        # blocks shared by several sequences: K/V bytes of each block counted once
         ub = unique_decode_bytes(spec, tb)
         line["unique_decode_bytes"] = ub
         line["roofline_unique_GBps"] = round(ub / (dec_avg_ms * 1e-3) / 1e9, 1)

@@ -63,6 +63,18 @@ typedef enum {
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
+/*
+ * Flags of pa_decode / pa_multi_query.
+ *   PA_KV_SHARED  some physical block is referenced by more than one sequence
+ *                 of the call (forks, beams, a prefix cache: [P1] section 3,
+ *                 [P3] mechanism paragraph). K/V tiles are then read through
+ *                 the caches so that repeated reads of a shared block are
+ *                 served there; without it they are streamed past the caches
+ *                 (read once per step), which sustains a higher HBM rate.
+ *                 Results are the same either way; only speed differs.
+ */
+#define PA_KV_SHARED 1u
+
 /* Static, human-readable text for a status code. Never NULL. */
 const char* pa_status_str(pa_status s);
 
@@ -176,6 +188,7 @@ size_t pa_decode_workspace_bytes(int32_t rows, int32_t Hq, int32_t D,
  *   workspace      device buffer of at least
  *                  pa_decode_workspace_bytes(B, Hq, D, max_ctx, partition)
  *                  bytes, 256-byte aligned (may be NULL when that is 0)
+ *   flags          0 or PA_KV_SHARED; other bits give PA_EINVAL
  * L == 0 gives an all-zero row. A sequence whose L is negative or exceeds
  * min(max_ctx, MB * bs), or whose table holds an id outside [0, NB) at a
  * position it reads, gets an all-NaN output row and its K/V are not read.
@@ -185,8 +198,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
                     const int32_t* context_lens, int32_t B, int32_t Hq,
                     int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
                     int32_t max_ctx, float scale, int32_t partition,
-                    void* workspace, size_t workspace_bytes, pa_dtype dt,
-                    hipStream_t stream);
+                    void* workspace, size_t workspace_bytes, uint32_t flags,
+                    pa_dtype dt, hipStream_t stream);
 
 /*
  * pa_multi_query — causal attention of several new tokens per sequence over
@@ -224,7 +237,7 @@ pa_status pa_multi_query(void* out, const void* q, const void* k_cache,
                          int32_t max_q, int32_t Hq, int32_t Hkv, int32_t D,
                          int32_t bs, int32_t NB, int32_t MB, int32_t max_ctx,
                          float scale, int32_t partition, void* workspace,
-                         size_t workspace_bytes, pa_dtype dt,
+                         size_t workspace_bytes, uint32_t flags, pa_dtype dt,
                          hipStream_t stream);
 
 /*
@@ -265,11 +278,51 @@ pa_status pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t* child);
 pa_status pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t n,
                        int32_t* slots, int32_t* pair, int32_t* n_pairs);
 
-/* Drop `seq`; blocks no other sequence holds return to the free list. */
+/*
+ * As pa_bm_append, for tokens whose ids are known: tokens host int32 [n].
+ * Every block these tokens fill becomes shareable with later requests (see
+ * pa_bm_add_seq_cached). Appending tokens of unknown content (pa_bm_append)
+ * ends that for the rest of the sequence.
+ */
+pa_status pa_bm_append_tokens(pa_block_manager* bm, int32_t seq,
+                              const int32_t* tokens, int32_t n, int32_t* slots,
+                              int32_t* pair, int32_t* n_pairs);
+
+/*
+ * Prefix sharing across requests ([P3] mechanism paragraph: requests share
+ * KV blocks within and across a batch; [P2] introduction: prefix caching).
+ * A new sequence for a request whose prompt is tokens host int32 [n]: its
+ * first blocks are the longest run of the prompt's full blocks that some
+ * earlier pa_bm_append_tokens registered, with exactly this prefix, at most
+ * (n - 1) / block_size of them (at least one prompt token is left to
+ * process). *n_cached receives the number of prompt tokens already in the
+ * cache; continue with pa_bm_append_tokens(seq, tokens + *n_cached, ...).
+ * Blocks are matched on their exact token ids and on the exact preceding
+ * chain, never on a hash alone.
+ * A registered block that its last holder releases is kept, evictable: it
+ * counts as free, allocation uses the free list first and then evicts kept
+ * blocks in the order they were released (oldest first), dropping their
+ * registration.
+ */
+pa_status pa_bm_add_seq_cached(pa_block_manager* bm, const int32_t* tokens,
+                               int32_t n, int32_t* seq, int32_t* n_cached);
+
+/*
+ * Beam search ([P1] section 3: beams share prompt blocks): sequence dst drops
+ * its blocks and shares every block of src instead, as a pruned beam replaced
+ * by a surviving one. dst == src is a no-op.
+ */
+pa_status pa_bm_fork_into(pa_block_manager* bm, int32_t dst, int32_t src);
+
+/* Drop `seq`; blocks no other sequence holds become free (or kept, when
+ * registered for sharing). */
 pa_status pa_bm_free_seq(pa_block_manager* bm, int32_t seq);
 
 pa_status pa_bm_seq_len(const pa_block_manager* bm, int32_t seq, int32_t* len);
+/* Blocks an append may take: free ones plus kept (evictable) ones. */
 pa_status pa_bm_num_free(const pa_block_manager* bm, int32_t* n);
+/* Kept blocks: registered for sharing, held by no sequence. */
+pa_status pa_bm_num_cached(const pa_block_manager* bm, int32_t* n);
 pa_status pa_bm_refcount(const pa_block_manager* bm, int32_t block, int32_t* ref);
 
 /* The table of `seq`: up to cap ids to out (host int32), count to *n. */

@@ -9,7 +9,7 @@ provides device memory and streams only.
     write_kv(k_new, v_new, k_cache, v_cache, slot_mapping)    (in place)
     copy_blocks(k_cache, v_cache, pairs)                      (in place)
     decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx,
-           partition=None, out=None, workspace=None)     -> [B, Hq, D]
+           partition=None, out=None, workspace=None, shared_kv=False) -> [B, Hq, D]
     multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start,
                 scale, max_ctx, max_q, partition=None)   -> [Tq, Hq, D]
     BlockManager(num_blocks, block_size=16, free_order=None)
@@ -22,9 +22,9 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PAError, check, lib  # noqa: F401
+from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PA_KV_SHARED, PAError, check, lib  # noqa: F401
 
-__all__ = ["slot_mapping", "write_kv", "copy_blocks", "decode", "multi_query",
+__all__ = ["slot_mapping", "write_kv", "copy_blocks", "decode", "multi_query", "shares_blocks",
            "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError"]
 
@@ -120,6 +120,14 @@ def copy_blocks(k_cache, v_cache, pairs):
               "pa_copy_blocks")
 
 
+def shares_blocks(block_tables):
+    """Whether some physical block appears more than once in the tables
+    (host numpy array or tensor): the case for shared_kv=True."""
+    bt = np.asarray(block_tables.cpu() if hasattr(block_tables, "cpu") else block_tables)
+    ids = bt[bt >= 0]
+    return bool(ids.size) and np.unique(ids).size < ids.size
+
+
 def default_partition(B, Hq, Hkv, D, max_ctx):
     return int(lib().pa_decode_default_partition(B, Hq, Hkv, D, max_ctx))
 
@@ -129,7 +137,10 @@ def decode_workspace_bytes(B, Hq, D, max_ctx, partition):
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx, partition=None,
-           out=None, workspace=None):
+           out=None, workspace=None, shared_kv=False):
+    """Single-query decode attention (pa_decode). shared_kv: some block is
+    referenced by several sequences (forks, beams, prefix cache); K/V are then
+    read through the caches instead of streamed past them (PA_KV_SHARED)."""
     NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
     _i32(block_tables, "block_tables")
     _i32(context_lens, "context_lens")
@@ -159,17 +170,17 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx, part
         check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                               block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs,
                               NB, MB, int(max_ctx), float(scale), int(partition), ws_ptr, ws_bytes,
-                              _dt(q), _stream(dev)), "pa_decode")
+                              PA_KV_SHARED if shared_kv else 0, _dt(q), _stream(dev)), "pa_decode")
     return out
 
 
 def multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, max_ctx,
-                max_q, partition=None, out=None, workspace=None):
+                max_q, partition=None, out=None, workspace=None, shared_kv=False):
     """Causal attention of several new tokens per sequence (pa_multi_query).
 
     q [Tq, Hq, D]; query_start int32 [B + 1]: sequence s owns rows
     query_start[s] .. query_start[s+1]-1, the last tokens of its context.
-    max_q bounds the rows per sequence."""
+    max_q bounds the rows per sequence. shared_kv as for decode()."""
     NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
     _i32(block_tables, "block_tables")
     _i32(context_lens, "context_lens")
@@ -202,7 +213,8 @@ def multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start, sc
                                    v_cache.data_ptr(), block_tables.data_ptr(),
                                    context_lens.data_ptr(), query_start.data_ptr(), B, Tq,
                                    int(max_q), Hq, Hkv, D, bs, NB, MB, int(max_ctx), float(scale),
-                                   int(partition), ws_ptr, ws_bytes, _dt(q), _stream(dev)),
+                                   int(partition), ws_ptr, ws_bytes,
+                                   PA_KV_SHARED if shared_kv else 0, _dt(q), _stream(dev)),
               "pa_multi_query")
     return out
 
@@ -249,6 +261,37 @@ class BlockManager:
         check(st, "pa_bm_append")
         pairs = [(int(pair[0]), int(pair[1]))] if npairs.value else []
         return slots[:n].tolist(), pairs
+
+    def append_tokens(self, sid, tokens):
+        """Append tokens with known ids (their full blocks become shareable)."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        n = toks.shape[0]
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        pair = np.empty(2, dtype=np.int32)
+        npairs = ctypes.c_int32()
+        check(lib().pa_bm_append_tokens(self._h, sid, toks.ctypes.data if n else None, n,
+                                        slots.ctypes.data, pair.ctypes.data,
+                                        ctypes.byref(npairs)), "pa_bm_append_tokens")
+        pairs = [(int(pair[0]), int(pair[1]))] if npairs.value else []
+        return slots[:n].tolist(), pairs
+
+    def add_seq_cached(self, tokens):
+        """New sequence reusing the registered prefix of `tokens`: (seq, n_cached)."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+        n = toks.shape[0]
+        sid, nc = ctypes.c_int32(), ctypes.c_int32()
+        check(lib().pa_bm_add_seq_cached(self._h, toks.ctypes.data if n else None, n,
+                                         ctypes.byref(sid), ctypes.byref(nc)),
+              "pa_bm_add_seq_cached")
+        return sid.value, nc.value
+
+    def fork_into(self, dst, src):
+        check(lib().pa_bm_fork_into(self._h, dst, src), "pa_bm_fork_into")
+
+    def num_cached(self):
+        out = ctypes.c_int32()
+        check(lib().pa_bm_num_cached(self._h, ctypes.byref(out)), "pa_bm_num_cached")
+        return out.value
 
     def free_seq(self, sid):
         check(lib().pa_bm_free_seq(self._h, sid), "pa_bm_free_seq")

@@ -11,6 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 c_i32, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+c_u32 = ctypes.c_uint32
 c_i32p = ctypes.POINTER(ctypes.c_int32)
 
 # name -> (restype, argtypes), in the order of include/pa.h
@@ -23,18 +24,22 @@ SIGNATURES = {
     "pa_decode_default_partition": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
-                          c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_i32, c_vp]),
+                          c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_i32, c_vp]),
     "pa_multi_query": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32,
-                               c_vp, c_sz, c_i32, c_vp]),
+                               c_vp, c_sz, c_u32, c_i32, c_vp]),
     "pa_bm_create": (c_i32, [ctypes.POINTER(c_vp), c_i32, c_i32, c_vp]),
     "pa_bm_destroy": (None, [c_vp]),
     "pa_bm_add_seq": (c_i32, [c_vp, c_i32p]),
     "pa_bm_fork": (c_i32, [c_vp, c_i32, c_i32p]),
     "pa_bm_append": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp, c_i32p]),
+    "pa_bm_append_tokens": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32p]),
+    "pa_bm_add_seq_cached": (c_i32, [c_vp, c_vp, c_i32, c_i32p, c_i32p]),
+    "pa_bm_fork_into": (c_i32, [c_vp, c_i32, c_i32]),
     "pa_bm_free_seq": (c_i32, [c_vp, c_i32]),
     "pa_bm_seq_len": (c_i32, [c_vp, c_i32, c_i32p]),
     "pa_bm_num_free": (c_i32, [c_vp, c_i32p]),
+    "pa_bm_num_cached": (c_i32, [c_vp, c_i32p]),
     "pa_bm_refcount": (c_i32, [c_vp, c_i32, c_i32p]),
     "pa_bm_block_table": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_i32p]),
     "pa_bm_fill_tables": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_vp, c_vp]),
@@ -42,6 +47,7 @@ SIGNATURES = {
 
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOBLOCKS = 0, -1, -2, -3, -4, -5
 PA_F32, PA_BF16 = 0, 1
+PA_KV_SHARED = 1
 
 _lib = None
 

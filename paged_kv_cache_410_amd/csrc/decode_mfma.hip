@@ -68,7 +68,7 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int k) {
 
 }  // namespace
 
-template <int NW, int DEPTH>
+template <int NW, int DEPTH, TilePolicy kPolicy>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES)))
 void decode_mfma_kernel(DecodeParams P) {
   constexpr int D = 128;
@@ -168,9 +168,9 @@ void decode_mfma_kernel(DecodeParams P) {
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kb[j] = ld16(rk, row_lane + j * kRowBytes);
+    for (int j = 0; j < 4; ++j) kb[j] = ld16<kPolicy>(rk, row_lane + j * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vb[j] = ld16(rv, row_lane + j * kRowBytes);
+    for (int j = 0; j < 4; ++j) vb[j] = ld16<kPolicy>(rv, row_lane + j * kRowBytes);
   };
 
   auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
@@ -314,7 +314,12 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
   constexpr int DEPTH = PA_MFMA_DEPTH;
   const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B), block(NW * kWave);
-  hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH>), grid, block, 0, stream, p);
+  if (p.shared_kv)
+    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared>), grid, block, 0, stream,
+                       p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream>), grid, block, 0, stream,
+                       p);
   return hipGetLastError();
 }
 

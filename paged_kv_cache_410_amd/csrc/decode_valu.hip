@@ -111,7 +111,7 @@ __device__ __forceinline__ void merge_all_rows(float& m, float& l, float (&o)[EP
 
 }  // namespace
 
-template <typename T, int D, int NW, int DEPTH>
+template <typename T, int D, int NW, int DEPTH, TilePolicy kPolicy>
 __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P) {
   constexpr int EPL = Elem<T>::kPerChunk;  // elements per 16-byte lane chunk
   constexpr int LPT = D / EPL;             // lanes per token row
@@ -183,9 +183,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) kb[j] = ld16(rk, lane_off + j * TPI * kRowBytes);
+    for (int j = 0; j < NLD; ++j) kb[j] = ld16<kPolicy>(rk, lane_off + j * TPI * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) vb[j] = ld16(rv, lane_off + j * TPI * kRowBytes);
+    for (int j = 0; j < NLD; ++j) vb[j] = ld16<kPolicy>(rv, lane_off + j * TPI * kRowBytes);
   };
 
   // Consume one tile: logits, online-softmax update, V accumulation.
@@ -324,21 +324,31 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   }
 }
 
-hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
+template <TilePolicy kPolicy>
+hipError_t launch_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
   constexpr int NW = PA_VALU_WAVES;
   constexpr int DEPTH = PA_VALU_DEPTH;
   const dim3 grid(p.Hq * p.max_q, p.n_parts, p.B), block(NW * kWave);
   if (dtype == 1 && D == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW, DEPTH>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW, DEPTH, kPolicy>), grid, block, 0,
+                       stream, p);
   else if (dtype == 1 && D == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW, DEPTH>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW, DEPTH, kPolicy>), grid, block, 0,
+                       stream, p);
   else if (dtype == 0 && D == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW, DEPTH>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW, DEPTH, kPolicy>), grid, block, 0,
+                       stream, p);
   else if (dtype == 0 && D == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW, DEPTH>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW, DEPTH, kPolicy>), grid, block, 0,
+                       stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
+  return p.shared_kv ? launch_valu<TilePolicy::kShared>(p, dtype, D, stream)
+                     : launch_valu<TilePolicy::kStream>(p, dtype, D, stream);
 }
 
 }  // namespace pa

@@ -127,9 +127,9 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
                     const int32_t* query_start, int32_t B, int32_t rows, int32_t max_q, int32_t Hq,
                     int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB, int32_t max_ctx,
                     float scale, int32_t partition, void* workspace, size_t workspace_bytes,
-                    pa_dtype dt, hipStream_t stream) {
+                    uint32_t flags, pa_dtype dt, hipStream_t stream) {
   if (B < 0 || rows < 0 || max_q < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || NB < 0 || MB < 0 ||
-      max_ctx < 0 || !dtype_ok(dt))
+      max_ctx < 0 || !dtype_ok(dt) || (flags & ~PA_KV_SHARED) != 0)
     return PA_EINVAL;
   if (Hq % Hkv != 0) return PA_EINVAL;
   if (partition < 0 || partition % kBs != 0) return PA_EINVAL;
@@ -171,6 +171,7 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   p.rows = rows;
   p.n_tiles = (int32_t)(((int64_t)max_q * p.G + 15) / 16);
   p.qscale = scale * 1.4426950408889634f;
+  p.shared_kv = (flags & PA_KV_SHARED) ? 1 : 0;
   if (parts > 1) {
     const size_t nrows = (size_t)rows * Hq * (size_t)parts;
     p.ws_ml = static_cast<float*>(workspace);
@@ -199,9 +200,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                     int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
                     int32_t max_ctx, float scale, int32_t partition, void* workspace,
-                    size_t workspace_bytes, pa_dtype dt, hipStream_t stream) {
+                    size_t workspace_bytes, uint32_t flags, pa_dtype dt, hipStream_t stream) {
   return attention(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, B, B, 1, Hq, Hkv,
-                   D, bs, NB, MB, max_ctx, scale, partition, workspace, workspace_bytes, dt,
+                   D, bs, NB, MB, max_ctx, scale, partition, workspace, workspace_bytes, flags, dt,
                    stream);
 }
 
@@ -210,11 +211,12 @@ pa_status pa_multi_query(void* out, const void* q, const void* k_cache, const vo
                          const int32_t* query_start, int32_t B, int32_t Tq, int32_t max_q,
                          int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
                          int32_t max_ctx, float scale, int32_t partition, void* workspace,
-                         size_t workspace_bytes, pa_dtype dt, hipStream_t stream) {
+                         size_t workspace_bytes, uint32_t flags, pa_dtype dt,
+                         hipStream_t stream) {
   if (B > 0 && Tq > 0 && !query_start) return PA_EINVAL;
   return attention(out, q, k_cache, v_cache, block_tables, context_lens, query_start, B, Tq,
                    max_q, Hq, Hkv, D, bs, NB, MB, max_ctx, scale, partition, workspace,
-                   workspace_bytes, dt, stream);
+                   workspace_bytes, flags, dt, stream);
 }
 
 }  // extern "C"

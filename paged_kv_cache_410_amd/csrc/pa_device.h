@@ -155,12 +155,17 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
-// Cache-policy bits of the K/V tile loads (0 = default caching).
-#ifndef PA_TILE_AUX
-#define PA_TILE_AUX 2
-#endif
+// Cache policy of the K/V tile loads. Streaming (the non-temporal bit): K/V
+// read once per step pass the caches by, which sustains a higher HBM rate.
+// Shared (default caching): when several sequences read the same physical
+// blocks (forks, beams, a prefix cache), the caches serve the repeats.
+// Measured on the 13B-shape batch: streaming 256 us vs cached 288 us; on the
+// copy-on-write batch: cached 183 us vs streaming 273 us.
+enum class TilePolicy { kStream, kShared };
+template <TilePolicy kPolicy>
 __device__ __forceinline__ uint4 ld16(rsrc_t r, int off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PA_TILE_AUX));
+  constexpr int kAux = kPolicy == TilePolicy::kStream ? 2 : 0;  // nt bit
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux));
 }
 
 // Software pipeline over the blocks one wave reads: logical blocks

@@ -26,6 +26,7 @@ struct DecodeParams {
   int32_t rows;                 // query rows in q / out (B for decode)
   int32_t n_tiles;              // MFMA: 16-column tiles per kv head (rows x heads per group)
   float qscale;                 // scale * log2(e): logits are kept in the log2 domain
+  int32_t shared_kv;            // K/V tiles read through the caches (blocks shared by sequences)
 };
 
 // The query rows of sequence s and the context each row attends over.

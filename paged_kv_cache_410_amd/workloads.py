@@ -21,6 +21,11 @@ Workloads (lengths, seeds and draw order are fixed here):
         1024 - r, r ~ U{1..15} (so the last prompt block is partly filled and
         shared by 8 samples); each sample then gets a private tail of
         U{1..256} tokens.                                           seed 4
+  prefix  bf16, 128 requests, 32/32 heads, head_dim 128, all starting with one
+        1024-token system prompt (seeded token ids) followed by a private tail
+        of U{16..512} tokens; the block manager must share prompt blocks
+        across requests (prefix cache), so the 64 prompt blocks are held by
+        all 128 sequences.                                          seed 7
   13b_verify4   the 13b shapes and length mix with 4 new tokens per
         sequence (several drafted tokens checked in one pass).      seed 5
   gqa_chunk512  bf16, 16 seqs, 64/8 heads, head_dim 128, contexts
@@ -65,6 +70,7 @@ class Spec:
     bs: int = 16
     cow: dict = field(default_factory=dict)  # prompts, samples, prompt_len, r_max, tail_lo, tail_hi
     chunk: tuple = ()          # several new tokens per sequence: ("uniform", lo, hi) | ("all",)
+    prefix: dict = field(default_factory=dict)  # shared, tail_lo, tail_hi, vocab
 
     @property
     def scale(self):
@@ -80,6 +86,9 @@ CONFIGS = {
     "cow": Spec("cow", "bf16", 128, 32, 32, 128, seed=4, lengths=("cow",),
                 cow=dict(prompts=16, samples=8, prompt_len=1024, r_max=15, tail_lo=1, tail_hi=256)),
     # several new tokens per sequence (multi-query attention, causal within the chunk)
+    # requests sharing one system prompt through the prefix cache
+    "prefix": Spec("prefix", "bf16", 128, 32, 32, 128, seed=7, lengths=("prefix",),
+                   prefix=dict(shared=1024, tail_lo=16, tail_hi=512, vocab=32000)),
     "13b_verify4": Spec("13b_verify4", "bf16", 128, 40, 40, 128, seed=5,
                         lengths=("lognormal", 500.0, 0.7, 16, 2048), chunk=("uniform", 4, 4)),
     "gqa_chunk512": Spec("gqa_chunk512", "bf16", 16, 64, 8, 128, seed=6,
@@ -94,7 +103,8 @@ def torch_dtype(spec):
 def draw_lengths(spec, rng):
     """Final context lengths (history + the step's tokens), int64 [B].
 
-    For cow also returns (prompt_lens [prompts], tail_lens [B])."""
+    For cow also returns (prompt_lens [prompts], tail_lens [B]); for prefix
+    ("prefix", shared prompt token ids, per-request tail token ids)."""
     kind = spec.lengths[0]
     if kind == "fixed":
         ctx = np.asarray(spec.lengths[1], dtype=np.int64)
@@ -107,6 +117,13 @@ def draw_lengths(spec, rng):
         med, sigma, lo, hi = spec.lengths[1:]
         raw = np.exp(rng.normal(math.log(med), sigma, size=spec.B))
         return np.clip(np.rint(raw), lo, hi).astype(np.int64), None
+    if kind == "prefix":
+        c = spec.prefix
+        tails = rng.integers(c["tail_lo"], c["tail_hi"], size=spec.B, endpoint=True)
+        shared = rng.integers(0, c["vocab"], size=c["shared"])
+        tail_ids = [rng.integers(0, c["vocab"], size=int(t)) for t in tails]
+        ctx = (c["shared"] + tails).astype(np.int64)
+        return ctx, ("prefix", shared, tail_ids)
     if kind == "cow":
         c = spec.cow
         r = rng.integers(1, c["r_max"], size=c["prompts"], endpoint=True)
@@ -137,7 +154,24 @@ def _populate(spec, bm, ctx, cow_parts, n_new):
         step_seq.extend([i] * n)
         step_pos.extend(range(start, start + n))
 
-    if cow_parts is None:
+    if cow_parts is not None and isinstance(cow_parts[0], str):
+        # requests share the system prompt's full blocks through the prefix
+        # cache: the first request registers them, the others reuse them
+        _, shared, tail_ids = cow_parts
+        for s in range(spec.B):
+            tokens = np.concatenate([shared, tail_ids[s]]).astype(np.int32)
+            sid, n_cached = bm.add_seq_cached(tokens[:-1])
+            seqs.append(sid)
+            bm.append_tokens(sid, tokens[n_cached:-1])       # history (untimed)
+        for i, sid in enumerate(seqs):
+            start = bm.seq_len(sid)
+            tokens = np.concatenate([shared, tail_ids[i]]).astype(np.int32)
+            slots, pairs = bm.append_tokens(sid, tokens[-1:])  # the step's token
+            step_slots.extend(slots)
+            step_pairs.extend(pairs)
+            step_seq.append(i)
+            step_pos.append(start)
+    elif cow_parts is None:
         for s in range(spec.B):
             sid = bm.add_seq()
             seqs.append(sid)

@@ -57,7 +57,8 @@ class Step:
 
     def __init__(self, spec, values_device="cpu", poison=False, oracle_full=True):
         self.spec = spec
-        self.tb = workloads.make_tables(spec, oracle.BlockManager)
+        # the prefix-sharing manager does everything the plain one does, the same way
+        self.tb = workloads.make_tables(spec, oracle.blockmgr.PrefixBlockManager)
         tb = self.tb
         vals = workloads.make_values(spec, tb.NB, len(tb.slots), device=values_device)
         dev = torch.device("cuda")
@@ -122,14 +123,18 @@ class Step:
         pa.write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, slots)
         return slots
 
-    def multi(self, pa, partition=None):
+    def multi(self, pa, partition=None, shared_kv=None):
+        if shared_kv is None:
+            shared_kv = pa.shares_blocks(self.tb.block_tables)
         return pa.multi_query(self.q, self.k_cache, self.v_cache, self.block_tables,
                               self.context_lens, self.query_start, self.spec.scale, self.max_ctx,
-                              self.max_q, partition=partition)
+                              self.max_q, partition=partition, shared_kv=shared_kv)
 
-    def decode(self, pa, partition=None):
+    def decode(self, pa, partition=None, shared_kv=None):
+        if shared_kv is None:
+            shared_kv = pa.shares_blocks(self.tb.block_tables)
         return pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
-                         self.spec.scale, self.max_ctx, partition=partition)
+                         self.spec.scale, self.max_ctx, partition=partition, shared_kv=shared_kv)
 
 
 def max_abs_err(got, expect):

@@ -65,11 +65,11 @@ FAKE = 0x7F0000000000
 
 def decode_args(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=2, Hq=8, Hkv=8, D=128, bs=16,
-             NB=10, MB=4, max_ctx=64, scale=0.1, partition=0, ws=None, ws_bytes=0, dt=1,
+             NB=10, MB=4, max_ctx=64, scale=0.1, partition=0, ws=None, ws_bytes=0, flags=0, dt=1,
              stream=None)
     a.update(kw)
     return [a[k] for k in ("out", "q", "k", "v", "bt", "cl", "B", "Hq", "Hkv", "D", "bs", "NB",
-                           "MB", "max_ctx", "scale", "partition", "ws", "ws_bytes", "dt",
+                           "MB", "max_ctx", "scale", "partition", "ws", "ws_bytes", "flags", "dt",
                            "stream")]
 
 
@@ -81,7 +81,7 @@ def decode_args(**kw):
     (dict(q=FAKE + 8), -1),
     (dict(partition=16, max_ctx=64), -3),
     (dict(partition=16, max_ctx=64, ws=FAKE, ws_bytes=10), -3),
-    (dict(B=70000), -2),
+    (dict(B=70000), -2), (dict(flags=2), -1), (dict(flags=0x80000000), -1),
 ])
 def test_decode_rejects_bad_arguments(palib, kw, status):
     assert palib.lib().pa_decode(*decode_args(**kw)) == status
@@ -94,11 +94,11 @@ def test_decode_empty_batch_is_a_noop(palib):
 def multi_args(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, B=2, Tq=6, max_q=4,
              Hq=8, Hkv=2, D=128, bs=16, NB=10, MB=4, max_ctx=64, scale=0.1, partition=0,
-             ws=None, ws_bytes=0, dt=1, stream=None)
+             ws=None, ws_bytes=0, flags=0, dt=1, stream=None)
     a.update(kw)
     return [a[k] for k in ("out", "q", "k", "v", "bt", "cl", "qs", "B", "Tq", "max_q", "Hq",
                            "Hkv", "D", "bs", "NB", "MB", "max_ctx", "scale", "partition", "ws",
-                           "ws_bytes", "dt", "stream")]
+                           "ws_bytes", "flags", "dt", "stream")]
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -106,7 +106,7 @@ def multi_args(**kw):
     (dict(Hq=6, Hkv=4), -1), (dict(partition=8), -1), (dict(D=80), -2), (dict(bs=32), -2),
     (dict(max_q=70000), -2), (dict(B=70000), -2),
     (dict(partition=16, max_ctx=64), -3),
-    (dict(out=FAKE + 4), -1),
+    (dict(out=FAKE + 4), -1), (dict(flags=4), -1),
 ])
 def test_multi_query_rejects_bad_arguments(palib, kw, status):
     assert palib.lib().pa_multi_query(*multi_args(**kw)) == status
@@ -211,12 +211,91 @@ def test_native_bm_matches_oracle(palib, ops, seed, nb):
 def test_native_bm_workload_tables_match_oracle(palib):
     """The benchmark's tables (native manager) equal the tests' (oracle manager)."""
     from paged_kv_cache_410_amd import workloads
-    for name in ("tiny", "13b", "cow"):
+    for name in ("tiny", "13b", "cow", "prefix", "13b_verify4"):
         spec = workloads.CONFIGS[name]
-        ta = workloads.make_tables(spec, oracle_bm.BlockManager)
+        ta = workloads.make_tables(spec, oracle_bm.PrefixBlockManager)
         tb = workloads.make_tables(spec, native_bm)
         assert ta.NB == tb.NB and ta.MB == tb.MB
         assert np.array_equal(ta.block_tables, tb.block_tables)
         assert np.array_equal(ta.context_lens, tb.context_lens)
         assert np.array_equal(ta.slots, tb.slots)
         assert np.array_equal(ta.pairs, tb.pairs)
+
+
+# ---------------------------------------- native block manager v2 (prefix sharing)
+ops_v2 = st.lists(st.tuples(st.sampled_from(["new", "tok", "unk", "fork", "into", "free"]),
+                            st.integers(0, 10**6), st.integers(0, 10**6),
+                            st.lists(st.integers(0, 2), min_size=0, max_size=40)),
+                  max_size=60)
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(ops=ops_v2, seed=st.integers(0, 2**31 - 1), nb=st.integers(2, 40),
+       bs=st.sampled_from([2, 4, 16]))
+def test_native_prefix_bm_matches_oracle(palib, ops, seed, nb, bs):
+    """Beam re-forks, prefix sharing, kept blocks and eviction: the native
+    manager hands out the same blocks as the oracle's, call by call."""
+    from paged_kv_cache_410_amd import PAError
+    order = np.random.default_rng(seed).permutation(nb)
+    a = oracle_bm.PrefixBlockManager(nb, bs, order)
+    b = native_bm(nb, bs, order)
+    ids = {}
+    for op, i, j, toks in ops:
+        live = sorted(ids)
+        if op == "new" or not live:
+            sa, ca = a.add_seq_cached(toks)
+            sb, cb = b.add_seq_cached(toks)
+            assert ca == cb
+            ids[sa] = sb
+            op, toks = "tok", toks[ca:]
+            live = sorted(ids)
+            i = live.index(sa)
+        sa = live[i % len(live)]
+        sb = ids[sa]
+        if op in ("tok", "unk"):
+            try:
+                ra = a.append_tokens(sa, toks) if op == "tok" else a.append(sa, len(toks))
+            except oracle_bm.OutOfBlocks:
+                with pytest.raises(PAError) as e:
+                    if op == "tok":
+                        b.append_tokens(sb, toks)
+                    else:
+                        b.append(sb, len(toks))
+                assert e.value.status == -5
+                continue
+            rb = b.append_tokens(sb, toks) if op == "tok" else b.append(sb, len(toks))
+            assert ra == (rb[0], rb[1])
+        elif op == "fork":
+            ids[a.fork(sa)] = b.fork(sb)
+        elif op == "into":
+            da = live[j % len(live)]
+            a.fork_into(da, sa)
+            b.fork_into(ids[da], sb)
+        else:
+            a.free_seq(sa)
+            b.free_seq(sb)
+            del ids[sa]
+        assert a.num_free() == b.num_free()
+        assert a.num_cached() == b.num_cached()
+        for x, y in ids.items():
+            assert a.block_table(x) == b.block_table(y)
+            assert a.seq_len(x) == b.seq_len(y)
+        assert [a.refcount(k) for k in range(nb)] == [b.refcount(k) for k in range(nb)]
+
+
+def test_native_prefix_bm_rejects_bad_arguments(palib):
+    lib = palib.lib()
+    import ctypes
+    h = ctypes.c_void_p()
+    assert lib.pa_bm_create(ctypes.byref(h), 8, 4, None) == 0
+    s, n = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.pa_bm_add_seq_cached(h, None, 3, ctypes.byref(s), ctypes.byref(n)) == -1
+    assert lib.pa_bm_add_seq_cached(h, None, 0, ctypes.byref(s), ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.pa_bm_fork_into(h, s.value, 999) == -1
+    slots = np.zeros(4, np.int32)
+    pair = np.zeros(2, np.int32)
+    npairs = ctypes.c_int32()
+    assert lib.pa_bm_append_tokens(h, s.value, None, 2, slots.ctypes.data, pair.ctypes.data,
+                                   ctypes.byref(npairs)) == -1
+    lib.pa_bm_destroy(h)

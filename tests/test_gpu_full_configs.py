@@ -41,7 +41,8 @@ def sample_rows(tb, Hq, n, seed):
     return list(zip(rows, heads))
 
 
-@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "cow", "13b_verify4", "gqa_chunk512"])
+@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "cow", "prefix", "13b_verify4",
+                                  "gqa_chunk512"])
 def test_full_config(pa, name):
     spec = workloads.CONFIGS[name]
     say(f"[full config] {name}: building inputs")

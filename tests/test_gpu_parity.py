@@ -47,6 +47,8 @@ SMALL = {
     "cow_small": Spec("cow_small", "bf16", 8, 4, 4, 128, seed=21, lengths=("cow",),
                       cow=dict(prompts=2, samples=4, prompt_len=96, r_max=15, tail_lo=1,
                                tail_hi=40)),
+    "prefix_small": Spec("prefix_small", "bf16", 6, 4, 2, 128, seed=26, lengths=("prefix",),
+                         prefix=dict(shared=80, tail_lo=1, tail_hi=40, vocab=50)),
     "cow_gqa": Spec("cow_gqa", "bf16", 6, 8, 2, 128, seed=22, lengths=("cow",),
                     cow=dict(prompts=2, samples=3, prompt_len=64, r_max=15, tail_lo=1,
                              tail_hi=30)),
@@ -90,6 +92,18 @@ def test_decode_matches_oracle(pa, name, partition):
     assert err <= TOL[spec.dtype]
 
 
+@pytest.mark.parametrize("name", ["mha_bf16", "gqa8", "tiny", "cow_small", "prefix_small"])
+def test_cache_policy_gives_identical_bits(pa, name):
+    """Streaming and cached tile loads (PA_KV_SHARED) move the same bits."""
+    say(f"[cache policy] {name}")
+    st = Step(SMALL[name], oracle_full=False)
+    st.run_cache_ops(pa)
+    for part in (0, 64):
+        a = st.decode(pa, partition=part, shared_kv=False)
+        b = st.decode(pa, partition=part, shared_kv=True)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), part
+
+
 def test_decode_deterministic_and_permutation_invariant(pa):
     """Same inputs twice -> same bits; physical blocks moved elsewhere (tables
     remapped) -> same bits: the arithmetic order never depends on block ids."""
@@ -112,9 +126,12 @@ def test_decode_deterministic_and_permutation_invariant(pa):
         assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-def test_decode_cow_shared_equals_private(pa):
-    say("[decode cow vs private] cow_small")
-    st = Step(SMALL["cow_small"], oracle_full=False)
+@pytest.mark.parametrize("name", ["cow_small", "prefix_small"])
+def test_decode_shared_blocks_equal_private_copies(pa, name):
+    """Blocks shared by forks (copy-on-write) or across requests (prefix
+    cache) give the bits that private copies of them give."""
+    say(f"[decode shared vs private] {name}")
+    st = Step(SMALL[name], oracle_full=False)
     st.run_cache_ops(pa)
     shared = st.decode(pa, partition=32).clone()
     bt = st.tb.block_tables.copy()
