@@ -47,6 +47,13 @@
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 2
 #endif
+// Waves (column tiles) per workgroup and ring depth when several column tiles share the blocks.
+#ifndef PA_MFMA_COL_WAVES
+#define PA_MFMA_COL_WAVES 8
+#endif
+#ifndef PA_MFMA_COL_DEPTH
+#define PA_MFMA_COL_DEPTH 2
+#endif
 // Minimum waves per SIMD the register allocation must allow.
 #ifndef PA_MFMA_MIN_WAVES
 #define PA_MFMA_MIN_WAVES 3
@@ -68,7 +75,14 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int k) {
 
 }  // namespace
 
-template <int NW, int DEPTH, TilePolicy kPolicy>
+// kColWaves (a kv head with more than one 16-column tile: several query rows
+// per sequence): the workgroup's waves take NW consecutive column tiles and
+// each streams every block of the partition, in the same order at about the
+// same time, so the repeats are served by the CU's caches and a K/V tile
+// leaves HBM about once per NW tiles. A wave then holds its columns' whole
+// state and writes them itself. Otherwise the waves interleave the blocks of
+// one tile and merge through LDS.
+template <int NW, int DEPTH, TilePolicy kPolicy, bool kColWaves>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES)))
 void decode_mfma_kernel(DecodeParams P) {
   constexpr int D = 128;
@@ -84,20 +98,24 @@ void decode_mfma_kernel(DecodeParams P) {
 
   const GridPos gp = grid_pos();
   const int p = gp.y;
-  const int g = gp.x / P.n_tiles;     // kv head
-  const int tile = gp.x % P.n_tiles;  // 16-column tile of this kv head's (row, head) pairs
+  const int groups = kColWaves ? (P.n_tiles + NW - 1) / NW : P.n_tiles;  // per kv head
+  const int g = gp.x / groups;        // kv head
+  // 16-column tile of this kv head's (row, head) pairs
+  const int tile = kColWaves ? (gp.x % groups) * NW + w : gp.x % P.n_tiles;
   const int s = gp.z;
 
   const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
   const int blk_begin = p * bpp;
-  const int first = blk_begin + w;       // this wave's blocks: first, first + NW, ...
+  // this wave's blocks: first, first + kStride, ...
+  constexpr int kStride = kColWaves ? 1 : NW;
+  const int first = kColWaves ? blk_begin : blk_begin + w;
 
   // Start-up loads, issued before anything waits on them: the wave's first 64
   // block ids (bounded by the partition's table range, as the context length
   // is not known yet), the sequence's rows and context length, the queries.
-  const int ids0 = first_chunk_ids(bt_row, first, NW, bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB,
-                                   lane);
+  const int ids0 = first_chunk_ids(bt_row, first, kStride,
+                                   bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB, lane);
   const SeqRows sr = seq_rows(P, s);
   // Columns of this tile: global column gc = 16 tile + col of the n x G grid
   // of (query row, head of the group), row-major; gc >= n G is padding.
@@ -205,11 +223,18 @@ void decode_mfma_kernel(DecodeParams P) {
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = exp2_fast(m - m_use);
+    // The accumulators need rescaling only when some column's max rose; for
+    // the others alpha is exactly 2^0 = 1, so skipping is bit-identical.
+    const bool rescale = __builtin_amdgcn_ballot_w64(m_new > m) != 0;
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(x[i] - m_use);
     lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m = m_new;
+    if (rescale) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    }
     const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
     const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
     const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
@@ -219,25 +244,71 @@ void decode_mfma_kernel(DecodeParams P) {
       const uint32_t w2 = word(vb[2], k), w3 = word(vb[3], k);
       const s16x4_t a_lo = __builtin_bit_cast(s16x4_t, make_uint2(pack_lo16(w0, w1), pack_lo16(w2, w3)));
       const s16x4_t a_hi = __builtin_bit_cast(s16x4_t, make_uint2(pack_hi16(w0, w1), pack_hi16(w2, w3)));
-      acc[2 * k] *= alpha;
-      acc[2 * k + 1] *= alpha;
       acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, pop, acc[2 * k], 0, 0, 0);
       acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, pop, acc[2 * k + 1], 0, 0, 0);
     }
   };
 
-  // This wave's blocks: first + k * NW, k < nk, through a ring of DEPTH tiles.
+  // This wave's blocks: first + k * kStride, k < nk, through a ring of DEPTH tiles.
   {
-    const int nk = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
+    const int nk = first < blk_end ? (blk_end - first + kStride - 1) / kStride : 0;
     uint4 kb[DEPTH][4], vb[DEPTH][4];
     block_pipeline<DEPTH>(
-        bt_row, first, NW, nk, lane, ids0,
-        [&](int d, int b, int k, bool exists) { load(kb[d], vb[d], b, first + k * NW, exists); },
-        [&](int d, int k) { consume(kb[d], vb[d], first + k * NW); });
+        bt_row, first, kStride, nk, lane, ids0,
+        [&](int d, int b, int k, bool exists) {
+          load(kb[d], vb[d], b, first + k * kStride, exists);
+        },
+        [&](int d, int k) { consume(kb[d], vb[d], first + k * kStride); });
   }
 
+  lsum = rows_sum(lsum);  // per column: sum over the 4 row groups
 
-  lsum = rows_sum(lsum);  // per query head: sum over the 4 row groups
+  if constexpr (kColWaves) {
+    // The wave holds its columns' whole state for this partition: lane
+    // (rg, col) writes dims 8 (4 rg + i) + 0..7 (i = 0..3) of column col,
+    // from acc[0..7][i].
+    if (!col_ok) return;
+    const int i = gc / P.G;
+    const int h = g * P.G + gc % P.G;
+    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
+    const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
+    if (np <= 1 ? p != 0 : p >= np) return;
+    const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
+    const float nan = __builtin_nanf("");
+    if (np > 1) {
+      const size_t part = orow * P.n_parts + p;
+      float* dst = P.ws_o + part * D;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float* d8 = dst + 8 * (4 * rg + ii);
+        *reinterpret_cast<float4*>(d8) =
+            bad ? make_float4(nan, nan, nan, nan)
+                : make_float4(acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]);
+        *reinterpret_cast<float4*>(d8 + 4) =
+            bad ? make_float4(nan, nan, nan, nan)
+                : make_float4(acc[4][ii], acc[5][ii], acc[6][ii], acc[7][ii]);
+      }
+      if (rg == 0) {
+        P.ws_ml[2 * part] = bad ? 0.0f : m;
+        P.ws_ml[2 * part + 1] = bad ? nan : lsum;
+      }
+    } else {
+      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float res[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) res[e] = bad ? nan : acc[e][ii] * inv;
+        uint4 u;
+        u.x = pack_bf16x2(res[0], res[1]);
+        u.y = pack_bf16x2(res[2], res[3]);
+        u.z = pack_bf16x2(res[4], res[5]);
+        u.w = pack_bf16x2(res[6], res[7]);
+        st16(reinterpret_cast<char*>(P.out) + (orow * D + 8 * (4 * rg + ii)) * 2, u);
+      }
+    }
+    return;
+  }
 
   // Waves -> LDS -> one merged state per (head, dim).
   __shared__ float sm_m[NW][16], sm_l[NW][16];
@@ -313,13 +384,22 @@ void decode_mfma_kernel(DecodeParams P) {
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
   constexpr int DEPTH = PA_MFMA_DEPTH;
-  const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B), block(NW * kWave);
-  if (p.shared_kv)
-    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared>), grid, block, 0, stream,
-                       p);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream>), grid, block, 0, stream,
-                       p);
+  const dim3 block(NW * kWave);
+  if (p.n_tiles > 1) {
+    // waves of a workgroup share each block: read through the caches
+    constexpr int CW = PA_MFMA_COL_WAVES;
+    const dim3 grid(p.Hkv * ((p.n_tiles + CW - 1) / CW), p.n_parts, p.B);
+    hipLaunchKernelGGL((decode_mfma_kernel<CW, PA_MFMA_COL_DEPTH, TilePolicy::kShared, true>), grid,
+                       dim3(CW * kWave), 0, stream, p);
+  } else {
+    const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B);
+    if (p.shared_kv)
+      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared, false>), grid, block,
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream, false>), grid, block,
+                         0, stream, p);
+  }
   return hipGetLastError();
 }
 
