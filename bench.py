@@ -4,8 +4,9 @@
 
 A step is one pass of the whole path over one batch of seeded synthetic
 input, all of it already resident in HBM:
-  copy-on-write block copies (workloads that have any) -> slot mapping ->
-  cache write of the step's new K/V -> decode attention over every sequence.
+  copy-on-write block copies (workloads that have any) -> slot mapping and
+  cache write of the step's new K/V (one fused launch) -> decode attention
+  over every sequence (or causal attention of each sequence's new tokens).
 W untimed steps, then exactly K timed steps between two device
 synchronisations. HIP events on the launch stream bracket each decode call
 inside the timed region, so the decode kernel's average duration (and from it
@@ -190,6 +191,9 @@ def main():
                     help="skip the oracle timing (e.g. under a counter profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-controls", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once as a HIP graph and replayed; the "
+                         "replayed step then sets value and ms_per_step")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -249,19 +253,23 @@ def main():
         dst = torch.from_numpy(tb.pairs[:, 1].astype(np.int64)).to(dev)
         k_saved, v_saved = k_cache[dst].clone(), v_cache[dst].clone()
 
+    def attend(tables, dest, shared):
+        if spec.chunk:
+            pa.multi_query(q, k_cache, v_cache, tables, cl, qs, spec.scale, max_ctx, max_q,
+                           partition=partition, out=dest, workspace=workspace, shared_kv=shared)
+        else:
+            pa.decode(q, k_cache, v_cache, tables, cl, spec.scale, max_ctx, partition=partition,
+                      out=dest, workspace=workspace, shared_kv=shared)
+
     def step(ev=None):
         if len(tb.pairs):
             pa.copy_blocks(k_cache, v_cache, pairs)
-        pa.slot_mapping(bt, step_pos, seq_ids=step_seq, out=slots)
-        pa.write_kv(k_new, v_new, k_cache, v_cache, slots)
+        # slot mapping and the cache write, one launch
+        pa.append_kv(k_new, v_new, k_cache, v_cache, bt, step_pos, seq_ids=step_seq,
+                     slots_out=slots)
         if ev is not None:
             ev[0].record()
-        if spec.chunk:
-            pa.multi_query(q, k_cache, v_cache, bt, cl, qs, spec.scale, max_ctx, max_q,
-                           partition=partition, out=out, workspace=workspace, shared_kv=shared_kv)
-        else:
-            pa.decode(q, k_cache, v_cache, bt, cl, spec.scale, max_ctx, partition=partition,
-                      out=out, workspace=workspace, shared_kv=shared_kv)
+        attend(bt, out, shared_kv)
         if ev is not None:
             ev[1].record()
 
@@ -280,9 +288,50 @@ def main():
     dec_ms = [a.elapsed_time(b) for a, b in evs]
     ms_step = wall * 1e3 / args.steps
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
-    dec_med_ms = sorted(dec_ms)[len(dec_ms) // 2]
+    dec_sorted = sorted(dec_ms)
+    dec_med_ms = dec_sorted[len(dec_ms) // 2]
+    dec_p10_ms = dec_sorted[len(dec_ms) // 10]
+    dec_p90_ms = dec_sorted[min(len(dec_ms) - 1, (9 * len(dec_ms)) // 10)]
     log(f"[bench] step {ms_step * 1e3:.1f} us, decode avg {dec_avg_ms * 1e3:.1f} us "
         f"(median {dec_med_ms * 1e3:.1f})")
+
+    graph = None
+    if args.graph:
+        # The same launches captured once and replayed: no host launch latency
+        # between the step's kernels. Every replay must reproduce the eager
+        # step's output bits: the kernels are deterministic, and a repeated
+        # step leaves every slot the attention reads as the first step left
+        # it (a repeated copy-on-write step may change slots past contexts).
+        eager_out = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        match = True
+        for _ in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            match = match and torch.equal(out, eager_out)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] timing {args.steps} graph replays")
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / args.steps
+        match = match and torch.equal(out, eager_out)
+        graph = dict(ms_per_step=round(gms, 5), eager_ms_per_step=round(ms_step, 5),
+                     replays_match_eager=bool(match))
+        log(f"[bench] graph step {gms * 1e3:.1f} us (eager {ms_step * 1e3:.1f} us), "
+            f"replays match eager: {match}")
+        if not match:
+            print("bench.py: graph replays differ from the eager step", file=sys.stderr)
+            sys.exit(1)
+        ms_step = gms
+        del g
 
     controls = {}
     if not args.no_controls:
@@ -305,6 +354,30 @@ def main():
         controls["d2d_copy"] = dict(bytes_read=n, bytes_written=n, us=round(cms * 1e3, 2),
                                     GBps=round(2 * n / (cms * 1e-3) / 1e9, 1))
         del a, b
+        # The same attention over sequentially placed blocks (sequence s holds
+        # blocks base_s, base_s + 1, ...): what the block-table indirection and
+        # scattered placement cost against a contiguous cache. The pool's
+        # contents are whatever it holds; only the time is used.
+        nblk = -(-tb.context_lens.astype(np.int64) // 16)
+        if int(nblk.sum()) <= tb.NB:
+            seq_bt = np.full_like(tb.block_tables, -1)
+            base = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+            for s_i, (b0, nb_i) in enumerate(zip(base, nblk)):
+                seq_bt[s_i, :nb_i] = np.arange(b0, b0 + nb_i, dtype=np.int32)
+            seq_bt_d = torch.from_numpy(seq_bt).to(dev)
+            scratch_out = torch.empty_like(out)
+            for _ in range(3):
+                attend(seq_bt_d, scratch_out, False)
+            e0.record()
+            for _ in range(reps):
+                attend(seq_bt_d, scratch_out, False)
+            e1.record()
+            torch.cuda.synchronize()
+            ims = e0.elapsed_time(e1) / reps
+            controls["sequential_tables"] = dict(
+                us=round(ims * 1e3, 2), GBps=round(nbytes["decode"] / (ims * 1e-3) / 1e9, 1),
+                paged_over_sequential=round(dec_avg_ms / ims, 4))
+            del scratch_out, seq_bt_d
 
     if len(tb.pairs):
         k_cache[dst], v_cache[dst] = k_saved, v_saved
@@ -362,6 +435,7 @@ def main():
         "attention_TFLOPs": round(nbytes["flops"] / (dec_avg_ms * 1e-3) / 1e12, 2),
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_median": round(dec_med_ms * 1e3, 2),
+        "decode_us_p10_p90": [round(dec_p10_ms * 1e3, 2), round(dec_p90_ms * 1e3, 2)],
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
@@ -371,6 +445,7 @@ def main():
         "cpu_baseline": cpu,
         "parity_max_abs_err_vs_oracle": parity,
         "controls": controls,
+        "graph": graph,
     }
     if shared_kv:
         # blocks shared by several sequences: K/V bytes of each block counted once

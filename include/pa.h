@@ -122,6 +122,31 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache,
                       pa_dtype dt, hipStream_t stream);
 
 /*
+ * pa_append_kv — pa_slot_mapping and pa_write_kv in one launch.
+ *
+ * [P1] section 2: each new token's slot comes from its sequence's block table
+ * (block_tables[s][p / bs] * bs + p % bs, as in pa_slot_mapping), and its K
+ * and V rows are written there (as in pa_write_kv). The effect on the pools,
+ * and on slot_mapping when it is given, is exactly that of the two calls in a
+ * row; one kernel replaces two dependent launches on the decode step.
+ *
+ *   k_new, v_new     [T][Hkv][D]
+ *   k_cache, v_cache [NB][Hkv][bs][D], modified in place
+ *   slot_mapping     out, int32 [T], or NULL when the caller does not need it
+ *   block_tables     int32 [B][MB]; entries may be -1 (unused)
+ *   seq_ids          int32 [T], or NULL for seq_ids[i] = i (then T must be <= B)
+ *   positions        int32 [T]
+ * Tokens whose slot is -1 (see pa_slot_mapping) or at or past NB * bs are not
+ * written. Slots must be distinct within one call. T == 0 is a no-op.
+ */
+pa_status pa_append_kv(const void* k_new, const void* v_new, void* k_cache,
+                       void* v_cache, int32_t* slot_mapping,
+                       const int32_t* block_tables, const int32_t* seq_ids,
+                       const int32_t* positions, int32_t T, int32_t B, int32_t MB,
+                       int32_t NB, int32_t Hkv, int32_t D, int32_t bs, pa_dtype dt,
+                       hipStream_t stream);
+
+/*
  * pa_copy_blocks — copy-on-write block copies.
  *
  * [P1] section 3: branches of one request share the physical prompt blocks;

@@ -24,7 +24,7 @@ import torch
 
 from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PA_KV_SHARED, PAError, check, lib  # noqa: F401
 
-__all__ = ["slot_mapping", "write_kv", "copy_blocks", "decode", "multi_query", "shares_blocks",
+__all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "decode", "multi_query", "shares_blocks",
            "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError"]
 
@@ -106,6 +106,43 @@ def write_kv(k_new, v_new, k_cache, v_cache, slot_mapping):
         check(lib().pa_write_kv(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
                                 v_cache.data_ptr(), slot_mapping.data_ptr(), T, NB, Hkv, D, bs,
                                 _dt(k_cache), _stream(dev)), "pa_write_kv")
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, block_tables, positions, seq_ids=None,
+              slots_out=None):
+    """slot_mapping + write_kv in one launch. Returns slots_out (None if not given)."""
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _i32(block_tables, "block_tables")
+    _i32(positions, "positions")
+    B, MB = block_tables.shape
+    T = positions.shape[0]
+    ts = [k_new, v_new, k_cache, v_cache, block_tables, positions]
+    if seq_ids is not None:
+        _i32(seq_ids, "seq_ids")
+        if seq_ids.shape != (T,):
+            raise ValueError("seq_ids must match positions")
+        ts.append(seq_ids)
+    elif T > B:
+        raise ValueError("without seq_ids there is one position per sequence")
+    if slots_out is not None:
+        _i32(slots_out, "slots_out")
+        if slots_out.shape != (T,):
+            raise ValueError("slots_out must be [T]")
+        ts.append(slots_out)
+    if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D):
+        raise ValueError("k_new / v_new must be [T, Hkv, D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("new rows and pools must share a dtype")
+    dev = _dev(*ts)
+    with torch.cuda.device(dev):
+        check(lib().pa_append_kv(k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                                 v_cache.data_ptr(),
+                                 slots_out.data_ptr() if slots_out is not None else None,
+                                 block_tables.data_ptr(),
+                                 seq_ids.data_ptr() if seq_ids is not None else None,
+                                 positions.data_ptr(), T, B, MB, NB, Hkv, D, bs, _dt(k_cache),
+                                 _stream(dev)), "pa_append_kv")
+    return slots_out
 
 
 def copy_blocks(k_cache, v_cache, pairs):

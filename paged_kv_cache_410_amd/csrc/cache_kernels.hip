@@ -11,12 +11,10 @@
 namespace pa {
 
 // slot = table[seq][p / 16] * 16 + p % 16, or -1 when there is no valid slot.
-__global__ void slot_mapping_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ bt,
-                                    const int32_t* __restrict__ seq_ids,
-                                    const int32_t* __restrict__ pos, int32_t T, int32_t B,
-                                    int32_t MB) {
-  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T) return;
+__device__ __forceinline__ int32_t slot_of(const int32_t* __restrict__ bt,
+                                           const int32_t* __restrict__ seq_ids,
+                                           const int32_t* __restrict__ pos, int32_t i, int32_t B,
+                                           int32_t MB) {
   const int32_t s = seq_ids ? seq_ids[i] : i;
   const int32_t p = pos[i];
   int32_t slot = -1;
@@ -24,11 +22,27 @@ __global__ void slot_mapping_kernel(int32_t* __restrict__ out, const int32_t* __
     const int32_t b = bt[(size_t)s * MB + p / kBlock];
     if (b >= 0) slot = b * kBlock + p % kBlock;
   }
-  out[i] = slot;
+  return slot;
+}
+
+__global__ void slot_mapping_kernel(int32_t* __restrict__ out, const int32_t* __restrict__ bt,
+                                    const int32_t* __restrict__ seq_ids,
+                                    const int32_t* __restrict__ pos, int32_t T, int32_t B,
+                                    int32_t MB) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T) return;
+  out[i] = slot_of(bt, seq_ids, pos, i, B, MB);
+}
+
+// Pool index of 16-byte chunk c of head g's row in slot `slot`.
+__device__ __forceinline__ int64_t pool_chunk(int32_t slot, int32_t g, int32_t c, int32_t Hkv,
+                                              int32_t chunks_per_row) {
+  return (((int64_t)(slot / kBlock) * Hkv + g) * kBlock + slot % kBlock) * chunks_per_row + c;
 }
 
 // One thread per 16-byte chunk of a (token, kv head) row; K and V together.
-// Source row (t, g) -> pool row (slot / 16, g, slot % 16).
+// Source row (t, g) -> pool row (slot / 16, g, slot % 16). The source chunks
+// are read before the slot is known, so both loads are in flight together.
 __global__ void write_kv_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
                                 uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
                                 const int32_t* __restrict__ slots, int32_t T, int32_t Hkv,
@@ -36,15 +50,44 @@ __global__ void write_kv_kernel(const uint4* __restrict__ k_new, const uint4* __
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)T * Hkv * chunks_per_row;
   if (i >= total) return;
+  const uint4 kx = k_new[i];
+  const uint4 vx = v_new[i];
   const int32_t c = (int32_t)(i % chunks_per_row);
   const int64_t row = i / chunks_per_row;
   const int32_t g = (int32_t)(row % Hkv);
   const int32_t t = (int32_t)(row / Hkv);
   const int32_t slot = slots[t];
   if (slot < 0 || slot >= n_slots) return;
-  const int64_t dst = (((int64_t)(slot / kBlock) * Hkv + g) * kBlock + slot % kBlock) * chunks_per_row + c;
-  k_cache[dst] = k_new[i];
-  v_cache[dst] = v_new[i];
+  const int64_t dst = pool_chunk(slot, g, c, Hkv, chunks_per_row);
+  k_cache[dst] = kx;
+  v_cache[dst] = vx;
+}
+
+// Slot mapping and cache write in one pass: each thread derives its token's
+// slot from the block table itself, then stores its chunk; the thread of
+// chunk 0, head 0 also records the slot when `slots_out` is given. The result
+// equals slot_mapping_kernel followed by write_kv_kernel.
+__global__ void append_kv_kernel(const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+                                 uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                 int32_t* __restrict__ slots_out, const int32_t* __restrict__ bt,
+                                 const int32_t* __restrict__ seq_ids,
+                                 const int32_t* __restrict__ pos, int32_t T, int32_t B, int32_t MB,
+                                 int32_t Hkv, int32_t chunks_per_row, int64_t n_slots) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)T * Hkv * chunks_per_row;
+  if (i >= total) return;
+  const uint4 kx = k_new[i];
+  const uint4 vx = v_new[i];
+  const int32_t c = (int32_t)(i % chunks_per_row);
+  const int64_t row = i / chunks_per_row;
+  const int32_t g = (int32_t)(row % Hkv);
+  const int32_t t = (int32_t)(row / Hkv);
+  const int32_t slot = slot_of(bt, seq_ids, pos, t, B, MB);
+  if (slots_out && g == 0 && c == 0) slots_out[t] = slot;
+  if (slot < 0 || slot >= n_slots) return;
+  const int64_t dst = pool_chunk(slot, g, c, Hkv, chunks_per_row);
+  k_cache[dst] = kx;
+  v_cache[dst] = vx;
 }
 
 // grid.y = pair, grid.z = 0 (K) / 1 (V); grid.x strides over the block's chunks.
@@ -89,6 +132,20 @@ hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, 
   hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      (const uint4*)k_new, (const uint4*)v_new, (uint4*)k_cache, (uint4*)v_cache,
                      slots, T, Hkv, chunks, (int64_t)NB * kBlock);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            int32_t* slots_out, const int32_t* bt, const int32_t* seq_ids,
+                            const int32_t* pos, int32_t T, int32_t B, int32_t MB, int32_t NB,
+                            int32_t Hkv, int32_t row_bytes, hipStream_t stream) {
+  const int32_t chunks = row_bytes / 16;
+  const int64_t total = (int64_t)T * Hkv * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     (const uint4*)k_new, (const uint4*)v_new, (uint4*)k_cache, (uint4*)v_cache,
+                     slots_out, bt, seq_ids, pos, T, B, MB, Hkv, chunks, (int64_t)NB * kBlock);
   return hipGetLastError();
 }
 

@@ -78,6 +78,26 @@ pa_status pa_write_kv(const void* k_new, const void* v_new, void* k_cache, void*
              : PA_EHIP;
 }
 
+pa_status pa_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       int32_t* slot_mapping, const int32_t* block_tables, const int32_t* seq_ids,
+                       const int32_t* positions, int32_t T, int32_t B, int32_t MB, int32_t NB,
+                       int32_t Hkv, int32_t D, int32_t bs, pa_dtype dt, hipStream_t stream) {
+  if (T < 0 || B < 0 || MB < 0 || NB < 0 || Hkv <= 0 || D <= 0 || !dtype_ok(dt)) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (D != 64 && D != 128) return PA_EUNSUPPORTED;
+  if (!seq_ids && T > B) return PA_EINVAL;
+  if (T == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !positions) return PA_EINVAL;
+  if (B > 0 && MB > 0 && !block_tables) return PA_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  if ((int64_t)T * Hkv * D * elem_bytes(dt) / 16 > (int64_t)INT32_MAX * 256) return PA_EUNSUPPORTED;
+  return pa::launch_append_kv(k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, seq_ids,
+                              positions, T, B, MB, NB, Hkv, D * elem_bytes(dt), stream) == hipSuccess
+             ? PA_OK
+             : PA_EHIP;
+}
+
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n, int32_t NB,
                          int32_t Hkv, int32_t D, int32_t bs, pa_dtype dt, hipStream_t stream) {
   if (n < 0 || NB < 0 || Hkv <= 0 || D <= 0 || !dtype_ok(dt)) return PA_EINVAL;

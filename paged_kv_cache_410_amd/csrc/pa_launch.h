@@ -64,6 +64,10 @@ hipError_t launch_slot_mapping(int32_t* out, const int32_t* bt, const int32_t* s
 hipError_t launch_write_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                            const int32_t* slots, int32_t T, int32_t NB, int32_t Hkv,
                            int32_t row_bytes, hipStream_t stream);
+hipError_t launch_append_kv(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            int32_t* slots_out, const int32_t* bt, const int32_t* seq_ids,
+                            const int32_t* pos, int32_t T, int32_t B, int32_t MB, int32_t NB,
+                            int32_t Hkv, int32_t row_bytes, hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n,
                               int32_t NB, size_t block_bytes, hipStream_t stream);
 

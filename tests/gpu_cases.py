@@ -115,10 +115,19 @@ class Step:
                              oracle_view(self.v_after), self.tb.block_tables,
                              self.tb.context_lens, self.spec.scale, pairs=pairs)
 
-    def run_cache_ops(self, pa):
-        """copy_blocks -> slot_mapping -> write_kv on the GPU; returns the slots."""
+    def run_cache_ops(self, pa, fused=False, want_slots=True):
+        """copy_blocks -> slot_mapping -> write_kv on the GPU (fused: copy_blocks ->
+        append_kv); returns the slots (None when fused and not wanted)."""
         if len(self.tb.pairs):
             pa.copy_blocks(self.k_cache, self.v_cache, self.pairs)
+        if fused:
+            slots = None
+            if want_slots:
+                slots = torch.full((self.step_pos.shape[0],), -7, dtype=torch.int32,
+                                   device=self.step_pos.device)
+            pa.append_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, self.block_tables,
+                         self.step_pos, seq_ids=self.step_seq, slots_out=slots)
+            return slots
         slots = pa.slot_mapping(self.block_tables, self.step_pos, seq_ids=self.step_seq)
         pa.write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, slots)
         return slots

@@ -146,6 +146,18 @@ def test_cache_ops_reject_bad_arguments(palib):
     assert lib.pa_slot_mapping(FAKE, FAKE, None, FAKE, 2, 2, 4, 32, None) == -2
     assert lib.pa_slot_mapping(FAKE, FAKE, None, FAKE, 3, 2, 4, 16, None) == -1   # T > B
     assert lib.pa_slot_mapping(None, None, None, None, 0, 4, 4, 16, None) == 0
+    # pa_append_kv(k_new, v_new, k, v, slots_out, bt, seq_ids, pos, T, B, MB, NB, Hkv, D, bs,
+    #              dt, stream)
+    ok = (FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE)
+    assert lib.pa_append_kv(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, 3, 4, 8, 10, 2, 128,
+                            16, 1, None) == -1                                     # no positions
+    assert lib.pa_append_kv(*ok, 5, 4, 8, 10, 2, 128, 16, 1, None) == -1           # T > B
+    assert lib.pa_append_kv(*ok, 3, 4, 8, 10, 2, 100, 16, 1, None) == -2           # D
+    assert lib.pa_append_kv(*ok, 3, 4, 8, 10, 2, 128, 8, 1, None) == -2            # bs
+    assert lib.pa_append_kv(FAKE + 4, *ok[1:], 3, 4, 8, 10, 2, 128, 16, 1, None) == -1
+    assert lib.pa_append_kv(*ok, 3, 4, 8, 10, 2, 128, 16, 7, None) == -1           # dtype
+    assert lib.pa_append_kv(None, None, None, None, None, None, None, None, 0, 4, 8, 10, 2, 128,
+                            16, 1, None) == 0
 
 
 # ------------------------------------------------------- native block manager

@@ -50,7 +50,7 @@ def test_full_config(pa, name):
     part = bench_partition(pa, spec, st.q.shape[0], st.max_ctx)
     say(f"[full config] {name}: NB={st.tb.NB} MB={st.tb.MB} T={len(st.tb.slots)} "
         f"pairs={len(st.tb.pairs)} partition={part}")
-    slots = st.run_cache_ops(pa)
+    slots = st.run_cache_ops(pa, fused=True)     # the launches bench.py times
     out = st.multi(pa, partition=part) if spec.chunk else st.decode(pa, partition=part)
     torch.cuda.synchronize()
     assert np.array_equal(slots.cpu().numpy(), st.tb.slots)

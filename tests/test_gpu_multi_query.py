@@ -94,3 +94,15 @@ def test_bad_row_counts_poison_only_their_rows(pa):
     keep = torch.ones(out.shape[0], dtype=torch.bool)
     keep[qs[1]:qs[2]] = False
     assert torch.allclose(out[keep], good[keep], atol=1e-2)
+
+
+@pytest.mark.parametrize("name", list(CHUNKS))
+def test_chunk_append_kv_bit_exact(pa, name):
+    # several tokens per sequence through the fused slot-mapping + write
+    say(f"[chunk append_kv] {name}")
+    st = Step(CHUNKS[name], oracle_full=False)
+    slots = st.run_cache_ops(pa, fused=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), st.tb.slots)
+    assert np.array_equal(host_bits(st.k_cache), st.k_after)
+    assert np.array_equal(host_bits(st.v_cache), st.v_after)

@@ -56,14 +56,53 @@ SMALL = {
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-def test_cache_ops_bit_exact(pa, name):
-    say(f"[cache ops] {name}")
+@pytest.mark.parametrize("fused", [False, True])
+def test_cache_ops_bit_exact(pa, name, fused):
+    say(f"[cache ops] {name} fused={fused}")
     st = Step(SMALL[name], oracle_full=False)
-    slots = st.run_cache_ops(pa)
+    slots = st.run_cache_ops(pa, fused=fused)
     torch.cuda.synchronize()
     assert np.array_equal(slots.cpu().numpy(), st.tb.slots)
     assert np.array_equal(host_bits(st.k_cache), st.k_after)
     assert np.array_equal(host_bits(st.v_cache), st.v_after)
+
+
+def test_append_kv_without_slot_output(pa):
+    say("[append_kv] no slot output")
+    st = Step(SMALL["cow_gqa"], oracle_full=False)
+    assert st.run_cache_ops(pa, fused=True, want_slots=False) is None
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(st.k_cache), st.k_after)
+    assert np.array_equal(host_bits(st.v_cache), st.v_after)
+
+
+def test_append_kv_edge_cases(pa):
+    # positions and tables that give no slot (-1) or a slot past the pool: the
+    # slot output matches pa_slot_mapping, and nothing is written for them
+    say("[append_kv] edges")
+    NB, Hkv, D = 6, 2, 64
+    bt = torch.tensor([[5, -1, 7], [2, 3, 4]], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0, 17, 47, 48, -1, 33, 20, 40], dtype=torch.int32, device="cuda")
+    seq = torch.tensor([0, 0, 1, 1, 1, 2, 1, 0], dtype=torch.int32, device="cuda")
+    T = pos.shape[0]
+    gen = torch.Generator().manual_seed(5)
+    k_new = torch.randn(T, Hkv, D, generator=gen).to("cuda")
+    v_new = torch.randn(T, Hkv, D, generator=gen).to("cuda")
+    k = torch.zeros(NB, Hkv, 16, D, device="cuda")
+    v = torch.zeros_like(k)
+    slots = torch.empty(T, dtype=torch.int32, device="cuda")
+    pa.append_kv(k_new, v_new, k, v, bt, pos, seq_ids=seq, slots_out=slots)
+    # sequence 0, position 40 -> table entry 7 -> slot 120, past the 6-block
+    # pool (96 slots): reported, not written
+    expect = [80, -1, 4 * 16 + 15, -1, -1, -1, 3 * 16 + 4, 7 * 16 + 8]
+    assert slots.cpu().tolist() == expect
+    k_h, v_h = k.cpu(), v.cpu()
+    kk, vv = torch.zeros_like(k_h), torch.zeros_like(v_h)
+    for t, sl in enumerate(expect):
+        if 0 <= sl < NB * 16:
+            kk[sl // 16, :, sl % 16] = k_new[t].cpu()
+            vv[sl // 16, :, sl % 16] = v_new[t].cpu()
+    assert torch.equal(k_h, kk) and torch.equal(v_h, vv)
 
 
 def test_copy_blocks_alone_bit_exact(pa):
@@ -197,3 +236,58 @@ def test_slot_mapping_edge_cases(pa):
     seq = torch.tensor([0, 0, 1, 1, 1, 2], dtype=torch.int32, device="cuda")
     got = pa.slot_mapping(bt, pos, seq_ids=seq).cpu().tolist()
     assert got == [80, -1, 4 * 16 + 15, -1, -1, -1]
+
+
+@pytest.mark.parametrize("name,partition", [("gqa8", 64), ("mha_bf16", 0), ("cow_small", 128)])
+def test_step_graph_replays_match_eager(pa, name, partition):
+    # The step (copies, fused slot mapping + write, attention with its merge)
+    # captured once as a HIP graph. Each replay starts from the pools the
+    # first step saw (restored by eager copies between replays) and must give
+    # the eager step's output bits, slots and pools. A repeated copy-on-write
+    # step would not reproduce the pools: the last sharer writes into the
+    # shared block, and the next copy carries its tail into the other copies,
+    # in slots past their contexts.
+    say(f"[graph replay] {name} partition={partition}")
+    st = Step(SMALL[name], oracle_full=False)
+    rows = st.q.shape[0]
+    ws = torch.empty(max(1, pa.decode_workspace_bytes(rows, st.spec.Hq, st.spec.D, st.max_ctx,
+                                                      partition)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(st.q)
+    slots = torch.empty(st.step_pos.shape[0], dtype=torch.int32, device="cuda")
+    shared = pa.shares_blocks(st.tb.block_tables)
+    k0, v0 = st.k_cache.clone(), st.v_cache.clone()
+
+    def step():
+        if len(st.tb.pairs):
+            pa.copy_blocks(st.k_cache, st.v_cache, st.pairs)
+        pa.append_kv(st.k_new, st.v_new, st.k_cache, st.v_cache, st.block_tables, st.step_pos,
+                     seq_ids=st.step_seq, slots_out=slots)
+        pa.decode(st.q, st.k_cache, st.v_cache, st.block_tables, st.context_lens, st.spec.scale,
+                  st.max_ctx, partition=partition, out=out, workspace=ws, shared_kv=shared)
+
+    def check(what):
+        assert np.array_equal(slots.cpu().numpy(), st.tb.slots), what
+        assert np.array_equal(host_bits(st.k_cache), st.k_after), what
+        assert np.array_equal(host_bits(st.v_cache), st.v_after), what
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    check("eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        st.k_cache.copy_(k0)
+        st.v_cache.copy_(v0)
+        out.fill_(float("nan"))
+        slots.fill_(-9)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        check(f"replay {i}")
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
