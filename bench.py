@@ -190,11 +190,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (e.g. under a counter profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-controls", action="store_true")
+    ap.add_argument("--controls", choices=["all", "copy", "none"], default="all",
+                    help="copy: only the device-to-device copy (profiled runs, where the "
+                         "sequential-table launches would mix into the attention kernel's "
+                         "statistics)")
+    ap.add_argument("--no-controls", action="store_true", help="same as --controls none")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed; the "
                          "replayed step then sets value and ms_per_step")
     args = ap.parse_args()
+    if args.no_controls:
+        args.controls = "none"
 
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
@@ -334,7 +340,7 @@ def main():
         del g
 
     controls = {}
-    if not args.no_controls:
+    if args.controls != "none":
         # A plain device-to-device copy of the decode's K/V byte count: the
         # bandwidth a streaming kernel reaches here (and the reference the HBM
         # counters are scaled by).
@@ -359,7 +365,7 @@ def main():
         # scattered placement cost against a contiguous cache. The pool's
         # contents are whatever it holds; only the time is used.
         nblk = -(-tb.context_lens.astype(np.int64) // 16)
-        if int(nblk.sum()) <= tb.NB:
+        if args.controls == "all" and int(nblk.sum()) <= tb.NB:
             seq_bt = np.full_like(tb.block_tables, -1)
             base = np.concatenate([[0], np.cumsum(nblk)[:-1]])
             for s_i, (b0, nb_i) in enumerate(zip(base, nblk)):

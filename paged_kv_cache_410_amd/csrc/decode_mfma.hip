@@ -51,29 +51,26 @@
 #ifndef PA_MFMA_COL_WAVES
 #define PA_MFMA_COL_WAVES 8
 #endif
+#ifndef PA_MFMA_COL_SWIZZLE
+#define PA_MFMA_COL_SWIZZLE 2
+#endif
 #ifndef PA_MFMA_COL_DEPTH
 #define PA_MFMA_COL_DEPTH 2
+#endif
+// Column-wave mode: K tiles written straight into LDS by the load
+// (buffer_load ... lds) instead of through registers and an LDS store.
+#ifndef PA_MFMA_COL_K_LDS
+#define PA_MFMA_COL_K_LDS 1
 #endif
 // Minimum waves per SIMD the register allocation must allow.
 #ifndef PA_MFMA_MIN_WAVES
 #define PA_MFMA_MIN_WAVES 3
 #endif
+#ifndef PA_MFMA_COL_MIN_WAVES
+#define PA_MFMA_COL_MIN_WAVES 4
+#endif
 
 namespace pa {
-
-namespace {
-
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);  // (x.lo, y.lo)
-}
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);  // (x.hi, y.hi)
-}
-__device__ __forceinline__ uint32_t word(const uint4& u, int k) {
-  return k == 0 ? u.x : k == 1 ? u.y : k == 2 ? u.z : u.w;
-}
-
-}  // namespace
 
 // kColWaves (a kv head with more than one 16-column tile: several query rows
 // per sequence): the workgroup's waves take NW consecutive column tiles and
@@ -83,8 +80,14 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int k) {
 // state and writes them itself. Otherwise the waves interleave the blocks of
 // one tile and merge through LDS.
 template <int NW, int DEPTH, TilePolicy kPolicy, bool kColWaves>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES)))
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
+    kColWaves && PA_MFMA_COL_K_LDS ? PA_MFMA_COL_MIN_WAVES : PA_MFMA_MIN_WAVES)))
 void decode_mfma_kernel(DecodeParams P) {
+  // K straight into LDS: one 4 KiB stage per ring slot and wave, each slot its
+  // own LDS object so that the compiler's load counting tells them apart and
+  // waits only for the slot being read.
+  constexpr bool kDma = kColWaves && PA_MFMA_COL_K_LDS;
+  static_assert(!kDma || DEPTH == 2, "the LDS ring has two slots");
   constexpr int D = 128;
   constexpr int kRowBytes = D * 2;
   constexpr int kPad = 4;  // LDS row padding (floats) against bank conflicts
@@ -96,9 +99,16 @@ void decode_mfma_kernel(DecodeParams P) {
   const int col = lane & 15;
   const int rg = lane >> 4;
 
-  const GridPos gp = grid_pos();
-  const int p = gp.y;
   const int groups = kColWaves ? (P.n_tiles + NW - 1) / NW : P.n_tiles;  // per kv head
+  // Column-wave workgroups of one (sequence, kv head, partition) stream the
+  // same K/V: keep them on one XCD (PA_MFMA_COL_SWIZZLE 2), or give each XCD
+  // a contiguous range of the grid (1).
+  GridPos gp;
+  if constexpr (kColWaves && PA_MFMA_COL_SWIZZLE == 2)
+    gp = grid_pos_grouped(groups);
+  else
+    gp = grid_pos<(kColWaves && PA_MFMA_COL_SWIZZLE == 1) || PA_XCD_SWIZZLE>();
+  const int p = gp.y;
   const int g = gp.x / groups;        // kv head
   // 16-column tile of this kv head's (row, head) pairs
   const int tile = kColWaves ? (gp.x % groups) * NW + w : gp.x % P.n_tiles;
@@ -137,8 +147,11 @@ void decode_mfma_kernel(DecodeParams P) {
   // region holds the wave's merge rows (16 columns x D floats, padded). The
   // wave overwrites its stage only after its last read of it, and a wave's
   // LDS accesses complete in order, so no barrier guards either use.
-  __shared__ float sm_o[NW][16][D + kPad];
-  char* const stage = reinterpret_cast<char*>(&sm_o[w][0][0]);
+  __shared__ float sm_o[kDma ? 1 : NW][16][D + kPad];
+  __shared__ __attribute__((aligned(16))) char sk0[kDma ? NW : 1][kBlock * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char sk1[kDma ? NW : 1][kBlock * kRowBytes];
+  char* const stage = reinterpret_cast<char*>(&sm_o[kDma ? 0 : w][0][0]);
+  auto kslot = [&](int d) -> char* { return d == 0 ? &sk0[kDma ? w : 0][0] : &sk1[kDma ? w : 0][0]; };
   {
     const char* qp = reinterpret_cast<const char*>(P.q) + ((size_t)qrow * P.Hq + qh) * kRowBytes;
 #pragma unroll
@@ -176,7 +189,19 @@ void decode_mfma_kernel(DecodeParams P) {
   // Issue the loads of physical block b's tile (logical block blk) into
   // (kb, vb). An id outside the pool marks the group bad and loads nothing;
   // so does a block that does not exist (an empty ring refill).
-  auto load = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, int blk, bool exists) {
+  // LDS image of a K tile (kDma): row r at r * 256 bytes, its 16-byte chunk c
+  // in slot c ^ r. Load j brings rows 4 j + rg: each group of 16 lanes still
+  // reads one whole 256-byte row (chunk col ^ row), and the operand reads
+  // below (chunk 4 kk + rg of row col, slot (4 kk + rg) ^ col) spread a
+  // 16-lane group over all 16 slots of the bank width: no conflicts.
+  int dma_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + rg;
+    dma_off[j] = r * kRowBytes + ((col ^ r) & 15) * 16;
+  }
+
+  auto load = [&](int d, uint4 (&kb)[4], uint4 (&vb)[4], int b, int blk, bool exists) {
     const bool valid = b >= 0 && b < P.NB;
     bad |= exists && !valid;
     const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
@@ -185,27 +210,48 @@ void decode_mfma_kernel(DecodeParams P) {
     const int bytes = exists && valid ? rows * kRowBytes : 0;
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
+    if constexpr (kDma) {
+      // The slot's previous tile was read (and its reads waited for) by the
+      // previous step's MFMAs: keep this refill after them.
+      asm volatile("" ::: "memory");
+      char* dst = kslot(d);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kb[j] = ld16<kPolicy>(rk, row_lane + j * kRowBytes);
+      for (int j = 0; j < 4; ++j) ld16_lds<kPolicy>(rk, dst + j * 4 * kRowBytes, dma_off[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kb[j] = ld16<kPolicy>(rk, row_lane + j * kRowBytes);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) vb[j] = ld16<kPolicy>(rv, row_lane + j * kRowBytes);
   };
 
-  auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
+  auto consume = [&](int d, const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
     // Transpose K through the wave's LDS stage into the A operand layout:
     // step kk needs, in lane (rg, col), dims 32 kk + 8 rg .. + 7 (chunk
     // 4 kk + rg) of row t = col. Rows are kStageRow apart (256 B + 16 B of
     // padding), so both the row writes and the strided reads are free of
     // bank conflicts.
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(stage + (4 * rg + j) * kStageRow + col * 16) = kb[j];
     f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (kDma) {
+      const char* src = kslot(d);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint4 ka = *reinterpret_cast<const uint4*>(stage + col * kStageRow + (4 * kk + rg) * 16);
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
-                                                  0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(
+            src + col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
+                                                    0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(stage + (4 * rg + j) * kStageRow + col * 16) = kb[j];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint4 ka =
+            *reinterpret_cast<const uint4*>(stage + col * kStageRow + (4 * kk + rg) * 16);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk],
+                                                    st, 0, 0, 0);
+      }
     }
     const int tok0 = blk * kBlock + 4 * rg;
     // Some column masks some row of this block (wave-uniform).
@@ -256,9 +302,9 @@ void decode_mfma_kernel(DecodeParams P) {
     block_pipeline<DEPTH>(
         bt_row, first, kStride, nk, lane, ids0,
         [&](int d, int b, int k, bool exists) {
-          load(kb[d], vb[d], b, first + k * kStride, exists);
+          load(d, kb[d], vb[d], b, first + k * kStride, exists);
         },
-        [&](int d, int k) { consume(kb[d], vb[d], first + k * kStride); });
+        [&](int d, int k) { consume(d, kb[d], vb[d], first + k * kStride); });
   }
 
   lsum = rows_sum(lsum);  // per column: sum over the 4 row groups
@@ -385,6 +431,10 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int NW = PA_MFMA_WAVES;
   constexpr int DEPTH = PA_MFMA_DEPTH;
   const dim3 block(NW * kWave);
+#ifndef PA_CHUNK_KERNEL
+#define PA_CHUNK_KERNEL 1
+#endif
+  if (PA_CHUNK_KERNEL && p.n_tiles > 1) return launch_chunk_mfma(p, stream);
   if (p.n_tiles > 1) {
     // waves of a workgroup share each block: read through the caches
     constexpr int CW = PA_MFMA_COL_WAVES;

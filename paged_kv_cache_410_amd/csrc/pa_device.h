@@ -26,6 +26,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// 16-bit halves of two words: (x.lo, y.lo) and (x.hi, y.hi).
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t x, uint32_t y) {
+  return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+__device__ __forceinline__ uint32_t word(const uint4& u, int k) {
+  return k == 0 ? u.x : k == 1 ? u.y : k == 2 ? u.z : u.w;
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -122,9 +133,12 @@ __device__ __forceinline__ int wave_id() {
 
 // ------------------------------------------------------- workgroup mapping
 // Workgroups of one dispatch go round-robin to the 8 XCDs (workgroup L runs on
-// XCD L % 8). With PA_XCD_SWIZZLE the grid's coordinates are taken from a
-// remapped linear id so that each XCD runs one contiguous range of work items
-// (its own sequences, all their heads) instead of every eighth one.
+// XCD L % 8), and each XCD has its own L2. With kSwizzle the grid's
+// coordinates are taken from a remapped linear id so that each XCD runs one
+// contiguous range of work items instead of every eighth one: workgroups that
+// read the same K/V (neighbours in grid order) then share one L2. Decode
+// workgroups share nothing and keep the plain order (PA_XCD_SWIZZLE=1 remaps
+// them too, for measurement).
 #ifndef PA_XCD_SWIZZLE
 #define PA_XCD_SWIZZLE 0
 #endif
@@ -132,8 +146,9 @@ constexpr int kXcds = 8;
 struct GridPos {
   int x, y, z;
 };
+template <bool kSwizzle = (PA_XCD_SWIZZLE != 0)>
 __device__ __forceinline__ GridPos grid_pos() {
-  if constexpr (PA_XCD_SWIZZLE == 0) {
+  if constexpr (!kSwizzle) {
     return {(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
   } else {
     const uint32_t X = gridDim.x, Y = gridDim.y;
@@ -143,6 +158,24 @@ __device__ __forceinline__ GridPos grid_pos() {
     const uint32_t w = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + j;
     return {(int)(w % X), (int)((w / X) % Y), (int)(w / (X * Y))};
   }
+}
+
+// Groups of S consecutive work items (in grid order) that read the same data
+// run on one XCD, and successive groups go round-robin over the XCDs: the
+// j-th workgroup dispatched to XCD k takes member j % S of group
+// k + 8 * (j / S). Items past the last whole round of 8 groups keep their
+// place. A bijection on [0, n); S must divide gridDim.x.
+__device__ __forceinline__ GridPos grid_pos_grouped(uint32_t S) {
+  const uint32_t X = gridDim.x, Y = gridDim.y;
+  const uint32_t n = X * Y * gridDim.z;
+  const uint32_t L = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+  const uint32_t round = kXcds * S;
+  uint32_t w = L;
+  if (L < n / round * round) {
+    const uint32_t k = L % kXcds, j = L / kXcds;
+    w = (k + kXcds * (j / S)) * S + j % S;
+  }
+  return {(int)(w % X), (int)((w / X) % Y), (int)(w / (X * Y))};
 }
 
 // ---------------------------------------------------------------- tile loads
@@ -166,6 +199,16 @@ template <TilePolicy kPolicy>
 __device__ __forceinline__ uint4 ld16(rsrc_t r, int off) {
   constexpr int kAux = kPolicy == TilePolicy::kStream ? 2 : 0;  // nt bit
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux));
+}
+// The same load written by the hardware straight into LDS
+// (buffer_load_dwordx4 ... lds): lane i's 16 bytes land at lds + 16 i, with
+// `lds` wave-uniform; lanes outside the resource's range write zeros. Its
+// completion is counted like a register load's (vmcnt).
+template <TilePolicy kPolicy>
+__device__ __forceinline__ void ld16_lds(rsrc_t r, void* lds, int off) {
+  constexpr int kAux = kPolicy == TilePolicy::kStream ? 2 : 0;  // nt bit
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           0, 0, kAux);
 }
 
 // Software pipeline over the blocks one wave reads: logical blocks

@@ -74,6 +74,7 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
 // dtype: 0 = fp32, 1 = bf16 (pa_dtype values)
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream);
 
 // Query-head groups of up to 16 handled by one MFMA workgroup.
