@@ -33,12 +33,16 @@
 #include "pa_device.h"
 #include "pa_launch.h"
 
-// LDS ring slots (2..4) and the register allocation's minimum waves per SIMD.
+// LDS ring slots (3 or 4) and the register allocation's minimum waves per SIMD.
 #ifndef PA_CHUNK_RING
 #define PA_CHUNK_RING 4
 #endif
 #ifndef PA_CHUNK_MIN_WAVES
 #define PA_CHUNK_MIN_WAVES 4
+#endif
+// Most waves per workgroup (2, 4 or 8).
+#ifndef PA_CHUNK_MAX_WAVES
+#define PA_CHUNK_MAX_WAVES 8
 #endif
 
 namespace pa {
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(NW >= 4 ? PA_CHUNK_MIN_WAVES : 3)))
 void chunk_mfma_kernel(DecodeParams P) {
   static_assert(kPieces % NW == 0, "pieces must divide over the waves");
-  static_assert(R >= 2 && R <= 4, "ring of 2 to 4 slots");
+  static_assert(R >= 3 && R <= 4, "ring of 3 or 4 slots");
   constexpr int kPer = kPieces / NW;  // load instructions per wave per block
   // One LDS object per slot, so that the compiler's load counting tells the
   // slots apart and waits only for the slot it reads.
@@ -123,14 +127,23 @@ void chunk_mfma_kernel(DecodeParams P) {
   const int qi = gcl / P.G;
   const int qh = g * P.G + gcl % P.G;
 
+  // The logit scale (log2 domain) is applied in the exponent, after the max
+  // is taken over the raw products, which needs it non-negative: a negative
+  // scale flips the sign bits of Q instead (exact), and a zero scale becomes
+  // a tiny positive one (every logit still rounds to 0).
+  const bool q_neg = P.qscale < 0.0f;
+  const float qs = fmaxf(fabsf(P.qscale), 1e-30f);
+
   // B operand of S^T: Q[column col][32 kk + 8 rg ..], zero for padded columns.
   bf16x8_t qop[4];
   if (has_cols) {
     const char* qp =
         reinterpret_cast<const char*>(P.q) + ((size_t)(sr.first + qi) * P.Hq + qh) * kRowBytes;
+    const uint32_t flip = q_neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 u = ld16(qp + (32 * kk + 8 * rg) * 2);
+      u = make_uint4(u.x ^ flip, u.y ^ flip, u.z ^ flip, u.w ^ flip);
       if (!col_ok) u = make_uint4(0, 0, 0, 0);
       qop[kk] = __builtin_bit_cast(bf16x8_t, u);
     }
@@ -188,7 +201,9 @@ void chunk_mfma_kernel(DecodeParams P) {
       ld16_lds<kPolicy>(piece_v[i] ? rv : rk, dst + piece_lds[i], piece_off[i]);
   };
 
-  auto consume = [&](int d, int blk) {
+  // S^T of the block in slot d: raw logits, lane (rg, col) holds tokens
+  // 4 rg + 0..3 of column col.
+  auto qk = [&](int d) -> f32x4_t {
     const char* src = slot(d);
     f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -198,30 +213,45 @@ void chunk_mfma_kernel(DecodeParams P) {
       st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
                                                   0, 0, 0);
     }
+    return st;
+  };
+
+  // Online softmax over the block's logits st, then O^T += V^T P^T with the
+  // block's V from slot d.
+  auto softmax_pv = [&](int d, const f32x4_t st, int blk) {
+    const char* src = slot(d);
     uint4 vb[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       vb[j] = *reinterpret_cast<const uint4*>(src + kTileBytes + (4 * rg + j) * kRowBytes + col * 16);
-    const int tok0 = blk * kBlock + 4 * rg;
-    const bool partial = blk * kBlock + kBlock > ctx_min;  // some column masks some row
-    float x[4];
+    // Raw logits; those past a column's causal limit are removed (only a
+    // block that reaches some column's limit needs the test: wave-uniform).
+    float x[4] = {st[0], st[1], st[2], st[3]};
+    if (blk * kBlock + kBlock > ctx_min) {
+      const int tok0 = blk * kBlock + 4 * rg;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = st[i] * P.qscale;
-      if (partial && tok0 + i >= ctx_col) x[i] = -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (tok0 + i >= ctx_col) x[i] = -INFINITY;
     }
-    const float mx = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const float mx_raw = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const float mx = mx_raw * qs;  // -inf stays -inf (qs > 0)
+    // The reference m (what the probabilities are taken relative to) moves
+    // only when a column's max passes it by more than kLazy: the
+    // probabilities then stay below 2^kLazy, the result is the same up to
+    // rounding, and the accumulators are rescaled a few times per column
+    // instead of whenever its max creeps up.
+    constexpr float kLazy = 8.0f;
     const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = exp2_fast(m - m_use);
-    // Rescale only when some column's max rose (else alpha is exactly 1).
-    const bool rescale = __builtin_amdgcn_ballot_w64(m_new > m) != 0;
+    const bool up = m_new > m + kLazy;  // from -inf: any finite max
+    const float ref = up ? m_new : m;
+    const float ref_use = (ref == -INFINITY) ? 0.0f : ref;
+    const float alpha = exp2_fast(m - ref_use);  // exactly 1 where the reference stays
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(x[i] - m_use);
+    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
     lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = m_new;
-    if (rescale) {
+    m = ref;
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     }
@@ -240,12 +270,15 @@ void chunk_mfma_kernel(DecodeParams P) {
     }
   };
 
-  // The ring: block k sits in slot k % R. Before block k is read, each wave
-  // waits for its own pieces of it (the R - 2 blocks issued after it may stay
-  // in flight), then a barrier makes every wave's pieces visible and shows
-  // that every wave is done with block k - 1, whose slot takes block
-  // k + R - 1. Block ids are read 64 at a time (lane j holds the chunk's j-th
-  // id, broadcast with readlane); the ring drains at each chunk's end.
+  // The ring: block k sits in slot k % R. Step k of a wave takes S^T of
+  // block k + 1 (independent of the softmax of block k, so the two overlap)
+  // and the softmax and PV product of block k. Before it, each wave waits
+  // for its own pieces of block k + 1 (the block issued after it may stay in
+  // flight), then a barrier makes every wave's pieces visible and shows that
+  // every wave is done with block k - 1 (its K was read at step k - 2, its V
+  // at step k - 1), whose slot takes block k + R - 1. Block ids are read 64
+  // at a time (lane j holds the chunk's j-th id, broadcast with readlane);
+  // the ring drains at each chunk's end.
   const int nk = max(0, blk_end - blk_begin);
   for (int c0 = 0; c0 < nk; c0 += kWave) {
     const int cn = min(kWave, nk - c0);
@@ -254,6 +287,10 @@ void chunk_mfma_kernel(DecodeParams P) {
 #pragma unroll
     for (int d = 0; d < R - 1; ++d)
       issue(d, __builtin_amdgcn_readlane(ids, d), blk_begin + c0 + d, d < cn);
+    wait_vmcnt<(R - 2) * kPer>();
+    ring_barrier();
+    f32x4_t s_next = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (has_cols) s_next = qk(0);
     // Steps past the chunk's last block still wait, meet and refill (with
     // empty loads): a refill under a branch costs the compiler its record of
     // which slot each load writes, and then it waits for every slot.
@@ -261,12 +298,14 @@ void chunk_mfma_kernel(DecodeParams P) {
 #pragma unroll
       for (int d = 0; d < R; ++d) {
         const int k = k0 + d;
-        wait_vmcnt<(R - 2) * kPer>();
+        wait_vmcnt<(R - 3) * kPer>();
         ring_barrier();
         const int kl = k + R - 1;
         issue((d + R - 1) % R, __builtin_amdgcn_readlane(ids, min(kl, kWave - 1)),
               blk_begin + c0 + kl, kl < cn);
-        if (has_cols && k < cn) consume(d, blk_begin + c0 + k);
+        const f32x4_t s_cur = s_next;
+        if (has_cols && k + 1 < cn) s_next = qk((d + 1) % R);
+        if (has_cols && k < cn) softmax_pv(d, s_cur, blk_begin + c0 + k);
       }
     }
   }
@@ -329,9 +368,9 @@ hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((chunk_mfma_kernel<NW, R, TilePolicy::kShared>), grid, dim3(NW * kWave), 0,
                        stream, p);
   };
-  if (p.n_tiles <= 2)
+  if (p.n_tiles <= 2 || PA_CHUNK_MAX_WAVES == 2)
     go(std::integral_constant<int, 2>{});
-  else if (p.n_tiles <= 4)
+  else if (p.n_tiles <= 4 || PA_CHUNK_MAX_WAVES == 4)
     go(std::integral_constant<int, 4>{});
   else
     go(std::integral_constant<int, 8>{});
