@@ -10,7 +10,8 @@
 // read once per 16 columns instead of once per column.
 //
 // Columns: the n x G (query row, head of the group) pairs of a sequence and
-// kv head, row-major, cut into tiles of 16; one workgroup per (tile,
+// kv head, row-major, in one tile of 16 (more columns go to the chunk kernel,
+// chunk_mfma.hip, with the same layouts); one workgroup per (kv head,
 // partition, sequence). Column (i, q) attends over its row's causal prefix
 // (ctx - n + i + 1 tokens): a per-column limit masks the logits. The decode
 // step is n = 1: the columns are the G heads.
@@ -47,47 +48,20 @@
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 2
 #endif
-// Waves (column tiles) per workgroup and ring depth when several column tiles share the blocks.
-#ifndef PA_MFMA_COL_WAVES
-#define PA_MFMA_COL_WAVES 8
-#endif
-#ifndef PA_MFMA_COL_SWIZZLE
-#define PA_MFMA_COL_SWIZZLE 2
-#endif
-#ifndef PA_MFMA_COL_DEPTH
-#define PA_MFMA_COL_DEPTH 2
-#endif
-// Column-wave mode: K tiles written straight into LDS by the load
-// (buffer_load ... lds) instead of through registers and an LDS store.
-#ifndef PA_MFMA_COL_K_LDS
-#define PA_MFMA_COL_K_LDS 1
-#endif
 // Minimum waves per SIMD the register allocation must allow.
 #ifndef PA_MFMA_MIN_WAVES
 #define PA_MFMA_MIN_WAVES 3
 #endif
-#ifndef PA_MFMA_COL_MIN_WAVES
-#define PA_MFMA_COL_MIN_WAVES 4
-#endif
 
 namespace pa {
 
-// kColWaves (a kv head with more than one 16-column tile: several query rows
-// per sequence): the workgroup's waves take NW consecutive column tiles and
-// each streams every block of the partition, in the same order at about the
-// same time, so the repeats are served by the CU's caches and a K/V tile
-// leaves HBM about once per NW tiles. A wave then holds its columns' whole
-// state and writes them itself. Otherwise the waves interleave the blocks of
-// one tile and merge through LDS.
-template <int NW, int DEPTH, TilePolicy kPolicy, bool kColWaves>
-__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(
-    kColWaves && PA_MFMA_COL_K_LDS ? PA_MFMA_COL_MIN_WAVES : PA_MFMA_MIN_WAVES)))
+// The waves of a workgroup interleave the blocks of one column tile (wave w
+// takes blocks w, w + NW, ...) and merge their states through LDS. A kv head
+// with more than one tile (several query rows per sequence) goes to the
+// chunk kernel instead, whose waves share each block.
+template <int NW, int DEPTH, TilePolicy kPolicy>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES)))
 void decode_mfma_kernel(DecodeParams P) {
-  // K straight into LDS: one 4 KiB stage per ring slot and wave, each slot its
-  // own LDS object so that the compiler's load counting tells them apart and
-  // waits only for the slot being read.
-  constexpr bool kDma = kColWaves && PA_MFMA_COL_K_LDS;
-  static_assert(!kDma || DEPTH == 2, "the LDS ring has two slots");
   constexpr int D = 128;
   constexpr int kRowBytes = D * 2;
   constexpr int kPad = 4;  // LDS row padding (floats) against bank conflicts
@@ -99,27 +73,18 @@ void decode_mfma_kernel(DecodeParams P) {
   const int col = lane & 15;
   const int rg = lane >> 4;
 
-  const int groups = kColWaves ? (P.n_tiles + NW - 1) / NW : P.n_tiles;  // per kv head
-  // Column-wave workgroups of one (sequence, kv head, partition) stream the
-  // same K/V: keep them on one XCD (PA_MFMA_COL_SWIZZLE 2), or give each XCD
-  // a contiguous range of the grid (1).
-  GridPos gp;
-  if constexpr (kColWaves && PA_MFMA_COL_SWIZZLE == 2)
-    gp = grid_pos_grouped(groups);
-  else
-    gp = grid_pos<(kColWaves && PA_MFMA_COL_SWIZZLE == 1) || PA_XCD_SWIZZLE>();
+  const GridPos gp = grid_pos();
   const int p = gp.y;
-  const int g = gp.x / groups;        // kv head
-  // 16-column tile of this kv head's (row, head) pairs
-  const int tile = kColWaves ? (gp.x % groups) * NW + w : gp.x % P.n_tiles;
+  const int g = gp.x / P.n_tiles;    // kv head
+  const int tile = gp.x % P.n_tiles;  // 16-column tile of this kv head's (row, head) pairs
   const int s = gp.z;
 
   const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
   const int blk_begin = p * bpp;
   // this wave's blocks: first, first + kStride, ...
-  constexpr int kStride = kColWaves ? 1 : NW;
-  const int first = kColWaves ? blk_begin : blk_begin + w;
+  constexpr int kStride = NW;
+  const int first = blk_begin + w;
 
   // Start-up loads, issued before anything waits on them: the wave's first 64
   // block ids (bounded by the partition's table range, as the context length
@@ -147,11 +112,8 @@ void decode_mfma_kernel(DecodeParams P) {
   // region holds the wave's merge rows (16 columns x D floats, padded). The
   // wave overwrites its stage only after its last read of it, and a wave's
   // LDS accesses complete in order, so no barrier guards either use.
-  __shared__ float sm_o[kDma ? 1 : NW][16][D + kPad];
-  __shared__ __attribute__((aligned(16))) char sk0[kDma ? NW : 1][kBlock * kRowBytes];
-  __shared__ __attribute__((aligned(16))) char sk1[kDma ? NW : 1][kBlock * kRowBytes];
-  char* const stage = reinterpret_cast<char*>(&sm_o[kDma ? 0 : w][0][0]);
-  auto kslot = [&](int d) -> char* { return d == 0 ? &sk0[kDma ? w : 0][0] : &sk1[kDma ? w : 0][0]; };
+  __shared__ float sm_o[NW][16][D + kPad];
+  char* const stage = reinterpret_cast<char*>(&sm_o[w][0][0]);
   {
     const char* qp = reinterpret_cast<const char*>(P.q) + ((size_t)qrow * P.Hq + qh) * kRowBytes;
 #pragma unroll
@@ -189,19 +151,7 @@ void decode_mfma_kernel(DecodeParams P) {
   // Issue the loads of physical block b's tile (logical block blk) into
   // (kb, vb). An id outside the pool marks the group bad and loads nothing;
   // so does a block that does not exist (an empty ring refill).
-  // LDS image of a K tile (kDma): row r at r * 256 bytes, its 16-byte chunk c
-  // in slot c ^ r. Load j brings rows 4 j + rg: each group of 16 lanes still
-  // reads one whole 256-byte row (chunk col ^ row), and the operand reads
-  // below (chunk 4 kk + rg of row col, slot (4 kk + rg) ^ col) spread a
-  // 16-lane group over all 16 slots of the bank width: no conflicts.
-  int dma_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 4 * j + rg;
-    dma_off[j] = r * kRowBytes + ((col ^ r) & 15) * 16;
-  }
-
-  auto load = [&](int d, uint4 (&kb)[4], uint4 (&vb)[4], int b, int blk, bool exists) {
+  auto load = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, int blk, bool exists) {
     const bool valid = b >= 0 && b < P.NB;
     bad |= exists && !valid;
     const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
@@ -210,48 +160,27 @@ void decode_mfma_kernel(DecodeParams P) {
     const int bytes = exists && valid ? rows * kRowBytes : 0;
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
-    if constexpr (kDma) {
-      // The slot's previous tile was read (and its reads waited for) by the
-      // previous step's MFMAs: keep this refill after them.
-      asm volatile("" ::: "memory");
-      char* dst = kslot(d);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ld16_lds<kPolicy>(rk, dst + j * 4 * kRowBytes, dma_off[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kb[j] = ld16<kPolicy>(rk, row_lane + j * kRowBytes);
-    }
+    for (int j = 0; j < 4; ++j) kb[j] = ld16<kPolicy>(rk, row_lane + j * kRowBytes);
 #pragma unroll
     for (int j = 0; j < 4; ++j) vb[j] = ld16<kPolicy>(rv, row_lane + j * kRowBytes);
   };
 
-  auto consume = [&](int d, const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
+  auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
     // Transpose K through the wave's LDS stage into the A operand layout:
     // step kk needs, in lane (rg, col), dims 32 kk + 8 rg .. + 7 (chunk
     // 4 kk + rg) of row t = col. Rows are kStageRow apart (256 B + 16 B of
     // padding), so both the row writes and the strided reads are free of
     // bank conflicts.
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<uint4*>(stage + (4 * rg + j) * kStageRow + col * 16) = kb[j];
     f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (kDma) {
-      const char* src = kslot(d);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 ka = *reinterpret_cast<const uint4*>(
-            src + col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16);
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
-                                                    0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(stage + (4 * rg + j) * kStageRow + col * 16) = kb[j];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint4 ka =
-            *reinterpret_cast<const uint4*>(stage + col * kStageRow + (4 * kk + rg) * 16);
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk],
-                                                    st, 0, 0, 0);
-      }
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 ka = *reinterpret_cast<const uint4*>(stage + col * kStageRow + (4 * kk + rg) * 16);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
+                                                  0, 0, 0);
     }
     const int tok0 = blk * kBlock + 4 * rg;
     // Some column masks some row of this block (wave-uniform).
@@ -302,59 +231,12 @@ void decode_mfma_kernel(DecodeParams P) {
     block_pipeline<DEPTH>(
         bt_row, first, kStride, nk, lane, ids0,
         [&](int d, int b, int k, bool exists) {
-          load(d, kb[d], vb[d], b, first + k * kStride, exists);
+          load(kb[d], vb[d], b, first + k * kStride, exists);
         },
-        [&](int d, int k) { consume(d, kb[d], vb[d], first + k * kStride); });
+        [&](int d, int k) { consume(kb[d], vb[d], first + k * kStride); });
   }
 
   lsum = rows_sum(lsum);  // per column: sum over the 4 row groups
-
-  if constexpr (kColWaves) {
-    // The wave holds its columns' whole state for this partition: lane
-    // (rg, col) writes dims 8 (4 rg + i) + 0..7 (i = 0..3) of column col,
-    // from acc[0..7][i].
-    if (!col_ok) return;
-    const int i = gc / P.G;
-    const int h = g * P.G + gc % P.G;
-    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
-    const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
-    if (np <= 1 ? p != 0 : p >= np) return;
-    const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
-    const float nan = __builtin_nanf("");
-    if (np > 1) {
-      const size_t part = orow * P.n_parts + p;
-      float* dst = P.ws_o + part * D;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        float* d8 = dst + 8 * (4 * rg + ii);
-        *reinterpret_cast<float4*>(d8) =
-            bad ? make_float4(nan, nan, nan, nan)
-                : make_float4(acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]);
-        *reinterpret_cast<float4*>(d8 + 4) =
-            bad ? make_float4(nan, nan, nan, nan)
-                : make_float4(acc[4][ii], acc[5][ii], acc[6][ii], acc[7][ii]);
-      }
-      if (rg == 0) {
-        P.ws_ml[2 * part] = bad ? 0.0f : m;
-        P.ws_ml[2 * part + 1] = bad ? nan : lsum;
-      }
-    } else {
-      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        float res[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) res[e] = bad ? nan : acc[e][ii] * inv;
-        uint4 u;
-        u.x = pack_bf16x2(res[0], res[1]);
-        u.y = pack_bf16x2(res[2], res[3]);
-        u.z = pack_bf16x2(res[4], res[5]);
-        u.w = pack_bf16x2(res[6], res[7]);
-        st16(reinterpret_cast<char*>(P.out) + (orow * D + 8 * (4 * rg + ii)) * 2, u);
-      }
-    }
-    return;
-  }
 
   // Waves -> LDS -> one merged state per (head, dim).
   __shared__ float sm_m[NW][16], sm_l[NW][16];
@@ -428,28 +310,17 @@ void decode_mfma_kernel(DecodeParams P) {
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
+  // several column tiles per kv head: the chunk kernel, whose waves share each block
+  if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
   constexpr int NW = PA_MFMA_WAVES;
   constexpr int DEPTH = PA_MFMA_DEPTH;
-  const dim3 block(NW * kWave);
-#ifndef PA_CHUNK_KERNEL
-#define PA_CHUNK_KERNEL 1
-#endif
-  if (PA_CHUNK_KERNEL && p.n_tiles > 1) return launch_chunk_mfma(p, stream);
-  if (p.n_tiles > 1) {
-    // waves of a workgroup share each block: read through the caches
-    constexpr int CW = PA_MFMA_COL_WAVES;
-    const dim3 grid(p.Hkv * ((p.n_tiles + CW - 1) / CW), p.n_parts, p.B);
-    hipLaunchKernelGGL((decode_mfma_kernel<CW, PA_MFMA_COL_DEPTH, TilePolicy::kShared, true>), grid,
-                       dim3(CW * kWave), 0, stream, p);
-  } else {
-    const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B);
-    if (p.shared_kv)
-      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared, false>), grid, block,
-                         0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream, false>), grid, block,
-                         0, stream, p);
-  }
+  const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B), block(NW * kWave);
+  if (p.shared_kv)
+    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared>), grid, block, 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream>), grid, block, 0,
+                       stream, p);
   return hipGetLastError();
 }
 
