@@ -8,34 +8,37 @@
 // section 01: a token attends to every earlier token and to itself).
 //
 // Columns: the n x G (query row, head of the group) pairs of a sequence and
-// kv head, row-major, cut into tiles of 16, in the MFMA layouts of the decode
-// MFMA kernel (S^T = K Q^T on v_mfma_f32_16x16x32_bf16, O^T = V^T P^T on
-// v_mfma_f32_16x16x16_bf16; every accumulator a lane holds belongs to its own
-// column). A workgroup of NW waves owns NW consecutive tiles, one per wave,
-// and each wave keeps its tile's online-softmax state to the end.
+// kv head, row-major, cut into tiles of 16, in the column layout of the
+// decode MFMA kernel (S^T = K Q^T on v_mfma_f32_16x16x32_bf16; every
+// accumulator a lane holds belongs to its own column). A workgroup of NW
+// waves owns NW consecutive tiles, one per wave, and each wave keeps its
+// tile's online-softmax state to the end.
 //
-// The waves stream the partition's K/V blocks together through an LDS ring
-// of R slots. A slot holds one block's K tile (4 KiB) and V tile (4 KiB),
-// written by the loads themselves (buffer_load ... lds) in eight 1 KiB
-// pieces, one load instruction each, shared out over the waves: every byte
-// crosses the vector memory path once per workgroup, not once per wave (the
-// per-wave loads of a column tile kept that path busy most of the time). One
-// barrier per block publishes the slot and frees the previous one.
+// The waves stream the partition's K/V blocks, two at a time, through an LDS
+// ring of R slots. A slot holds a pair of blocks A, B: K tiles (4 KiB each)
+// then V tiles, written by the loads themselves (buffer_load ... lds) in
+// sixteen 1 KiB pieces, one load instruction each, shared out over the
+// waves: every byte crosses the vector memory path once per workgroup, not
+// once per wave (the per-wave loads of a column tile kept that path busy
+// most of the time). One barrier per pair publishes the slot and frees the
+// previous one. Taking blocks in pairs makes O^T = V^T P^T one K = 32
+// contraction (v_mfma_f32_16x16x32_bf16, the full-rate form) instead of two
+// K = 16 ones, and halves the softmax's per-lane work per block.
 //
-// LDS image of a slot (rows of 256 bytes, 16 chunks of 16 bytes):
+// LDS image of a tile (rows of 256 bytes, 16 chunks of 16 bytes):
 //   K row r at r * 256, its chunk c in position c ^ r: a 16-lane group loads
 //     one whole row (chunk col ^ row), and the MFMA operand reads (chunk
 //     4 kk + rg of row col) put the 16 lanes on 16 different positions of
 //     the bank width, so neither side conflicts;
-//   V row r at 4096 + r * 256, chunks in order: the operand reads (chunk col
-//     of row 4 rg + j) take one row per 16-lane group.
+//   V row r at r * 256, chunks in order: the operand reads (chunk col of row
+//     4 rg + j) take one row per 16-lane group.
 // Lanes of a load past the block's rows inside the context write zeros.
 #include "pa_device.h"
 #include "pa_launch.h"
 
-// LDS ring slots (3 or 4) and the register allocation's minimum waves per SIMD.
+// LDS ring slots (3 or 4 pairs of blocks) and the register allocation's minimum waves per SIMD.
 #ifndef PA_CHUNK_RING
-#define PA_CHUNK_RING 4
+#define PA_CHUNK_RING 3
 #endif
 #ifndef PA_CHUNK_MIN_WAVES
 #define PA_CHUNK_MIN_WAVES 4
@@ -51,10 +54,10 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;
-constexpr int kTileBytes = kBlock * kRowBytes;      // one K or V tile
-constexpr int kSlotBytes = 2 * kTileBytes;          // K, then V
+constexpr int kTileBytes = kBlock * kRowBytes;      // one K or V tile of one block
+constexpr int kSlotBytes = 4 * kTileBytes;          // a pair of blocks: K A, K B, V A, V B
 constexpr int kPieceBytes = kWave * 16;             // one load instruction
-constexpr int kPieces = kSlotBytes / kPieceBytes;   // per block
+constexpr int kPieces = kSlotBytes / kPieceBytes;   // per pair
 
 // s_waitcnt bounding only the vector memory count (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
@@ -77,11 +80,11 @@ __device__ __forceinline__ void ring_barrier() {
 
 template <int NW, int R, TilePolicy kPolicy>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(NW >= 4 ? PA_CHUNK_MIN_WAVES : 3)))
+__attribute__((amdgpu_waves_per_eu(NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
 void chunk_mfma_kernel(DecodeParams P) {
   static_assert(kPieces % NW == 0, "pieces must divide over the waves");
   static_assert(R >= 3 && R <= 4, "ring of 3 or 4 slots");
-  constexpr int kPer = kPieces / NW;  // load instructions per wave per block
+  constexpr int kPer = kPieces / NW;  // load instructions per wave per pair
   // One LDS object per slot, so that the compiler's load counting tells the
   // slots apart and waits only for the slot it reads.
   __shared__ __attribute__((aligned(16))) char ring0[kSlotBytes];
@@ -170,71 +173,85 @@ void chunk_mfma_kernel(DecodeParams P) {
   const size_t head_off = (size_t)g * kTileBytes;
   const size_t block_stride = (size_t)P.Hkv * kTileBytes;
 
-  // This wave's pieces of every block: piece q = kPer w + i; pieces 0..3 are
-  // K rows 4 q .. 4 q + 3, pieces 4..7 V rows 4 (q - 4) .. + 3.
-  int piece_lds[kPer], piece_off[kPer];
-  bool piece_v[kPer];
+  // This wave's pieces of every pair: piece q = kPer w + i holds rows
+  // 4 (q & 3) + 0..3 of tile q >> 2 (0: K of block A, 1: K of block B, 2: V
+  // of A, 3: V of B), at q KiB into the slot.
+  int piece_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = kPer * w + i;
-    piece_v[i] = q >= 4;
     const int r = 4 * (q & 3) + rg;
-    piece_lds[i] = q * kPieceBytes;
-    piece_off[i] = r * kRowBytes + (piece_v[i] ? col : ((col ^ r) & 15)) * 16;
+    piece_off[i] = r * kRowBytes + (q >= 8 ? col : ((col ^ r) & 15)) * 16;
   }
 
-  // Load physical block b (logical block blk) into slot d. An id outside the
-  // pool marks the columns bad and loads nothing; so does a block that does
-  // not exist (an empty refill past the last block, kept so that every step
-  // issues the same number of loads).
-  auto issue = [&](int d, int b, int blk, bool exists) {
-    const bool valid = b >= 0 && b < P.NB;
-    bad |= exists && !valid;
-    const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
-    const int rows = min(kBlock, ctx_wg - blk * kBlock);
-    const int bytes = exists && valid ? rows * kRowBytes : 0;
-    const rsrc_t rk = make_rsrc(kbase + off, bytes);
-    const rsrc_t rv = make_rsrc(vbase + off, bytes);
+  // Load logical blocks blk (A, physical ba) and blk + 1 (B, physical bb)
+  // into slot d. An id outside the pool marks the columns bad and loads
+  // nothing; so does a block that does not exist (past the partition, or an
+  // empty refill past the last pair, kept so that every step issues the same
+  // number of loads). Only rows inside the workgroup's context are fetched.
+  auto issue = [&](int d, int ba, int bb, int blk, bool ea, bool eb) {
+    const bool oka = ba >= 0 && ba < P.NB;
+    const bool okb = bb >= 0 && bb < P.NB;
+    bad |= (ea && !oka) || (eb && !okb);
+    const size_t offa = (size_t)(oka ? ba : 0) * block_stride + head_off;
+    const size_t offb = (size_t)(okb ? bb : 0) * block_stride + head_off;
+    const int bytes_a = ea && oka ? max(0, min(kBlock, ctx_wg - blk * kBlock)) * kRowBytes : 0;
+    const int bytes_b =
+        eb && okb ? max(0, min(kBlock, ctx_wg - (blk + 1) * kBlock)) * kRowBytes : 0;
+    const rsrc_t rka = make_rsrc(kbase + offa, bytes_a);
+    const rsrc_t rkb = make_rsrc(kbase + offb, bytes_b);
+    const rsrc_t rva = make_rsrc(vbase + offa, bytes_a);
+    const rsrc_t rvb = make_rsrc(vbase + offb, bytes_b);
     char* dst = slot(d);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      ld16_lds<kPolicy>(piece_v[i] ? rv : rk, dst + piece_lds[i], piece_off[i]);
+    for (int i = 0; i < kPer; ++i) {
+      const int q = kPer * w + i;
+      const int t = q >> 2;  // wave-uniform
+      const rsrc_t r = t == 0 ? rka : t == 1 ? rkb : t == 2 ? rva : rvb;
+      ld16_lds<kPolicy>(r, dst + q * kPieceBytes, piece_off[i]);
+    }
   };
 
-  // S^T of the block in slot d: raw logits, lane (rg, col) holds tokens
-  // 4 rg + 0..3 of column col.
-  auto qk = [&](int d) -> f32x4_t {
+  // One pair of blocks: S^T of both (lane (rg, col) holds tokens 4 rg + 0..3
+  // of each, column col), the online softmax over their 32 tokens, then
+  // O^T += V^T P^T as one K = 32 contraction: contraction slots 8 rg + 0..3
+  // are block A's tokens 4 rg + 0..3 and slots 8 rg + 4..7 block B's, so a
+  // lane's own probabilities are its B operand as they stand.
+  auto consume = [&](int d, int blk, bool b_live) {
     const char* src = slot(d);
-    f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t sa = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t sb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint4 ka = *reinterpret_cast<const uint4*>(
-          src + col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16);
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
+      const int o = col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16;
+      const uint4 ka = *reinterpret_cast<const uint4*>(src + o);
+      const uint4 kb = *reinterpret_cast<const uint4*>(src + kTileBytes + o);
+      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], sa,
+                                                  0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qop[kk], sb,
                                                   0, 0, 0);
     }
-    return st;
-  };
-
-  // Online softmax over the block's logits st, then O^T += V^T P^T with the
-  // block's V from slot d.
-  auto softmax_pv = [&](int d, const f32x4_t st, int blk) {
-    const char* src = slot(d);
-    uint4 vb[4];
+    uint4 va[4], vb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      vb[j] = *reinterpret_cast<const uint4*>(src + kTileBytes + (4 * rg + j) * kRowBytes + col * 16);
-    // Raw logits; those past a column's causal limit are removed (only a
-    // block that reaches some column's limit needs the test: wave-uniform).
-    float x[4] = {st[0], st[1], st[2], st[3]};
-    if (blk * kBlock + kBlock > ctx_min) {
+    for (int j = 0; j < 4; ++j) {
+      const int o = (4 * rg + j) * kRowBytes + col * 16;
+      va[j] = *reinterpret_cast<const uint4*>(src + 2 * kTileBytes + o);
+      vb[j] = *reinterpret_cast<const uint4*>(src + 3 * kTileBytes + o);
+    }
+    // Raw logits; those past a column's causal limit, and all of block B when
+    // it lies past the partition, are removed (wave-uniform test first).
+    float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+    if (blk * kBlock + 2 * kBlock > ctx_min || !b_live) {
       const int tok0 = blk * kBlock + 4 * rg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
         if (tok0 + i >= ctx_col) x[i] = -INFINITY;
+        if (!b_live || tok0 + kBlock + i >= ctx_col) x[4 + i] = -INFINITY;
+      }
     }
-    const float mx_raw = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    const float mx = mx_raw * qs;  // -inf stays -inf (qs > 0)
+    const float m8 = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    const float mx = rows_max(m8) * qs;  // -inf stays -inf (qs > 0)
     // The reference m (what the probabilities are taken relative to) moves
     // only when a column's max passes it by more than kLazy: the
     // probabilities then stay below 2^kLazy, the result is the same up to
@@ -246,66 +263,68 @@ void chunk_mfma_kernel(DecodeParams P) {
     const float ref = up ? m_new : m;
     const float ref_use = (ref == -INFINITY) ? 0.0f : ref;
     const float alpha = exp2_fast(m - ref_use);  // exactly 1 where the reference stays
-    float pr[4];
+    float pr[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
+    lsum = lsum * alpha +
+           (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
     m = ref;
     if (__builtin_amdgcn_ballot_w64(up) != 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] *= alpha;
     }
-    const s16x4_t pop = __builtin_bit_cast(
-        s16x4_t, make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])));
+    const bf16x8_t pop = __builtin_bit_cast(
+        bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                             pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {  // 32-bit word k of each V chunk: dims 2k, 2k+1
-      const uint32_t w0 = word(vb[0], k), w1 = word(vb[1], k);
-      const uint32_t w2 = word(vb[2], k), w3 = word(vb[3], k);
-      const s16x4_t a_lo =
-          __builtin_bit_cast(s16x4_t, make_uint2(pack_lo16(w0, w1), pack_lo16(w2, w3)));
-      const s16x4_t a_hi =
-          __builtin_bit_cast(s16x4_t, make_uint2(pack_hi16(w0, w1), pack_hi16(w2, w3)));
-      acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, pop, acc[2 * k], 0, 0, 0);
-      acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, pop, acc[2 * k + 1], 0, 0, 0);
+      const uint32_t a0 = word(va[0], k), a1 = word(va[1], k), a2 = word(va[2], k),
+                     a3 = word(va[3], k);
+      const uint32_t b0 = word(vb[0], k), b1 = word(vb[1], k), b2 = word(vb[2], k),
+                     b3 = word(vb[3], k);
+      const bf16x8_t v_lo = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_lo16(a0, a1), pack_lo16(a2, a3), pack_lo16(b0, b1),
+                               pack_lo16(b2, b3)));
+      const bf16x8_t v_hi = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_hi16(a0, a1), pack_hi16(a2, a3), pack_hi16(b0, b1),
+                               pack_hi16(b2, b3)));
+      acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_lo, pop, acc[2 * k], 0, 0, 0);
+      acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_hi, pop, acc[2 * k + 1], 0, 0, 0);
     }
   };
 
-  // The ring: block k sits in slot k % R. Step k of a wave takes S^T of
-  // block k + 1 (independent of the softmax of block k, so the two overlap)
-  // and the softmax and PV product of block k. Before it, each wave waits
-  // for its own pieces of block k + 1 (the block issued after it may stay in
-  // flight), then a barrier makes every wave's pieces visible and shows that
-  // every wave is done with block k - 1 (its K was read at step k - 2, its V
-  // at step k - 1), whose slot takes block k + R - 1. Block ids are read 64
-  // at a time (lane j holds the chunk's j-th id, broadcast with readlane);
-  // the ring drains at each chunk's end.
+  // The ring: pair j (blocks 2 j, 2 j + 1 of the partition's range) sits in
+  // slot j % R. Before pair j is read, each wave waits for its own pieces of
+  // it (the R - 2 pairs issued after it may stay in flight), then a barrier
+  // makes every wave's pieces visible and shows that every wave is done with
+  // pair j - 1, whose slot takes pair j + R - 1. Block ids are read 64 at a
+  // time (lane i holds the chunk's i-th id, broadcast with readlane); the
+  // ring drains at each chunk's end.
   const int nk = max(0, blk_end - blk_begin);
   for (int c0 = 0; c0 < nk; c0 += kWave) {
-    const int cn = min(kWave, nk - c0);
-    if (c0 > 0) ring_barrier();  // every wave is done with the previous chunk's slots
+    const int cn = min(kWave, nk - c0);  // blocks in this chunk
+    const int pn = (cn + 1) / 2;         // pairs
+    if (c0 > 0) ring_barrier();          // every wave is done with the previous chunk's slots
     const int ids = c0 == 0 ? ids0 : (lane < cn ? bt_row[blk_begin + c0 + lane] : -1);
+    auto issue_pair = [&](int d, int j) {
+      const int i = 2 * j;
+      issue(d, __builtin_amdgcn_readlane(ids, min(i, kWave - 1)),
+            __builtin_amdgcn_readlane(ids, min(i + 1, kWave - 1)), blk_begin + c0 + i, i < cn,
+            i + 1 < cn);
+    };
 #pragma unroll
-    for (int d = 0; d < R - 1; ++d)
-      issue(d, __builtin_amdgcn_readlane(ids, d), blk_begin + c0 + d, d < cn);
-    wait_vmcnt<(R - 2) * kPer>();
-    ring_barrier();
-    f32x4_t s_next = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (has_cols) s_next = qk(0);
-    // Steps past the chunk's last block still wait, meet and refill (with
+    for (int d = 0; d < R - 1; ++d) issue_pair(d, d);
+    // Steps past the chunk's last pair still wait, meet and refill (with
     // empty loads): a refill under a branch costs the compiler its record of
     // which slot each load writes, and then it waits for every slot.
-    for (int k0 = 0; k0 < cn; k0 += R) {
+    for (int j0 = 0; j0 < pn; j0 += R) {
 #pragma unroll
       for (int d = 0; d < R; ++d) {
-        const int k = k0 + d;
-        wait_vmcnt<(R - 3) * kPer>();
+        const int j = j0 + d;
+        wait_vmcnt<(R - 2) * kPer>();
         ring_barrier();
-        const int kl = k + R - 1;
-        issue((d + R - 1) % R, __builtin_amdgcn_readlane(ids, min(kl, kWave - 1)),
-              blk_begin + c0 + kl, kl < cn);
-        const f32x4_t s_cur = s_next;
-        if (has_cols && k + 1 < cn) s_next = qk((d + 1) % R);
-        if (has_cols && k < cn) softmax_pv(d, s_cur, blk_begin + c0 + k);
+        issue_pair((d + R - 1) % R, j + R - 1);
+        if (has_cols && j < pn) consume(d, blk_begin + c0 + 2 * j, 2 * j + 1 < cn);
       }
     }
   }
