@@ -291,3 +291,43 @@ def test_step_graph_replays_match_eager(pa, name, partition):
         step()                                   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("f32", 1, 1, 64), ("bf16", 8, 1, 128)])
+def test_decode_at_the_batch_limit(pa, dtype, Hq, Hkv, D):
+    # 65535 sequences (the largest batch the ABI takes: one grid row each),
+    # short ragged contexts including empty ones, blocks scattered over a
+    # shuffled pool; every output row against the oracle.
+    say(f"[batch limit] {dtype} Hq={Hq} Hkv={Hkv} D={D}")
+    import oracle
+    B = 65535
+    rng = np.random.default_rng(41)
+    cl = rng.integers(0, 41, B).astype(np.int32)
+    nblk = (cl + 15) // 16
+    NB = int(nblk.sum()) + 7
+    MB = int(nblk.max())
+    perm = rng.permutation(NB).astype(np.int32)
+    bt = np.full((B, MB), -1, np.int32)
+    start = np.concatenate([[0], np.cumsum(nblk)[:-1]])
+    for j in range(MB):
+        has = nblk > j
+        bt[has, j] = perm[start[has] + j]
+    if dtype == "f32":
+        mk = lambda *s: rng.standard_normal(s, dtype=np.float32)  # noqa: E731
+        tdt = torch.float32
+    else:
+        mk = lambda *s: (rng.standard_normal(s, dtype=np.float32).view(np.uint32) >> 16  # noqa: E731
+                         ).astype(np.uint16) & np.uint16(0xFF7F)     # finite bf16 bits
+        tdt = torch.bfloat16
+    q, k, v = mk(B, Hq, D), mk(NB, Hkv, 16, D), mk(NB, Hkv, 16, D)
+    dev = lambda a: (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16  # noqa: E731
+                     else torch.from_numpy(a)).to("cuda")
+    scale = 1.0 / np.sqrt(D)
+    for part in (0, 16):
+        out = pa.decode(dev(q), dev(k), dev(v), torch.from_numpy(bt).to("cuda"),
+                        torch.from_numpy(cl).to("cuda"), scale, int(cl.max()), partition=part)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy().astype(np.float64)
+        expect = oracle.decode(q, k, v, bt, cl, scale)
+        assert np.all(got[cl == 0] == 0.0)
+        assert max_abs_err(out, expect) <= TOL[dtype], part
