@@ -10,7 +10,8 @@ import torch
 
 from paged_kv_cache_410_amd.workloads import Spec
 
-from gpu_cases import TOL, Step, host_bits, max_abs_err, say
+import oracle
+from gpu_cases import TOL, Step, host_bits, max_abs_err, oracle_view, say
 
 pytestmark = pytest.mark.gpu
 
@@ -45,6 +46,9 @@ CHUNKS = {
     # unsplit rows longer than one 64-block id chunk per wave
     "mq_long": Spec("mq_long", "bf16", 2, 2, 2, 128, seed=38, lengths=("fixed", [9000, 3000]),
                     chunk=("uniform", 2, 6)),
+    # two 16-column tiles per kv head: the chunk kernel's two-wave shape
+    "mq_gqa8_short": Spec("mq_gqa8_short", "bf16", 4, 16, 2, 128, seed=39,
+                          lengths=("uniform", 1, 900), chunk=("uniform", 2, 4)),
 }
 
 
@@ -106,3 +110,22 @@ def test_chunk_append_kv_bit_exact(pa, name):
     assert np.array_equal(slots.cpu().numpy(), st.tb.slots)
     assert np.array_equal(host_bits(st.k_cache), st.k_after)
     assert np.array_equal(host_bits(st.v_cache), st.v_after)
+
+
+@pytest.mark.parametrize("name", ["mq_gqa8", "mq_gqa8_short", "mq_single", "mq_f32"])
+@pytest.mark.parametrize("scale_mul", [-1.0, 0.0])
+def test_negative_and_zero_scale(pa, name, scale_mul):
+    # A negative logit scale and a zero one through every attention kernel
+    # (chunk, matrix-core decode, vector), against the oracle at that scale.
+    say(f"[scale x{scale_mul}] {name}")
+    st = Step(CHUNKS[name], oracle_full=False)
+    st.run_cache_ops(pa)
+    scale = st.spec.scale * scale_mul
+    out = pa.multi_query(st.q, st.k_cache, st.v_cache, st.block_tables, st.context_lens,
+                         st.query_start, scale, st.max_ctx, st.max_q, partition=64)
+    expect = oracle.multi_query(oracle_view(st.q_bits), oracle_view(st.k_after),
+                                oracle_view(st.v_after), st.tb.block_tables, st.tb.context_lens,
+                                st.tb.query_start, scale)
+    err = max_abs_err(out, expect)
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL[st.spec.dtype]
