@@ -23,15 +23,18 @@
 // most of the time). One barrier per pair publishes the slot and frees the
 // previous one. Taking blocks in pairs makes O^T = V^T P^T one K = 32
 // contraction (v_mfma_f32_16x16x32_bf16, the full-rate form) instead of two
-// K = 16 ones, and halves the softmax's per-lane work per block.
+// K = 16 ones, and halves the softmax's per-lane work per block. Output tile
+// et of the PV product holds dims 16 et + 0..15 (row m: dim 16 et + m).
 //
 // LDS image of a tile (rows of 256 bytes, 16 chunks of 16 bytes):
 //   K row r at r * 256, its chunk c in position c ^ r: a 16-lane group loads
 //     one whole row (chunk col ^ row), and the MFMA operand reads (chunk
 //     4 kk + rg of row col) put the 16 lanes on 16 different positions of
 //     the bank width, so neither side conflicts;
-//   V row r at r * 256, chunks in order: the operand reads (chunk col of row
-//     4 rg + j) take one row per 16-lane group.
+//   V row r at r * 256, its chunk c in position c ^ r as well: the operand
+//     comes from transposing LDS reads (ds_read_b64_tr_b16), each 16-lane
+//     group naming 4 rows x 32 bytes, which the swizzle spreads over the
+//     bank width.
 // Lanes of a load past the block's rows inside the context write zeros.
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -175,13 +178,29 @@ void chunk_mfma_kernel(DecodeParams P) {
 
   // This wave's pieces of every pair: piece q = kPer w + i holds rows
   // 4 (q & 3) + 0..3 of tile q >> 2 (0: K of block A, 1: K of block B, 2: V
-  // of A, 3: V of B), at q KiB into the slot.
+  // of A, 3: V of B), at q KiB into the slot. K and V tiles alike keep
+  // chunk c of row r at position c ^ r.
   int piece_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = kPer * w + i;
     const int r = 4 * (q & 3) + rg;
-    piece_off[i] = r * kRowBytes + (q >= 8 ? col : ((col ^ r) & 15)) * 16;
+    piece_off[i] = r * kRowBytes + ((col ^ r) & 15) * 16;
+  }
+
+  // Transposed V reads (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+  // t names 4 consecutive bf16 (row t of a 16 x 4 block) and lane i receives
+  // element (row 4 e + i / 4, column i % 4) for e = 0..3. Lane (rg, col)
+  // names row 4 rg + col / 4 of the V tile at dims 16 et + 4 (col % 4) ..
+  // + 3, so it receives V[4 rg + e][16 et + col], e = 0..3: its operand of
+  // output tile et, row m = col standing for dim 16 et + col. Offsets within
+  // a (swizzled) V tile, per tile et:
+  int vtr_off[8];
+#pragma unroll
+  for (int et = 0; et < 8; ++et) {
+    const int r = 4 * rg + col / 4;
+    const int dim = 16 * et + 4 * (col % 4);
+    vtr_off[et] = r * kRowBytes + (((dim / 8) ^ r) & 15) * 16 + (dim % 8) * 2;
   }
 
   // Load logical blocks blk (A, physical ba) and blk + 1 (B, physical bb)
@@ -231,13 +250,6 @@ void chunk_mfma_kernel(DecodeParams P) {
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qop[kk], sb,
                                                   0, 0, 0);
     }
-    uint4 va[4], vb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int o = (4 * rg + j) * kRowBytes + col * 16;
-      va[j] = *reinterpret_cast<const uint4*>(src + 2 * kTileBytes + o);
-      vb[j] = *reinterpret_cast<const uint4*>(src + 3 * kTileBytes + o);
-    }
     // Raw logits; those past a column's causal limit, and all of block B when
     // it lies past the partition, are removed (wave-uniform test first).
     float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
@@ -276,20 +288,21 @@ void chunk_mfma_kernel(DecodeParams P) {
     const bf16x8_t pop = __builtin_bit_cast(
         bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                              pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
+    // O^T tile et (dims 16 et + m) += V^T P^T: the A operand of lane (rg, col)
+    // is V_A[4 rg + 0..3][16 et + col] then V_B[4 rg + 0..3][16 et + col],
+    // read transposed from LDS.
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    const char* va = src + 2 * kTileBytes;
+    const char* vb = src + 3 * kTileBytes;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {  // 32-bit word k of each V chunk: dims 2k, 2k+1
-      const uint32_t a0 = word(va[0], k), a1 = word(va[1], k), a2 = word(va[2], k),
-                     a3 = word(va[3], k);
-      const uint32_t b0 = word(vb[0], k), b1 = word(vb[1], k), b2 = word(vb[2], k),
-                     b3 = word(vb[3], k);
-      const bf16x8_t v_lo = __builtin_bit_cast(
-          bf16x8_t, make_uint4(pack_lo16(a0, a1), pack_lo16(a2, a3), pack_lo16(b0, b1),
-                               pack_lo16(b2, b3)));
-      const bf16x8_t v_hi = __builtin_bit_cast(
-          bf16x8_t, make_uint4(pack_hi16(a0, a1), pack_hi16(a2, a3), pack_hi16(b0, b1),
-                               pack_hi16(b2, b3)));
-      acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_lo, pop, acc[2 * k], 0, 0, 0);
-      acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v_hi, pop, acc[2 * k + 1], 0, 0, 0);
+    for (int et = 0; et < 8; ++et) {
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(__attribute__((address_space(3))) char*)(va + vtr_off[et]));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(__attribute__((address_space(3))) char*)(vb + vtr_off[et]));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, acc[et], 0, 0, 0);
     }
   };
 
@@ -333,8 +346,8 @@ void chunk_mfma_kernel(DecodeParams P) {
   lsum = rows_sum(lsum);  // per column: sum over the 4 row groups
 
   // The wave holds its columns' whole state for this partition: lane
-  // (rg, col) writes dims 8 (4 rg + i) + 0..7 (i = 0..3) of column col, from
-  // acc[0..7][i].
+  // (rg, col) writes dims 16 et + 4 rg + 0..3 of column col, from acc[et]
+  // (et = 0..7).
   if (!col_ok) return;
   const int i = gc / P.G;
   const int h = g * P.G + gc % P.G;
@@ -347,15 +360,10 @@ void chunk_mfma_kernel(DecodeParams P) {
     const size_t part = orow * P.n_parts + p;
     float* dst = P.ws_o + part * kD;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float* d8 = dst + 8 * (4 * rg + ii);
-      *reinterpret_cast<float4*>(d8) =
+    for (int et = 0; et < 8; ++et)
+      *reinterpret_cast<float4*>(dst + 16 * et + 4 * rg) =
           bad ? make_float4(nan, nan, nan, nan)
-              : make_float4(acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]);
-      *reinterpret_cast<float4*>(d8 + 4) =
-          bad ? make_float4(nan, nan, nan, nan)
-              : make_float4(acc[4][ii], acc[5][ii], acc[6][ii], acc[7][ii]);
-    }
+              : make_float4(acc[et][0], acc[et][1], acc[et][2], acc[et][3]);
     if (rg == 0) {
       P.ws_ml[2 * part] = bad ? 0.0f : m;
       P.ws_ml[2 * part + 1] = bad ? nan : lsum;
@@ -363,16 +371,13 @@ void chunk_mfma_kernel(DecodeParams P) {
   } else {
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float res[8];
+    for (int et = 0; et < 8; ++et) {
+      float res[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) res[e] = bad ? nan : acc[e][ii] * inv;
-      uint4 u;
-      u.x = pack_bf16x2(res[0], res[1]);
-      u.y = pack_bf16x2(res[2], res[3]);
-      u.z = pack_bf16x2(res[4], res[5]);
-      u.w = pack_bf16x2(res[6], res[7]);
-      st16(reinterpret_cast<char*>(P.out) + (orow * kD + 8 * (4 * rg + ii)) * 2, u);
+      for (int e = 0; e < 4; ++e) res[e] = bad ? nan : acc[et][e] * inv;
+      *reinterpret_cast<uint2*>(reinterpret_cast<char*>(P.out) +
+                                (orow * kD + 16 * et + 4 * rg) * 2) =
+          make_uint2(pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]));
     }
   }
 }
