@@ -214,9 +214,9 @@ void chunk_mfma_kernel(DecodeParams P) {
     bad |= (ea && !oka) || (eb && !okb);
     const size_t offa = (size_t)(oka ? ba : 0) * block_stride + head_off;
     const size_t offb = (size_t)(okb ? bb : 0) * block_stride + head_off;
-    const int bytes_a = ea && oka ? max(0, min(kBlock, ctx_wg - blk * kBlock)) * kRowBytes : 0;
-    const int bytes_b =
-        eb && okb ? max(0, min(kBlock, ctx_wg - (blk + 1) * kBlock)) * kRowBytes : 0;
+    // (a block that exists starts inside the workgroup's context: >= 1 row)
+    const int bytes_a = ea && oka ? min(kBlock, ctx_wg - blk * kBlock) * kRowBytes : 0;
+    const int bytes_b = eb && okb ? min(kBlock, ctx_wg - (blk + 1) * kBlock) * kRowBytes : 0;
     const rsrc_t rka = make_rsrc(kbase + offa, bytes_a);
     const rsrc_t rkb = make_rsrc(kbase + offb, bytes_b);
     const rsrc_t rva = make_rsrc(vbase + offa, bytes_a);
