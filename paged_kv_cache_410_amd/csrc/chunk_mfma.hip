@@ -250,6 +250,20 @@ void chunk_mfma_kernel(DecodeParams P) {
       sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qop[kk], sb,
                                                   0, 0, 0);
     }
+    // The V operands, read transposed from LDS now so that their latency
+    // passes under the softmax: the A operand of lane (rg, col) for output
+    // tile et is V_A[4 rg + 0..3][16 et + col] then V_B[4 rg + 0..3][16 et + col].
+    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+    bf16x8_t vop[8];
+#pragma unroll
+    for (int et = 0; et < 8; ++et) {
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 2 * kTileBytes + vtr_off[et]));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 3 * kTileBytes + vtr_off[et]));
+      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+      vop[et] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+    }
     // Raw logits; those past a column's causal limit, and all of block B when
     // it lies past the partition, are removed (wave-uniform test first).
     float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
@@ -288,22 +302,10 @@ void chunk_mfma_kernel(DecodeParams P) {
     const bf16x8_t pop = __builtin_bit_cast(
         bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                              pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
-    // O^T tile et (dims 16 et + m) += V^T P^T: the A operand of lane (rg, col)
-    // is V_A[4 rg + 0..3][16 et + col] then V_B[4 rg + 0..3][16 et + col],
-    // read transposed from LDS.
-    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-    const char* va = src + 2 * kTileBytes;
-    const char* vb = src + 3 * kTileBytes;
+    // O^T tile et (dims 16 et + m) += V^T P^T.
 #pragma unroll
-    for (int et = 0; et < 8; ++et) {
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(__attribute__((address_space(3))) char*)(va + vtr_off[et]));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(__attribute__((address_space(3))) char*)(vb + vtr_off[et]));
-      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, acc[et], 0, 0, 0);
-    }
+    for (int et = 0; et < 8; ++et)
+      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], pop, acc[et], 0, 0, 0);
   };
 
   // The ring: pair j (blocks 2 j, 2 j + 1 of the partition's range) sits in
