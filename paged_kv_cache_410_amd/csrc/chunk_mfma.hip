@@ -31,10 +31,11 @@
 //     one whole row (chunk col ^ row), and the MFMA operand reads (chunk
 //     4 kk + rg of row col) put the 16 lanes on 16 different positions of
 //     the bank width, so neither side conflicts;
-//   V row r at r * 256, its chunk c in position c ^ r as well: the operand
-//     comes from transposing LDS reads (ds_read_b64_tr_b16), each 16-lane
-//     group naming 4 rows x 32 bytes, which the swizzle spreads over the
-//     bank width.
+//   V row r at r * 256, its chunk c in position c ^ (2 r mod 16): the
+//     operand comes from transposing LDS reads (ds_read_b64_tr_b16), each
+//     16-lane group naming 32 bytes (chunks 2 et, 2 et + 1) of 4 rows; the
+//     swizzle puts any 8 consecutive rows' 16 chunks on 16 different
+//     positions of the bank width (with c ^ r, two rows 8 apart met).
 // Lanes of a load past the block's rows inside the context write zeros.
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -178,14 +179,15 @@ void chunk_mfma_kernel(DecodeParams P) {
 
   // This wave's pieces of every pair: piece q = kPer w + i holds rows
   // 4 (q & 3) + 0..3 of tile q >> 2 (0: K of block A, 1: K of block B, 2: V
-  // of A, 3: V of B), at q KiB into the slot. K and V tiles alike keep
-  // chunk c of row r at position c ^ r.
+  // of A, 3: V of B), at q KiB into the slot. K tiles keep chunk c of row r
+  // at position c ^ r, V tiles at c ^ (2 r mod 16).
   int piece_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = kPer * w + i;
     const int r = 4 * (q & 3) + rg;
-    piece_off[i] = r * kRowBytes + ((col ^ r) & 15) * 16;
+    const int swz = q >= 8 ? (2 * r) & 14 : r;  // V tiles: c ^ (2 r mod 16); K tiles: c ^ r
+    piece_off[i] = r * kRowBytes + ((col ^ swz) & 15) * 16;
   }
 
   // Transposed V reads (ds_read_b64_tr_b16): in each group of 16 lanes, lane
@@ -200,7 +202,7 @@ void chunk_mfma_kernel(DecodeParams P) {
   for (int et = 0; et < 8; ++et) {
     const int r = 4 * rg + col / 4;
     const int dim = 16 * et + 4 * (col % 4);
-    vtr_off[et] = r * kRowBytes + (((dim / 8) ^ r) & 15) * 16 + (dim % 8) * 2;
+    vtr_off[et] = r * kRowBytes + (((dim / 8) ^ ((2 * r) & 14)) & 15) * 16 + (dim % 8) * 2;
   }
 
   // Load logical blocks blk (A, physical ba) and blk + 1 (B, physical bb)
