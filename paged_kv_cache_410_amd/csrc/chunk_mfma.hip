@@ -213,23 +213,32 @@ void chunk_mfma_kernel(DecodeParams P) {
   auto issue = [&](int d, int ba, int bb, int blk, bool ea, bool eb) {
     const bool oka = ba >= 0 && ba < P.NB;
     const bool okb = bb >= 0 && bb < P.NB;
-    bad |= (ea && !oka) || (eb && !okb);
-    const size_t offa = (size_t)(oka ? ba : 0) * block_stride + head_off;
-    const size_t offb = (size_t)(okb ? bb : 0) * block_stride + head_off;
-    // (a block that exists starts inside the workgroup's context: >= 1 row)
-    const int bytes_a = ea && oka ? min(kBlock, ctx_wg - blk * kBlock) * kRowBytes : 0;
-    const int bytes_b = eb && okb ? min(kBlock, ctx_wg - (blk + 1) * kBlock) * kRowBytes : 0;
-    const rsrc_t rka = make_rsrc(kbase + offa, bytes_a);
-    const rsrc_t rkb = make_rsrc(kbase + offb, bytes_b);
-    const rsrc_t rva = make_rsrc(vbase + offa, bytes_a);
-    const rsrc_t rvb = make_rsrc(vbase + offb, bytes_b);
+    bad |= (ea && !oka) || (eb && !okb);  // every wave checks both ids
+    // The descriptor of tile t (0: K of A, 1: K of B, 2: V of A, 3: V of B),
+    // built only for the tiles this wave's pieces belong to. (A block that
+    // exists starts inside the workgroup's context: at least one row.)
+    auto rsrc_of = [&](int t) {
+      const bool second = (t & 1) != 0;
+      const bool ok = second ? okb : oka;
+      const bool ex = second ? eb : ea;
+      const size_t off = (size_t)(ok ? (second ? bb : ba) : 0) * block_stride + head_off;
+      const int bytes = ex && ok ? min(kBlock, ctx_wg - (blk + (second ? 1 : 0)) * kBlock) * kRowBytes
+                                 : 0;
+      return make_rsrc((t >= 2 ? vbase : kbase) + off, bytes);
+    };
     char* dst = slot(d);
+    if constexpr (kPer <= 4) {
+      // all of the wave's pieces lie in one tile: one descriptor
+      const rsrc_t r = rsrc_of((kPer * w) >> 2);
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int q = kPer * w + i;
-      const int t = q >> 2;  // wave-uniform
-      const rsrc_t r = t == 0 ? rka : t == 1 ? rkb : t == 2 ? rva : rvb;
-      ld16_lds<kPolicy>(r, dst + q * kPieceBytes, piece_off[i]);
+      for (int i = 0; i < kPer; ++i)
+        ld16_lds<kPolicy>(r, dst + (kPer * w + i) * kPieceBytes, piece_off[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int q = kPer * w + i;
+        ld16_lds<kPolicy>(rsrc_of(q >> 2), dst + q * kPieceBytes, piece_off[i]);
+      }
     }
   };
 
