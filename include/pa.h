@@ -204,7 +204,8 @@ size_t pa_decode_workspace_bytes(int32_t rows, int32_t Hq, int32_t D,
  *   context_lens   int32 [B], device memory
  *   max_ctx        host-side upper bound on every context_lens[s] (sizes the
  *                  grid without a device-to-host read)
- *   scale          fp32 logit scale (usually 1 / sqrt(D))
+ *   scale          fp32 logit scale (usually 1 / sqrt(D)); any finite value,
+ *                  negative and zero included (NaN or infinity: PA_EINVAL)
  *   partition      tokens per split-context partition: 0 = no split, else a
  *                  positive multiple of bs. With a split, every partition is
  *                  attended independently and a second kernel merges the

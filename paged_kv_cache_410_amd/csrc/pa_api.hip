@@ -149,7 +149,7 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
                     float scale, int32_t partition, void* workspace, size_t workspace_bytes,
                     uint32_t flags, pa_dtype dt, hipStream_t stream) {
   if (B < 0 || rows < 0 || max_q < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || NB < 0 || MB < 0 ||
-      max_ctx < 0 || !dtype_ok(dt) || (flags & ~PA_KV_SHARED) != 0)
+      max_ctx < 0 || !dtype_ok(dt) || (flags & ~PA_KV_SHARED) != 0 || !__builtin_isfinite(scale))
     return PA_EINVAL;
   if (Hq % Hkv != 0) return PA_EINVAL;
   if (partition < 0 || partition % kBs != 0) return PA_EINVAL;

@@ -82,6 +82,8 @@ def decode_args(**kw):
     (dict(partition=16, max_ctx=64), -3),
     (dict(partition=16, max_ctx=64, ws=FAKE, ws_bytes=10), -3),
     (dict(B=70000), -2), (dict(flags=2), -1), (dict(flags=0x80000000), -1),
+    (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1),
+    (dict(scale=float("-inf")), -1),
 ])
 def test_decode_rejects_bad_arguments(palib, kw, status):
     assert palib.lib().pa_decode(*decode_args(**kw)) == status
@@ -106,7 +108,7 @@ def multi_args(**kw):
     (dict(Hq=6, Hkv=4), -1), (dict(partition=8), -1), (dict(D=80), -2), (dict(bs=32), -2),
     (dict(max_q=70000), -2), (dict(B=70000), -2),
     (dict(partition=16, max_ctx=64), -3),
-    (dict(out=FAKE + 4), -1), (dict(flags=4), -1),
+    (dict(out=FAKE + 4), -1), (dict(flags=4), -1), (dict(scale=float("nan")), -1),
 ])
 def test_multi_query_rejects_bad_arguments(palib, kw, status):
     assert palib.lib().pa_multi_query(*multi_args(**kw)) == status
