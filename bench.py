@@ -162,6 +162,7 @@ def cpu_baseline(st_inputs, spec, tb, budget_s):
     what = "the whole" if k_seq == spec.B else f"the first {k_seq} of {spec.B} sequences of the"
     return out, rows, dict(
         value=round(sample_bytes / t / 1e9, 3), unit="GB/s", cores=threads, kind="oracle",
+        host_cpus=os.cpu_count(), omp_num_threads=os.environ.get("OMP_NUM_THREADS"),
         sample=f"{what} {spec.name} step's attention ({spec.Hq} heads; fp64 oracle, OpenMP over "
                f"(query row, head)), median of {len(times)} runs; GB/s on that sample's "
                f"algorithmic bytes",
@@ -269,21 +270,26 @@ def main():
                       out=dest, workspace=workspace, shared_kv=shared)
 
     def step(ev=None):
+        # ev: events before the copies, before the write, before and after the attention
+        if ev is not None:
+            ev[0].record()
         if len(tb.pairs):
             pa.copy_blocks(k_cache, v_cache, pairs)
+        if ev is not None:
+            ev[1].record()
         # slot mapping and the cache write, one launch
         pa.append_kv(k_new, v_new, k_cache, v_cache, bt, step_pos, seq_ids=step_seq,
                      slots_out=slots)
         if ev is not None:
-            ev[0].record()
+            ev[2].record()
         attend(bt, out, shared_kv)
         if ev is not None:
-            ev[1].record()
+            ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4))
            for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps")
     torch.cuda.synchronize()
@@ -292,7 +298,9 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    copy_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    write_ms = [e[1].elapsed_time(e[2]) for e in evs]
     ms_step = wall * 1e3 / args.steps
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     dec_sorted = sorted(dec_ms)
@@ -443,6 +451,8 @@ def main():
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_median": round(dec_med_ms * 1e3, 2),
         "decode_us_p10_p90": [round(dec_p10_ms * 1e3, 2), round(dec_p90_ms * 1e3, 2)],
+        "write_us": round(sum(write_ms) / len(write_ms) * 1e3, 2),
+        "copy_us": round(sum(copy_ms) / len(copy_ms) * 1e3, 2) if len(tb.pairs) else None,
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
