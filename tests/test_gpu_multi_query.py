@@ -53,7 +53,7 @@ CHUNKS = {
 
 
 @pytest.mark.parametrize("name", list(CHUNKS))
-@pytest.mark.parametrize("partition", [None, 0, 16, 64, 512])
+@pytest.mark.parametrize("partition", [None, 0, 16, 48, 64, 512])
 def test_multi_query_matches_oracle(pa, name, partition):
     spec = CHUNKS[name]
     say(f"[multi-query] {name} partition={partition}")
