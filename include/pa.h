@@ -164,6 +164,42 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
                          int32_t bs, pa_dtype dt, hipStream_t stream);
 
 /*
+ * Precondition checks, for debugging a caller. The write, copy and attention
+ * calls take these on trust (their own checks cover the rest); each check
+ * counts the violating entries of its input on the device and writes the
+ * number to count[0] (device memory, int32; 0 = none). Two launches on
+ * `stream`, no allocation; read count[0] after the stream is synchronised.
+ *
+ * pa_check_slots — [P1] section 2: the cache write fills the slots the block
+ * table maps new tokens to, so two tokens of one pa_write_kv / pa_append_kv
+ * call must not share a slot. Counts tokens whose slot is >= 0 and equal to
+ * an earlier token's. Cost O(T^2 / 64) loads.
+ */
+pa_status pa_check_slots(const int32_t* slot_mapping, int32_t T, int32_t* count,
+                         hipStream_t stream);
+
+/*
+ * pa_check_pairs — [P1] section 3: copy-on-write copies of one pa_copy_blocks
+ * call run in parallel, so among pairs with both ids in [0, NB) (the others
+ * are skipped), no destination may repeat and no destination may also be a
+ * source. Counts the pairs whose destination repeats an earlier pair's or is
+ * some pair's source. Cost O(n^2).
+ */
+pa_status pa_check_pairs(const int32_t* pairs, int32_t n, int32_t NB, int32_t* count,
+                         hipStream_t stream);
+
+/*
+ * pa_check_tables — [P1] section 2: attention reads a sequence's first
+ * ceil(L / bs) table entries. Counts the sequences whose context length L is
+ * negative or above min(max_ctx, MB * bs), or one of whose entries below
+ * ceil(L / bs) lies outside [0, NB). (pa_decode returns NaN rows for such
+ * sequences.)
+ */
+pa_status pa_check_tables(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                          int32_t MB, int32_t NB, int32_t max_ctx, int32_t bs, int32_t* count,
+                          hipStream_t stream);
+
+/*
  * pa_decode_default_partition — split-context partition size (tokens) the
  * library would pick for this shape on the current device: 0 (no split) when
  * one workgroup per (sequence, kv head) already fills the GPU, else a

@@ -24,7 +24,8 @@ import torch
 
 from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PA_KV_SHARED, PAError, check, lib  # noqa: F401
 
-__all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "decode", "multi_query", "shares_blocks",
+__all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "check_slots", "check_pairs",
+           "check_tables", "decode", "multi_query", "shares_blocks",
            "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError"]
 
@@ -143,6 +144,45 @@ def append_kv(k_new, v_new, k_cache, v_cache, block_tables, positions, seq_ids=N
                                  positions.data_ptr(), T, B, MB, NB, Hkv, D, bs, _dt(k_cache),
                                  _stream(dev)), "pa_append_kv")
     return slots_out
+
+
+def _count(dev, call, name):
+    count = torch.empty(1, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        check(call(count.data_ptr(), _stream(dev)), name)
+    return int(count.item())          # synchronises
+
+
+def check_slots(slot_mapping):
+    """Tokens of one cache write whose slot repeats an earlier token's (0: none)."""
+    _i32(slot_mapping, "slot_mapping")
+    dev = _dev(slot_mapping)
+    T = slot_mapping.shape[0]
+    return _count(dev, lambda c, st: lib().pa_check_slots(slot_mapping.data_ptr(), T, c, st),
+                  "pa_check_slots")
+
+
+def check_pairs(pairs, num_blocks):
+    """Copy pairs whose destination repeats or is also a source (0: none)."""
+    _i32(pairs, "pairs")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    dev = _dev(pairs)
+    return _count(dev, lambda c, st: lib().pa_check_pairs(pairs.data_ptr(), pairs.shape[0],
+                                                          num_blocks, c, st), "pa_check_pairs")
+
+
+def check_tables(block_tables, context_lens, num_blocks, max_ctx):
+    """Sequences with a length out of bounds or a used table entry outside the pool."""
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    B, MB = block_tables.shape
+    if context_lens.shape != (B,):
+        raise ValueError("context_lens must be [B]")
+    dev = _dev(block_tables, context_lens)
+    return _count(dev, lambda c, st: lib().pa_check_tables(
+        block_tables.data_ptr(), context_lens.data_ptr(), B, MB, num_blocks, max_ctx,
+        BLOCK_SIZE, c, st), "pa_check_tables")
 
 
 def copy_blocks(k_cache, v_cache, pairs):

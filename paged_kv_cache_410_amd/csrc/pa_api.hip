@@ -98,6 +98,32 @@ pa_status pa_append_kv(const void* k_new, const void* v_new, void* k_cache, void
              : PA_EHIP;
 }
 
+pa_status pa_check_slots(const int32_t* slot_mapping, int32_t T, int32_t* count,
+                         hipStream_t stream) {
+  if (T < 0 || !count || (T > 0 && !slot_mapping)) return PA_EINVAL;
+  return pa::launch_check_slots(slot_mapping, T, count, stream) == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+pa_status pa_check_pairs(const int32_t* pairs, int32_t n, int32_t NB, int32_t* count,
+                         hipStream_t stream) {
+  if (n < 0 || NB < 0 || !count || (n > 0 && !pairs)) return PA_EINVAL;
+  return pa::launch_check_pairs(pairs, n, NB, count, stream) == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+pa_status pa_check_tables(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                          int32_t MB, int32_t NB, int32_t max_ctx, int32_t bs, int32_t* count,
+                          hipStream_t stream) {
+  if (B < 0 || MB < 0 || NB < 0 || max_ctx < 0 || !count) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (B > 0 && (!context_lens || (MB > 0 && !block_tables))) return PA_EINVAL;
+  const int64_t cap = (int64_t)MB * kBs;
+  const int32_t limit = (int32_t)(cap < max_ctx ? cap : max_ctx);
+  return pa::launch_check_tables(block_tables, context_lens, B, MB, NB, limit, count, stream) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_EHIP;
+}
+
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n, int32_t NB,
                          int32_t Hkv, int32_t D, int32_t bs, pa_dtype dt, hipStream_t stream) {
   if (n < 0 || NB < 0 || Hkv <= 0 || D <= 0 || !dtype_ok(dt)) return PA_EINVAL;

@@ -77,6 +77,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream);
 
+// Precondition checks: count[0] = number of violating entries (two launches).
+hipError_t launch_check_slots(const int32_t* slots, int32_t T, int32_t* count, hipStream_t stream);
+hipError_t launch_check_pairs(const int32_t* pairs, int32_t n, int32_t NB, int32_t* count,
+                              hipStream_t stream);
+hipError_t launch_check_tables(const int32_t* bt, const int32_t* ctx_lens, int32_t B, int32_t MB,
+                               int32_t NB, int32_t ctx_limit, int32_t* count, hipStream_t stream);
+
 // Query-head groups of up to 16 handled by one MFMA workgroup.
 __host__ __device__ inline int mfma_q_groups(int G) { return (G + 15) / 16; }
 

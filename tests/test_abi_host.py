@@ -162,6 +162,26 @@ def test_cache_ops_reject_bad_arguments(palib):
                             16, 1, None) == 0
 
 
+def test_checks_reject_bad_arguments(palib):
+    # only argument combinations that fail validation: nothing may be launched here
+    lib = palib.lib()
+    # pa_check_slots(slots, T, count, stream)
+    assert lib.pa_check_slots(FAKE, -1, FAKE, None) == -1
+    assert lib.pa_check_slots(None, 3, FAKE, None) == -1
+    assert lib.pa_check_slots(FAKE, 3, None, None) == -1
+    # pa_check_pairs(pairs, n, NB, count, stream)
+    assert lib.pa_check_pairs(FAKE, -1, 10, FAKE, None) == -1
+    assert lib.pa_check_pairs(FAKE, 2, -1, FAKE, None) == -1
+    assert lib.pa_check_pairs(None, 2, 10, FAKE, None) == -1
+    assert lib.pa_check_pairs(FAKE, 2, 10, None, None) == -1
+    # pa_check_tables(bt, cl, B, MB, NB, max_ctx, bs, count, stream)
+    assert lib.pa_check_tables(FAKE, FAKE, 2, 4, 10, 64, 32, FAKE, None) == -2
+    assert lib.pa_check_tables(FAKE, FAKE, 2, 4, 10, 64, 16, None, None) == -1
+    assert lib.pa_check_tables(FAKE, FAKE, -1, 4, 10, 64, 16, FAKE, None) == -1
+    assert lib.pa_check_tables(FAKE, None, 2, 4, 10, 64, 16, FAKE, None) == -1
+    assert lib.pa_check_tables(None, FAKE, 2, 4, 10, 64, 16, FAKE, None) == -1
+
+
 # ------------------------------------------------------- native block manager
 def native_bm(n, bs, order):
     from paged_kv_cache_410_amd import BlockManager

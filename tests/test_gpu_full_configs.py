@@ -50,7 +50,11 @@ def test_full_config(pa, name):
     part = bench_partition(pa, spec, st.q.shape[0], st.max_ctx)
     say(f"[full config] {name}: NB={st.tb.NB} MB={st.tb.MB} T={len(st.tb.slots)} "
         f"pairs={len(st.tb.pairs)} partition={part}")
+    # the generated step respects the preconditions the kernels take on trust
+    assert pa.check_tables(st.block_tables, st.context_lens, st.tb.NB, st.max_ctx) == 0
+    assert pa.check_pairs(st.pairs, st.tb.NB) == 0
     slots = st.run_cache_ops(pa, fused=True)     # the launches bench.py times
+    assert pa.check_slots(slots) == 0
     out = st.multi(pa, partition=part) if spec.chunk else st.decode(pa, partition=part)
     torch.cuda.synchronize()
     assert np.array_equal(slots.cpu().numpy(), st.tb.slots)
