@@ -11,8 +11,9 @@
 // kv head, row-major, cut into tiles of 16, in the column layout of the
 // decode MFMA kernel (S^T = K Q^T on v_mfma_f32_16x16x32_bf16; every
 // accumulator a lane holds belongs to its own column). A workgroup of NW
-// waves owns NW consecutive tiles, one per wave, and each wave keeps its
-// tile's online-softmax state to the end.
+// waves owns NW x TPW consecutive tiles, TPW per wave (one, or two for long
+// chunks, which halves the LDS reads per flop), and each wave keeps its
+// tiles' online-softmax states to the end.
 //
 // The waves stream the partition's K/V blocks, two at a time, through an LDS
 // ring of R slots. A slot holds a pair of blocks A, B: K tiles (4 KiB each)
@@ -51,6 +52,11 @@
 #ifndef PA_CHUNK_MAX_WAVES
 #define PA_CHUNK_MAX_WAVES 8
 #endif
+// Column tiles (16 columns each) per wave for more than 8 tiles per kv
+// head: 2 (on 4 waves) or 1 (on 8 waves).
+#ifndef PA_CHUNK_TILES_PER_WAVE
+#define PA_CHUNK_TILES_PER_WAVE 2
+#endif
 
 namespace pa {
 
@@ -82,12 +88,13 @@ __device__ __forceinline__ void ring_barrier() {
 
 }  // namespace
 
-template <int NW, int R, TilePolicy kPolicy>
+template <int NW, int R, int TPW, TilePolicy kPolicy>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(TPW > 1 ? 3 : NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
 void chunk_mfma_kernel(DecodeParams P) {
   static_assert(kPieces % NW == 0, "pieces must divide over the waves");
   static_assert(R >= 3 && R <= 4, "ring of 3 or 4 slots");
+  static_assert(TPW == 1 || TPW == 2, "one or two column tiles per wave");
   constexpr int kPer = kPieces / NW;  // load instructions per wave per pair
   // One LDS object per slot, so that the compiler's load counting tells the
   // slots apart and waits only for the slot it reads.
@@ -106,12 +113,13 @@ void chunk_mfma_kernel(DecodeParams P) {
 
   // Workgroups per (kv head, partition, sequence); those of one such triple
   // read the same K/V and are kept on one XCD.
-  const int groups = (P.n_tiles + NW - 1) / NW;
+  constexpr int kTilesPerWg = NW * TPW;
+  const int groups = (P.n_tiles + kTilesPerWg - 1) / kTilesPerWg;
   const GridPos gp = grid_pos_grouped(groups);
   const int p = gp.y;
   const int s = gp.z;
-  const int g = gp.x / groups;             // kv head
-  const int tile0 = (gp.x % groups) * NW;  // the workgroup's first tile
+  const int g = gp.x / groups;                     // kv head
+  const int tile0 = (gp.x % groups) * kTilesPerWg;  // the workgroup's first tile
 
   const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
@@ -120,19 +128,13 @@ void chunk_mfma_kernel(DecodeParams P) {
       first_chunk_ids(bt_row, blk_begin, 1, bpp > 0 ? min(P.MB, blk_begin + bpp) : P.MB, lane);
   const SeqRows sr = seq_rows(P, s);
 
-  // Columns: global column gc of the n x G grid, row-major; gc >= n G is padding.
+  // Columns: global column gc of the n x G grid, row-major; gc >= n G is
+  // padding. Wave w owns tiles tile0 + TPW w + t, t < TPW.
   const int ncols = min(sr.n, P.max_q) * P.G;
   const int wg_begin = 16 * tile0;
   if (wg_begin >= ncols) return;  // the whole workgroup is padding
-  const int wg_end = min(ncols, wg_begin + 16 * NW);
-  const int c_begin = 16 * (tile0 + w);
-  const bool has_cols = c_begin < ncols;  // else the wave only loads (wave-uniform)
-  const int c_end = has_cols ? min(ncols, c_begin + 16) : wg_end;
-  const int gc = c_begin + col;
-  const bool col_ok = has_cols && gc < c_end;
-  const int gcl = col_ok ? gc : c_end - 1;  // padded lanes shadow a real column
-  const int qi = gcl / P.G;
-  const int qh = g * P.G + gcl % P.G;
+  const int wg_end = min(ncols, wg_begin + 16 * kTilesPerWg);
+  const bool has_cols = 16 * (tile0 + TPW * w) < ncols;  // else the wave only loads (wave-uniform)
 
   // The logit scale (log2 domain) is applied in the exponent, after the max
   // is taken over the raw products, which needs it non-negative: a negative
@@ -141,35 +143,55 @@ void chunk_mfma_kernel(DecodeParams P) {
   const bool q_neg = P.qscale < 0.0f;
   const float qs = fmaxf(fabsf(P.qscale), 1e-30f);
 
-  // B operand of S^T: Q[column col][32 kk + 8 rg ..], zero for padded columns.
-  bf16x8_t qop[4];
-  if (has_cols) {
-    const char* qp =
-        reinterpret_cast<const char*>(P.q) + ((size_t)(sr.first + qi) * P.Hq + qh) * kRowBytes;
-    const uint32_t flip = q_neg ? 0x80008000u : 0u;
+  // Per tile: this lane's column (padded lanes, and all lanes of a tile past
+  // the last column, shadow a real column and carry a zero query), its
+  // causal context, the tile's shortest context, and the B operand of S^T,
+  // Q[column col][32 kk + 8 rg ..].
+  int gc[TPW], ctx_col[TPW], ctx_min[TPW];
+  bool col_ok[TPW];
+  bf16x8_t qop[TPW][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint4 u = ld16(qp + (32 * kk + 8 * rg) * 2);
-      u = make_uint4(u.x ^ flip, u.y ^ flip, u.z ^ flip, u.w ^ flip);
-      if (!col_ok) u = make_uint4(0, 0, 0, 0);
-      qop[kk] = __builtin_bit_cast(bf16x8_t, u);
+  for (int t = 0; t < TPW; ++t) {
+    const int cb = 16 * (tile0 + TPW * w + t);
+    const bool tile_ok = cb < ncols;
+    const int ce = tile_ok ? min(ncols, cb + 16) : wg_end;
+    gc[t] = cb + col;
+    col_ok[t] = tile_ok && gc[t] < ce;
+    const int gcl = col_ok[t] ? gc[t] : ce - 1;
+    const int qi = gcl / P.G;
+    const int qh = g * P.G + gcl % P.G;
+    ctx_col[t] = sr.row_ctx(qi);
+    ctx_min[t] = sr.row_ctx((tile_ok ? cb : ce - 1) / P.G);
+    if (has_cols) {
+      const char* qp =
+          reinterpret_cast<const char*>(P.q) + ((size_t)(sr.first + qi) * P.Hq + qh) * kRowBytes;
+      const uint32_t flip = q_neg ? 0x80008000u : 0u;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint4 u = ld16(qp + (32 * kk + 8 * rg) * 2);
+        u = make_uint4(u.x ^ flip, u.y ^ flip, u.z ^ flip, u.w ^ flip);
+        if (!col_ok[t]) u = make_uint4(0, 0, 0, 0);
+        qop[t][kk] = __builtin_bit_cast(bf16x8_t, u);
+      }
     }
   }
 
-  // Contexts: each column's causal prefix; the wave's shortest and longest;
-  // the workgroup's longest (what the ring streams).
-  const int ctx_col = sr.row_ctx(qi);
-  const int ctx_min = sr.row_ctx(c_begin / P.G);
+  // The workgroup's longest context: what the ring streams.
   const int ctx_wg = sr.row_ctx((wg_end - 1) / P.G);
   const int nblk = (ctx_wg + kBlock - 1) / kBlock;
   const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
   const int nparts_wg = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
   if (p >= max(nparts_wg, 1)) return;  // partition past the workgroup's contexts
 
-  float m = -INFINITY, lsum = 0.0f;
-  f32x4_t acc[8];
+  float m[TPW], lsum[TPW];
+  f32x4_t acc[TPW][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < TPW; ++t) {
+    m[t] = -INFINITY;
+    lsum[t] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[t][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   bool bad = sr.bad;
 
   const char* kbase = reinterpret_cast<const char*>(P.k_cache);
@@ -242,81 +264,102 @@ void chunk_mfma_kernel(DecodeParams P) {
     }
   };
 
-  // One pair of blocks: S^T of both (lane (rg, col) holds tokens 4 rg + 0..3
-  // of each, column col), the online softmax over their 32 tokens, then
-  // O^T += V^T P^T as one K = 32 contraction: contraction slots 8 rg + 0..3
-  // are block A's tokens 4 rg + 0..3 and slots 8 rg + 4..7 block B's, so a
-  // lane's own probabilities are its B operand as they stand.
+  // One pair of blocks, for each of the wave's tiles: S^T of both blocks
+  // (lane (rg, col) holds tokens 4 rg + 0..3 of each, column col), the
+  // online softmax over their 32 tokens, then O^T += V^T P^T as one K = 32
+  // contraction: contraction slots 8 rg + 0..3 are block A's tokens
+  // 4 rg + 0..3 and slots 8 rg + 4..7 block B's, so a lane's own
+  // probabilities are its B operand as they stand. The K and V operands are
+  // read once for all the wave's tiles.
   auto consume = [&](int d, int blk, bool b_live) {
     const char* src = slot(d);
-    f32x4_t sa = {0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4_t sb = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t sa[TPW], sb[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      sa[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      sb[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int o = col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16;
-      const uint4 ka = *reinterpret_cast<const uint4*>(src + o);
-      const uint4 kb = *reinterpret_cast<const uint4*>(src + kTileBytes + o);
-      sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], sa,
-                                                  0, 0, 0);
-      sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qop[kk], sb,
-                                                  0, 0, 0);
+      const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + o));
+      const bf16x8_t kb =
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + kTileBytes + o));
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[t][kk], sa[t], 0, 0, 0);
+        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[t][kk], sb[t], 0, 0, 0);
+      }
     }
     // The V operands, read transposed from LDS now so that their latency
     // passes under the softmax: the A operand of lane (rg, col) for output
     // tile et is V_A[4 rg + 0..3][16 et + col] then V_B[4 rg + 0..3][16 et + col].
+    // (With two tiles per wave the registers are short: each operand is then
+    // read just before its MFMAs.)
     typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-    bf16x8_t vop[8];
-#pragma unroll
-    for (int et = 0; et < 8; ++et) {
+    auto v_operand = [&](int et) {
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 2 * kTileBytes + vtr_off[et]));
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 3 * kTileBytes + vtr_off[et]));
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-      vop[et] = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-    }
-    // Raw logits; those past a column's causal limit, and all of block B when
-    // it lies past the partition, are removed (wave-uniform test first).
-    float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-    if (blk * kBlock + 2 * kBlock > ctx_min || !b_live) {
-      const int tok0 = blk * kBlock + 4 * rg;
+      return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+    };
+    constexpr int kEarly = TPW == 1 ? 8 : 1;
+    bf16x8_t vop[kEarly];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tok0 + i >= ctx_col) x[i] = -INFINITY;
-        if (!b_live || tok0 + kBlock + i >= ctx_col) x[4 + i] = -INFINITY;
+    for (int et = 0; et < kEarly; ++et) vop[et] = v_operand(et);
+    bf16x8_t pop[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      // Raw logits; those past a column's causal limit, and all of block B
+      // when it lies past the partition, are removed (wave-uniform test).
+      float x[8] = {sa[t][0], sa[t][1], sa[t][2], sa[t][3],
+                    sb[t][0], sb[t][1], sb[t][2], sb[t][3]};
+      if (blk * kBlock + 2 * kBlock > ctx_min[t] || !b_live) {
+        const int tok0 = blk * kBlock + 4 * rg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (tok0 + i >= ctx_col[t]) x[i] = -INFINITY;
+          if (!b_live || tok0 + kBlock + i >= ctx_col[t]) x[4 + i] = -INFINITY;
+        }
       }
+      const float m8 = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      const float mx = rows_max(m8) * qs;  // -inf stays -inf (qs > 0)
+      // The reference m (what the probabilities are taken relative to)
+      // moves only when a column's max passes it by more than kLazy: the
+      // probabilities then stay below 2^kLazy, the result is the same up to
+      // rounding, and the accumulators are rescaled a few times per column
+      // instead of whenever its max creeps up.
+      constexpr float kLazy = 8.0f;
+      const float m_new = fmaxf(m[t], mx);
+      const bool up = m_new > m[t] + kLazy;  // from -inf: any finite max
+      const float ref = up ? m_new : m[t];
+      const float ref_use = (ref == -INFINITY) ? 0.0f : ref;
+      const float alpha = exp2_fast(m[t] - ref_use);  // exactly 1 where the reference stays
+      float pr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
+      lsum[t] = lsum[t] * alpha +
+                (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+      m[t] = ref;
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[t][e] *= alpha;
+      }
+      pop[t] = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                               pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
     }
-    const float m8 = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    const float mx = rows_max(m8) * qs;  // -inf stays -inf (qs > 0)
-    // The reference m (what the probabilities are taken relative to) moves
-    // only when a column's max passes it by more than kLazy: the
-    // probabilities then stay below 2^kLazy, the result is the same up to
-    // rounding, and the accumulators are rescaled a few times per column
-    // instead of whenever its max creeps up.
-    constexpr float kLazy = 8.0f;
-    const float m_new = fmaxf(m, mx);
-    const bool up = m_new > m + kLazy;  // from -inf: any finite max
-    const float ref = up ? m_new : m;
-    const float ref_use = (ref == -INFINITY) ? 0.0f : ref;
-    const float alpha = exp2_fast(m - ref_use);  // exactly 1 where the reference stays
-    float pr[8];
+    // O^T tile et (dims 16 et + m) += V^T P^T, for each of the wave's tiles.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
-    lsum = lsum * alpha +
-           (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-    m = ref;
-    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+    for (int et = 0; et < 8; ++et) {
+      const bf16x8_t v = et < kEarly ? vop[et < kEarly ? et : 0] : v_operand(et);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      for (int t = 0; t < TPW; ++t)
+        acc[t][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop[t], acc[t][et], 0, 0, 0);
     }
-    const bf16x8_t pop = __builtin_bit_cast(
-        bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                             pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
-    // O^T tile et (dims 16 et + m) += V^T P^T.
-#pragma unroll
-    for (int et = 0; et < 8; ++et)
-      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], pop, acc[et], 0, 0, 0);
   };
 
   // The ring: pair j (blocks 2 j, 2 j + 1 of the partition's range) sits in
@@ -356,61 +399,69 @@ void chunk_mfma_kernel(DecodeParams P) {
   }
 
   if (!has_cols) return;
-  lsum = rows_sum(lsum);  // per column: sum over the 4 row groups
-
-  // The wave holds its columns' whole state for this partition: lane
-  // (rg, col) writes dims 16 et + 4 rg + 0..3 of column col, from acc[et]
-  // (et = 0..7).
-  if (!col_ok) return;
-  const int i = gc / P.G;
-  const int h = g * P.G + gc % P.G;
-  const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
-  const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
-  if (np <= 1 ? p != 0 : p >= np) return;  // this column has no such partition
-  const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
+  // Each tile's columns hold their whole state for this partition: lane
+  // (rg, col) writes dims 16 et + 4 rg + 0..3 of its column, from acc[t][et].
   const float nan = __builtin_nanf("");
-  if (np > 1) {
-    const size_t part = orow * P.n_parts + p;
-    float* dst = P.ws_o + part * kD;
 #pragma unroll
-    for (int et = 0; et < 8; ++et)
-      *reinterpret_cast<float4*>(dst + 16 * et + 4 * rg) =
-          bad ? make_float4(nan, nan, nan, nan)
-              : make_float4(acc[et][0], acc[et][1], acc[et][2], acc[et][3]);
-    if (rg == 0) {
-      P.ws_ml[2 * part] = bad ? 0.0f : m;
-      P.ws_ml[2 * part + 1] = bad ? nan : lsum;
-    }
-  } else {
-    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  for (int t = 0; t < TPW; ++t) {
+    const float l_col = rows_sum(lsum[t]);  // per column: sum over the 4 row groups
+    if (!col_ok[t]) continue;
+    const int i = gc[t] / P.G;
+    const int h = g * P.G + gc[t] % P.G;
+    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
+    const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
+    if (np <= 1 ? p != 0 : p >= np) continue;  // this column has no such partition
+    const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
+    if (np > 1) {
+      const size_t part = orow * P.n_parts + p;
+      float* dst = P.ws_o + part * kD;
 #pragma unroll
-    for (int et = 0; et < 8; ++et) {
-      float res[4];
+      for (int et = 0; et < 8; ++et)
+        *reinterpret_cast<float4*>(dst + 16 * et + 4 * rg) =
+            bad ? make_float4(nan, nan, nan, nan)
+                : make_float4(acc[t][et][0], acc[t][et][1], acc[t][et][2], acc[t][et][3]);
+      if (rg == 0) {
+        P.ws_ml[2 * part] = bad ? 0.0f : m[t];
+        P.ws_ml[2 * part + 1] = bad ? nan : l_col;
+      }
+    } else {
+      const float inv = l_col > 0.0f ? 1.0f / l_col : 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) res[e] = bad ? nan : acc[et][e] * inv;
-      *reinterpret_cast<uint2*>(reinterpret_cast<char*>(P.out) +
-                                (orow * kD + 16 * et + 4 * rg) * 2) =
-          make_uint2(pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]));
+      for (int et = 0; et < 8; ++et) {
+        float res[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = bad ? nan : acc[t][et][e] * inv;
+        *reinterpret_cast<uint2*>(reinterpret_cast<char*>(P.out) +
+                                  (orow * kD + 16 * et + 4 * rg) * 2) =
+            make_uint2(pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]));
+      }
     }
   }
 }
 
-// Waves per workgroup: as many as the kv head has tiles, up to 8 (a wave
-// without columns still brings its share of every block).
+// Waves per workgroup and column tiles per wave. Up to 8 tiles per kv
+// head: one tile per wave, as many waves as tiles (a wave without columns
+// still brings its share of every block). More: two tiles per wave on 4
+// waves, so that every K/V operand read from LDS serves 32 columns (with
+// PA_CHUNK_TILES_PER_WAVE 1, one tile per wave on 8 waves).
 hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int R = PA_CHUNK_RING;
-  auto go = [&](auto nw) {
+  auto go = [&](auto nw, auto tpw) {
     constexpr int NW = decltype(nw)::value;
-    const dim3 grid(p.Hkv * ((p.n_tiles + NW - 1) / NW), p.n_parts, p.B);
-    hipLaunchKernelGGL((chunk_mfma_kernel<NW, R, TilePolicy::kShared>), grid, dim3(NW * kWave), 0,
-                       stream, p);
+    constexpr int TPW = decltype(tpw)::value;
+    const dim3 grid(p.Hkv * ((p.n_tiles + NW * TPW - 1) / (NW * TPW)), p.n_parts, p.B);
+    hipLaunchKernelGGL((chunk_mfma_kernel<NW, R, TPW, TilePolicy::kShared>), grid,
+                       dim3(NW * kWave), 0, stream, p);
   };
+  using I = std::integral_constant<int, 1>;
   if (p.n_tiles <= 2 || PA_CHUNK_MAX_WAVES == 2)
-    go(std::integral_constant<int, 2>{});
+    go(std::integral_constant<int, 2>{}, I{});
   else if (p.n_tiles <= 4 || PA_CHUNK_MAX_WAVES == 4)
-    go(std::integral_constant<int, 4>{});
+    go(std::integral_constant<int, 4>{}, I{});
+  else if (p.n_tiles <= 8 || PA_CHUNK_TILES_PER_WAVE == 1)
+    go(std::integral_constant<int, 8>{}, I{});
   else
-    go(std::integral_constant<int, 8>{});
+    go(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
   return hipGetLastError();
 }
 
