@@ -52,6 +52,10 @@
 #ifndef PA_CHUNK_MAX_WAVES
 #define PA_CHUNK_MAX_WAVES 8
 #endif
+// V operands read before the softmax with two tiles per wave (registers).
+#ifndef PA_CHUNK_TPW2_EARLY
+#define PA_CHUNK_TPW2_EARLY 1
+#endif
 // Column tiles (16 columns each) per wave for more than 8 tiles per kv
 // head: 2 (on 4 waves) or 1 (on 8 waves).
 #ifndef PA_CHUNK_TILES_PER_WAVE
@@ -305,7 +309,7 @@ void chunk_mfma_kernel(DecodeParams P) {
       const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
       return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
     };
-    constexpr int kEarly = TPW == 1 ? 8 : 1;
+    constexpr int kEarly = TPW == 1 ? 8 : PA_CHUNK_TPW2_EARLY;
     bf16x8_t vop[kEarly];
 #pragma unroll
     for (int et = 0; et < kEarly; ++et) vop[et] = v_operand(et);
