@@ -52,9 +52,23 @@
 #ifndef PA_CHUNK_MAX_WAVES
 #define PA_CHUNK_MAX_WAVES 8
 #endif
-// V operands read before the softmax with two tiles per wave (registers).
-#ifndef PA_CHUNK_TPW2_EARLY
-#define PA_CHUNK_TPW2_EARLY 1
+// Two-tile step laid out as a pipeline (1: softmax of one tile between the
+// other's MFMAs; needs registers for 2 waves per SIMD) or in plain order (0).
+#ifndef PA_CHUNK_TPW2_PIPELINE
+#define PA_CHUNK_TPW2_PIPELINE 0
+#endif
+// Both tiles' softmax before one joint rescale branch (1) or each tile's
+// softmax and rescale in turn (0).
+#ifndef PA_CHUNK_TPW2_JOINT
+#define PA_CHUNK_TPW2_JOINT 1
+#endif
+// Waves per SIMD the two-tile kernel's registers are sized for (2 or 3).
+#ifndef PA_CHUNK_TPW2_WAVES
+#define PA_CHUNK_TPW2_WAVES (PA_CHUNK_TPW2_PIPELINE ? 2 : 3)
+#endif
+// Vector ALU instructions scheduled after each MFMA in the two-tile step.
+#ifndef PA_CHUNK_VALU_PER_MFMA
+#define PA_CHUNK_VALU_PER_MFMA 6
 #endif
 // Column tiles (16 columns each) per wave for more than 8 tiles per kv
 // head: 2 (on 4 waves) or 1 (on 8 waves).
@@ -72,6 +86,10 @@ constexpr int kTileBytes = kBlock * kRowBytes;      // one K or V tile of one bl
 constexpr int kSlotBytes = 4 * kTileBytes;          // a pair of blocks: K A, K B, V A, V B
 constexpr int kPieceBytes = kWave * 16;             // one load instruction
 constexpr int kPieces = kSlotBytes / kPieceBytes;   // per pair
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;    // vector ALU, MFMA excluded
+constexpr int kSchedMfma = 0x008;
 
 // s_waitcnt bounding only the vector memory count (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
@@ -94,7 +112,7 @@ __device__ __forceinline__ void ring_barrier() {
 
 template <int NW, int R, int TPW, TilePolicy kPolicy>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(TPW > 1 ? 3 : NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(TPW > 1 ? PA_CHUNK_TPW2_WAVES : NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
 void chunk_mfma_kernel(DecodeParams P) {
   static_assert(kPieces % NW == 0, "pieces must divide over the waves");
   static_assert(R >= 3 && R <= 4, "ring of 3 or 4 slots");
@@ -268,14 +286,117 @@ void chunk_mfma_kernel(DecodeParams P) {
     }
   };
 
-  // One pair of blocks, for each of the wave's tiles: S^T of both blocks
-  // (lane (rg, col) holds tokens 4 rg + 0..3 of each, column col), the
-  // online softmax over their 32 tokens, then O^T += V^T P^T as one K = 32
-  // contraction: contraction slots 8 rg + 0..3 are block A's tokens
+  // Transposed V operand of output tile et from slot src: the A operand of
+  // lane (rg, col) is V_A[4 rg + 0..3][16 et + col] then
+  // V_B[4 rg + 0..3][16 et + col].
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  auto v_operand = [&](const char* src, int et) {
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 2 * kTileBytes + vtr_off[et]));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 3 * kTileBytes + vtr_off[et]));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+  };
+
+  // Logits of tile t past the column's causal limit, and all of block B
+  // when it lies past the partition, removed (lane (rg, col): tokens
+  // 4 rg + 0..3 of each block).
+  auto mask_logits = [&](int t, float (&x)[8], int blk, bool b_live) {
+    const int tok0 = blk * kBlock + 4 * rg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (tok0 + i >= ctx_col[t]) x[i] = -INFINITY;
+      if (!b_live || tok0 + kBlock + i >= ctx_col[t]) x[4 + i] = -INFINITY;
+    }
+  };
+  // The online softmax of tile t over one pair of blocks, from its raw
+  // logits x (S^T of block A, then of block B): updates the tile's reference
+  // m and sum, and gives the probabilities as the bf16 B operand of the PV
+  // product with the factor alpha that takes the accumulators to the new
+  // reference.
+  struct Probs {
+    bf16x8_t pop;
+    float alpha;
+    bool up;
+  };
+  auto lane_max = [](const float (&x)[8]) {
+    return vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])), vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
+  };
+  // col_max: the column's largest raw logit over the pair (all 4 row groups).
+  auto softmax_with = [&](int t, const float (&x)[8], float col_max) -> Probs {
+    const float mx = col_max * qs;  // -inf stays -inf (qs > 0)
+    // The reference m (what the probabilities are taken relative to) moves
+    // only when a column's max passes it by more than kLazy: the
+    // probabilities then stay below 2^kLazy, the result is the same up to
+    // rounding, and the accumulators are rescaled a few times per column
+    // instead of whenever its max creeps up.
+    constexpr float kLazy = 8.0f;
+    const float m_new = vmax(m[t], mx);
+    const bool up = m_new > m[t] + kLazy;  // from -inf: any finite max
+    const float ref = up ? m_new : m[t];
+    const float ref_use = (ref == -INFINITY) ? 0.0f : ref;
+    const float alpha = exp2_fast(m[t] - ref_use);  // exactly 1 where the reference stays
+    float pr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
+    m[t] = ref;
+    const uint4 w4 = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
+    // The sum takes the probabilities as rounded for the PV product (a dot
+    // product of each bf16 pair with (1, 1)): numerator and denominator see
+    // the same values, in 4 instructions instead of 8.
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float l = lsum[t] * alpha;
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.x), ones, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.y), ones, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.z), ones, l, false);
+    l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.w), ones, l, false);
+    lsum[t] = l;
+    return {__builtin_bit_cast(bf16x8_t, w4), alpha, up};
+  };
+  auto softmax = [&](int t, const float (&x)[8]) {
+    return softmax_with(t, x, rows_vmax(lane_max(x)));
+  };
+  // Raw logits of tile t (S^T of blocks A and B), masked where kMask (a
+  // wave-uniform bool, or a constant type) says the pair needs it.
+  auto logits = [&](int t, const f32x4_t& sa, const f32x4_t& sb, int blk, bool b_live, auto kMask,
+                    float (&x)[8]) {
+    const float v[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = v[i];
+    if (static_cast<bool>(kMask)) mask_logits(t, x, blk, b_live);
+  };
+  // Pins the probabilities in registers at this point: otherwise the
+  // compiler sinks their exponentials past the rescale branch below, into
+  // the block of the PV products, and the pipeline's stages merge.
+  auto pin = [](Probs& pr) {
+    uint4 u = __builtin_bit_cast(uint4, pr.pop);
+    asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
+    pr.pop = __builtin_bit_cast(bf16x8_t, u);
+  };
+  // The accumulators of tile t to the new reference, where any column's moved.
+  auto rescale = [&](int t, const Probs& pr) {
+    if (__builtin_amdgcn_ballot_w64(pr.up) != 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[t][e] *= pr.alpha;
+    }
+  };
+
+  // One pair of blocks in slot d, for each of the wave's tiles: S^T of both
+  // blocks (lane (rg, col) holds tokens 4 rg + 0..3 of each, column col),
+  // the online softmax over their 32 tokens, then O^T += V^T P^T as one
+  // K = 32 contraction: contraction slots 8 rg + 0..3 are block A's tokens
   // 4 rg + 0..3 and slots 8 rg + 4..7 block B's, so a lane's own
   // probabilities are its B operand as they stand. The K and V operands are
   // read once for all the wave's tiles.
-  auto consume = [&](int d, int blk, bool b_live) {
+  //
+  // The matrix cores and the vector ALU run side by side only where one
+  // wave's instruction stream alternates between them (it issues in order),
+  // so with two tiles the step is laid out as a pipeline: tile 0's softmax
+  // goes between tile 1's QK products, tile 1's softmax between tile 0's PV
+  // products (the scheduling group barriers below fix that interleave).
+  auto consume_pair = [&](int d, int blk, bool b_live, auto kMask) {
     const char* src = slot(d);
     f32x4_t sa[TPW], sb[TPW];
 #pragma unroll
@@ -283,86 +404,128 @@ void chunk_mfma_kernel(DecodeParams P) {
       sa[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       sb[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // K operands, each read once for the wave's tiles; in the pipeline,
+    // tile 0's products come first.
+    constexpr bool kTileMajor = TPW == 2 && PA_CHUNK_TPW2_PIPELINE;
+    bf16x8_t ka[4], kb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int o = col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16;
-      const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + o));
-      const bf16x8_t kb =
-          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + kTileBytes + o));
+      ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + o));
+      kb[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + kTileBytes + o));
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[t][kk], sa[t], 0, 0, 0);
-        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[t][kk], sb[t], 0, 0, 0);
+      for (int t = 0; t < (kTileMajor ? 1 : TPW); ++t) {
+        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[t][kk], sa[t], 0, 0, 0);
+        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qop[t][kk], sb[t], 0, 0, 0);
       }
     }
-    // The V operands, read transposed from LDS now so that their latency
-    // passes under the softmax: the A operand of lane (rg, col) for output
-    // tile et is V_A[4 rg + 0..3][16 et + col] then V_B[4 rg + 0..3][16 et + col].
-    // (With two tiles per wave the registers are short: each operand is then
-    // read just before its MFMAs.)
-    typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-    auto v_operand = [&](int et) {
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 2 * kTileBytes + vtr_off[et]));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(__attribute__((address_space(3))) char*)(src + 3 * kTileBytes + vtr_off[et]));
-      const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-      return __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
-    };
-    constexpr int kEarly = TPW == 1 ? 8 : PA_CHUNK_TPW2_EARLY;
-    bf16x8_t vop[kEarly];
+    if constexpr (kTileMajor) {
 #pragma unroll
-    for (int et = 0; et < kEarly; ++et) vop[et] = v_operand(et);
-    bf16x8_t pop[TPW];
+      for (int kk = 0; kk < 4; ++kk) {
+        sa[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[1][kk], sa[1], 0, 0, 0);
+        sb[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qop[1][kk], sb[1], 0, 0, 0);
+      }
+    }
+    if constexpr (TPW == 1) {
+      // V operands read now, so that their latency passes under the softmax.
+      bf16x8_t vop[8];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      // Raw logits; those past a column's causal limit, and all of block B
-      // when it lies past the partition, are removed (wave-uniform test).
-      float x[8] = {sa[t][0], sa[t][1], sa[t][2], sa[t][3],
-                    sb[t][0], sb[t][1], sb[t][2], sb[t][3]};
-      if (blk * kBlock + 2 * kBlock > ctx_min[t] || !b_live) {
-        const int tok0 = blk * kBlock + 4 * rg;
+      for (int et = 0; et < 8; ++et) vop[et] = v_operand(src, et);
+      float x0[8];
+      logits(0, sa[0], sb[0], blk, b_live, kMask, x0);
+      const Probs p0 = softmax(0, x0);
+      rescale(0, p0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (tok0 + i >= ctx_col[t]) x[i] = -INFINITY;
-          if (!b_live || tok0 + kBlock + i >= ctx_col[t]) x[4 + i] = -INFINITY;
+      for (int et = 0; et < 8; ++et)
+        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p0.pop, acc[0][et], 0, 0, 0);
+    } else if constexpr (!PA_CHUNK_TPW2_PIPELINE) {
+      // Both softmaxes, then each V operand read just before its two MFMAs
+      // (registers are short with two tiles).
+#if PA_CHUNK_TPW2_JOINT
+      // Both tiles' softmax in one block (their dependency chains overlap),
+      // then one branch rescales both where either's reference moved (the
+      // other's alpha is then exactly 1).
+      float x0[8], x1[8];
+      logits(0, sa[0], sb[0], blk, false, std::false_type{}, x0);
+      logits(1, sa[1], sb[1], blk, false, std::false_type{}, x1);
+      if (static_cast<bool>(kMask)) {  // one branch for both tiles
+        mask_logits(0, x0, blk, b_live);
+        mask_logits(1, x1, blk, b_live);
+      }
+      float cm0, cm1;
+      rows_vmax2(lane_max(x0), lane_max(x1), cm0, cm1);
+      const Probs p0 = softmax_with(0, x0, cm0);
+      const Probs p1 = softmax_with(1, x1, cm1);
+      if (__builtin_amdgcn_ballot_w64(p0.up || p1.up) != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc[0][e] *= p0.alpha;
+          acc[1][e] *= p1.alpha;
         }
       }
-      const float m8 = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      const float mx = rows_max(m8) * qs;  // -inf stays -inf (qs > 0)
-      // The reference m (what the probabilities are taken relative to)
-      // moves only when a column's max passes it by more than kLazy: the
-      // probabilities then stay below 2^kLazy, the result is the same up to
-      // rounding, and the accumulators are rescaled a few times per column
-      // instead of whenever its max creeps up.
-      constexpr float kLazy = 8.0f;
-      const float m_new = fmaxf(m[t], mx);
-      const bool up = m_new > m[t] + kLazy;  // from -inf: any finite max
-      const float ref = up ? m_new : m[t];
-      const float ref_use = (ref == -INFINITY) ? 0.0f : ref;
-      const float alpha = exp2_fast(m[t] - ref_use);  // exactly 1 where the reference stays
-      float pr[8];
+#else
+      float x0[8], x1[8];
+      logits(0, sa[0], sb[0], blk, b_live, kMask, x0);
+      const Probs p0 = softmax(0, x0);
+      rescale(0, p0);
+      logits(1, sa[1], sb[1], blk, b_live, kMask, x1);
+      const Probs p1 = softmax(1, x1);
+      rescale(1, p1);
+#endif
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
-      lsum[t] = lsum[t] * alpha +
-                (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-      m[t] = ref;
-      if (__builtin_amdgcn_ballot_w64(up) != 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[t][e] *= alpha;
+      for (int et = 0; et < 8; ++et) {
+        const bf16x8_t v = v_operand(src, et);
+        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p0.pop, acc[0][et], 0, 0, 0);
+        acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p1.pop, acc[1][et], 0, 0, 0);
       }
-      pop[t] = __builtin_bit_cast(
-          bf16x8_t, make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                               pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])));
+    } else {
+      float x0[8], x1[8];
+      logits(0, sa[0], sb[0], blk, b_live, kMask, x0);
+      Probs p0 = softmax(0, x0);
+      bf16x8_t vop[8];
+#pragma unroll
+      for (int et = 0; et < 8; ++et) vop[et] = v_operand(src, et);
+      // Tile 0's QK products, then each of tile 1's with a share of tile
+      // 0's softmax; the V reads go in the second half, as K operands die.
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, PA_CHUNK_VALU_PER_MFMA, 0);
+      }
+      pin(p0);
+      rescale(0, p0);
+      logits(1, sa[1], sb[1], blk, b_live, kMask, x1);
+      Probs p1 = softmax(1, x1);
+#pragma unroll
+      for (int et = 0; et < 8; ++et)
+        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p0.pop, acc[0][et], 0, 0, 0);
+      // Each of tile 0's PV products with a share of tile 1's softmax.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, PA_CHUNK_VALU_PER_MFMA, 0);
+      }
+      pin(p1);
+      rescale(1, p1);
+#pragma unroll
+      for (int et = 0; et < 8; ++et)
+        acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p1.pop, acc[1][et], 0, 0, 0);
     }
-    // O^T tile et (dims 16 et + m) += V^T P^T, for each of the wave's tiles.
+  };
+  // Steps whose pair reaches a column's causal limit, or whose block B is
+  // past the partition, take the masked form (wave-uniform); with two tiles
+  // the whole step is duplicated, so that no branch cuts its pipeline.
+  auto consume = [&](int d, int blk, bool b_live) {
+    bool edge = !b_live;
 #pragma unroll
-    for (int et = 0; et < 8; ++et) {
-      const bf16x8_t v = et < kEarly ? vop[et < kEarly ? et : 0] : v_operand(et);
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-        acc[t][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop[t], acc[t][et], 0, 0, 0);
+    for (int t = 0; t < TPW; ++t) edge |= blk * kBlock + 2 * kBlock > ctx_min[t];
+    if constexpr (TPW == 1 || !PA_CHUNK_TPW2_PIPELINE) {
+      consume_pair(d, blk, b_live, edge);  // a branch inside the softmax
+    } else if (edge) {
+      consume_pair(d, blk, b_live, std::true_type{});
+    } else {
+      consume_pair(d, blk, true, std::false_type{});
     }
   };
 

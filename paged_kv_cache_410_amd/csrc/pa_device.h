@@ -99,6 +99,32 @@ __device__ __forceinline__ float rows_max(float x) {
   p = pair32(x);
   return fmaxf(p.a, p.b);
 }
+// NaN-propagating maximum: v_maximum3_f32, with no quieting of the inputs
+// first (fmaxf spends one v_max_f32 per operand on that).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float rows_vmax(float x) {
+  LanePair p = pair16(x);
+  x = vmax(p.a, p.b);
+  p = pair32(x);
+  return vmax(p.a, p.b);
+}
+// rows_vmax of two values at once, in three lane swaps instead of four. This
+// one depends on the order of the swaps' results, as measured on gfx950 with
+// rows (16-lane groups) a0..a3 of the first operand and b0..b3 of the second:
+// permlane16_swap returns [a0 b0 a2 b2] and [a1 b1 a3 b3], permlane32_swap
+// [a0 a1 b0 b1] and [a2 a3 b2 b3]. So the maximum of the first swap's
+// results is [a01 b01 a23 b23], folding it over the halves gives
+// [A B A B], and a last swap of that with itself returns A and B on all
+// four rows, in that order.
+__device__ __forceinline__ void rows_vmax2(float a, float b, float& ma, float& mb) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float c = vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const LanePair p = pair32(c);
+  const float d = vmax(p.a, p.b);
+  const LanePair q = pair16(d);
+  ma = q.a;
+  mb = q.b;
+}
 __device__ __forceinline__ float rows_sum(float x) {
   LanePair p = pair16(x);
   x = p.a + p.b;
