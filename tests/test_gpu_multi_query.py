@@ -129,3 +129,39 @@ def test_negative_and_zero_scale(pa, name, scale_mul):
     err = max_abs_err(out, expect)
     say(f"    max abs err {err:.3e}")
     assert err <= TOL[st.spec.dtype]
+
+
+@pytest.mark.parametrize("big_tile", [0, 1])
+@pytest.mark.parametrize("partition", [None, 0, 64])
+def test_two_tiles_per_wave_keep_their_own_max(pa, big_tile, partition):
+    # 64 rows x 8 heads per kv head: 32 column tiles, so the chunk kernel's
+    # waves hold two tiles each (tiles 2w and 2w + 1) and take both tiles'
+    # column maxima from one shared lane exchange. One tile of each pair gets
+    # queries 64x larger (exact in bf16), so its logits span hundreds of log2
+    # units: a tile that took the other's max as its reference would overflow
+    # to inf or underflow to an all-zero sum, while the right reference keeps
+    # every probability in range.
+    spec = Spec("mq_gqa8_wide", "bf16", 2, 16, 2, 128, seed=40, lengths=("uniform", 300, 1200),
+                chunk=("uniform", 64, 64))
+    say(f"[two tiles per wave] big tile {big_tile} partition={partition}")
+    st = Step(spec, oracle_full=False)
+    st.run_cache_ops(pa)
+    G = spec.Hq // spec.Hkv
+    bits = st.q_bits.copy()
+    qs = st.tb.query_start
+    for s in range(spec.B):
+        for i in range(qs[s + 1] - qs[s]):
+            if (i * G // 16) % 2 == big_tile:
+                row = (bits[qs[s] + i].astype(np.uint32) << 16).view(np.float32) * np.float32(64.0)
+                bits[qs[s] + i] = (row.view(np.uint32) >> 16).astype(np.uint16)
+    q = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(st.q.device)
+    out = pa.multi_query(q, st.k_cache, st.v_cache, st.block_tables, st.context_lens,
+                         st.query_start, st.spec.scale, st.max_ctx, st.max_q, partition=partition)
+    expect = oracle.multi_query(oracle_view(bits), oracle_view(st.k_after), oracle_view(st.v_after),
+                                st.tb.block_tables, st.tb.context_lens, st.tb.query_start,
+                                st.spec.scale)
+    o = out.float().cpu().numpy()
+    assert np.all(np.isfinite(o))
+    err = max_abs_err(out, expect)
+    say(f"    max abs err {err:.3e}")
+    assert err <= TOL[spec.dtype]
