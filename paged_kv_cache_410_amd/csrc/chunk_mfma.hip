@@ -249,25 +249,21 @@ void chunk_mfma_kernel(DecodeParams P) {
     vtr_off[et] = r * kRowBytes + (((dim / 8) ^ ((2 * r) & 14)) & 15) * 16 + (dim % 8) * 2;
   }
 
-  // Load logical blocks blk (A, physical ba) and blk + 1 (B, physical bb)
-  // into slot d. An id outside the pool marks the columns bad and loads
-  // nothing; so does a block that does not exist (past the partition, or an
-  // empty refill past the last pair, kept so that every step issues the same
-  // number of loads). Only rows inside the workgroup's context are fetched.
-  auto issue = [&](int d, int ba, int bb, int blk, bool ea, bool eb) {
-    const bool oka = ba >= 0 && ba < P.NB;
-    const bool okb = bb >= 0 && bb < P.NB;
-    bad |= (ea && !oka) || (eb && !okb);  // every wave checks both ids
+  // Load the pair of blocks at lanes i, i + 1 of the current 64-block chunk
+  // into slot d. Per lane of the chunk, off_lo/off_hi hold its tile's byte
+  // offset in the pool and nbytes the bytes to fetch: the rows inside the
+  // workgroup's context, or nothing for a bad id or a block past the chunk
+  // (an empty refill past the last pair, kept so that every step issues the
+  // same number of loads).
+  auto issue = [&](int d, int i, int cn, uint32_t off_lo, uint32_t off_hi, int nbytes) {
     // The descriptor of tile t (0: K of A, 1: K of B, 2: V of A, 3: V of B),
-    // built only for the tiles this wave's pieces belong to. (A block that
-    // exists starts inside the workgroup's context: at least one row.)
+    // built only for the tiles this wave's pieces belong to.
     auto rsrc_of = [&](int t) {
-      const bool second = (t & 1) != 0;
-      const bool ok = second ? okb : oka;
-      const bool ex = second ? eb : ea;
-      const size_t off = (size_t)(ok ? (second ? bb : ba) : 0) * block_stride + head_off;
-      const int bytes = ex && ok ? min(kBlock, ctx_wg - (blk + (second ? 1 : 0)) * kBlock) * kRowBytes
-                                 : 0;
+      const int li = i + (t & 1);
+      const int lc = min(li, kWave - 1);
+      const uint64_t off = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)off_hi, lc) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)off_lo, lc);
+      const int bytes = li < cn ? __builtin_amdgcn_readlane(nbytes, lc) : 0;
       return make_rsrc((t >= 2 ? vbase : kbase) + off, bytes);
     };
     char* dst = slot(d);
@@ -275,13 +271,13 @@ void chunk_mfma_kernel(DecodeParams P) {
       // all of the wave's pieces lie in one tile: one descriptor
       const rsrc_t r = rsrc_of((kPer * w) >> 2);
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        ld16_lds<kPolicy>(r, dst + (kPer * w + i) * kPieceBytes, piece_off[i]);
+      for (int q = 0; q < kPer; ++q)
+        ld16_lds<kPolicy>(r, dst + (kPer * w + q) * kPieceBytes, piece_off[q]);
     } else {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int q = kPer * w + i;
-        ld16_lds<kPolicy>(rsrc_of(q >> 2), dst + q * kPieceBytes, piece_off[i]);
+      for (int q = 0; q < kPer; ++q) {
+        const int pc = kPer * w + q;
+        ld16_lds<kPolicy>(rsrc_of(pc >> 2), dst + pc * kPieceBytes, piece_off[q]);
       }
     }
   };
@@ -542,12 +538,16 @@ void chunk_mfma_kernel(DecodeParams P) {
     const int pn = (cn + 1) / 2;         // pairs
     if (c0 > 0) ring_barrier();          // every wave is done with the previous chunk's slots
     const int ids = c0 == 0 ? ids0 : (lane < cn ? bt_row[blk_begin + c0 + lane] : -1);
-    auto issue_pair = [&](int d, int j) {
-      const int i = 2 * j;
-      issue(d, __builtin_amdgcn_readlane(ids, min(i, kWave - 1)),
-            __builtin_amdgcn_readlane(ids, min(i + 1, kWave - 1)), blk_begin + c0 + i, i < cn,
-            i + 1 < cn);
-    };
+    // Lane i: block c0 + i of the range. An id outside the pool marks the
+    // columns bad and loads nothing; only rows inside the workgroup's context
+    // are fetched (a block that exists starts inside it: at least one row).
+    const bool ok_id = ids >= 0 && ids < P.NB;
+    if (__builtin_amdgcn_ballot_w64(lane < cn && !ok_id) != 0) bad = true;
+    const uint64_t off = (uint64_t)(uint32_t)(ok_id ? ids : 0) * block_stride + head_off;
+    const int nbytes =
+        lane < cn && ok_id ? min(kBlock, ctx_wg - (blk_begin + c0 + lane) * kBlock) * kRowBytes : 0;
+    const uint32_t off_lo = (uint32_t)off, off_hi = (uint32_t)(off >> 32);
+    auto issue_pair = [&](int d, int j) { issue(d, 2 * j, cn, off_lo, off_hi, nbytes); };
 #pragma unroll
     for (int d = 0; d < R - 1; ++d) issue_pair(d, d);
     // Steps past the chunk's last pair still wait, meet and refill (with
