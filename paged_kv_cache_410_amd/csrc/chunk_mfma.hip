@@ -40,11 +40,9 @@
 // Lanes of a load past the block's rows inside the context write zeros.
 #include "pa_device.h"
 #include "pa_launch.h"
+#include "chunk_ring.h"
 
-// LDS ring slots (3 or 4 pairs of blocks) and the register allocation's minimum waves per SIMD.
-#ifndef PA_CHUNK_RING
-#define PA_CHUNK_RING 3
-#endif
+// The register allocation's minimum waves per SIMD (8-wave, one-tile kernel).
 #ifndef PA_CHUNK_MIN_WAVES
 #define PA_CHUNK_MIN_WAVES 4
 #endif
@@ -80,33 +78,9 @@ namespace pa {
 
 namespace {
 
-constexpr int kD = 128;
-constexpr int kRowBytes = kD * 2;
-constexpr int kTileBytes = kBlock * kRowBytes;      // one K or V tile of one block
-constexpr int kSlotBytes = 4 * kTileBytes;          // a pair of blocks: K A, K B, V A, V B
-constexpr int kPieceBytes = kWave * 16;             // one load instruction
-constexpr int kPieces = kSlotBytes / kPieceBytes;   // per pair
-
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x002;    // vector ALU, MFMA excluded
 constexpr int kSchedMfma = 0x008;
-
-// s_waitcnt bounding only the vector memory count (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier with no memory fence: a fence would wait for every load
-// in flight, the ring's prefetches included. The empty asm statements keep
-// the compiler from moving memory accesses across it.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 }  // namespace
 
@@ -209,7 +183,7 @@ void chunk_mfma_kernel(DecodeParams P) {
   f32x4_t acc[TPW][8];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    m[t] = -INFINITY;
+    m[t] = kNoRef;
     lsum[t] = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -329,13 +303,14 @@ void chunk_mfma_kernel(DecodeParams P) {
     // instead of whenever its max creeps up.
     constexpr float kLazy = 8.0f;
     const float m_new = vmax(m[t], mx);
-    const bool up = m_new > m[t] + kLazy;  // from -inf: any finite max
+    const bool up = m_new > m[t] + kLazy;  // from kNoRef: any finite max
     const float ref = up ? m_new : m[t];
-    const float ref_use = (ref == -INFINITY) ? 0.0f : ref;
-    const float alpha = exp2_fast(m[t] - ref_use);  // exactly 1 where the reference stays
+    // Exactly 1 where the reference stays; 0 (or 2^-inf) from kNoRef, where
+    // the accumulators hold nothing yet.
+    const float alpha = exp2_fast(m[t] - ref);
     float pr[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref_use));
+    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref));
     m[t] = ref;
     const uint4 w4 = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                 pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
@@ -588,7 +563,7 @@ void chunk_mfma_kernel(DecodeParams P) {
             bad ? make_float4(nan, nan, nan, nan)
                 : make_float4(acc[t][et][0], acc[t][et][1], acc[t][et][2], acc[t][et][3]);
       if (rg == 0) {
-        P.ws_ml[2 * part] = bad ? 0.0f : m[t];
+        P.ws_ml[2 * part] = bad ? 0.0f : (m[t] == kNoRef ? -INFINITY : m[t]);
         P.ws_ml[2 * part + 1] = bad ? nan : l_col;
       }
     } else {
