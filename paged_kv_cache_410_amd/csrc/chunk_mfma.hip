@@ -50,24 +50,6 @@
 #ifndef PA_CHUNK_MAX_WAVES
 #define PA_CHUNK_MAX_WAVES 8
 #endif
-// Two-tile step laid out as a pipeline (1: softmax of one tile between the
-// other's MFMAs; needs registers for 2 waves per SIMD) or in plain order (0).
-#ifndef PA_CHUNK_TPW2_PIPELINE
-#define PA_CHUNK_TPW2_PIPELINE 0
-#endif
-// Both tiles' softmax before one joint rescale branch (1) or each tile's
-// softmax and rescale in turn (0).
-#ifndef PA_CHUNK_TPW2_JOINT
-#define PA_CHUNK_TPW2_JOINT 1
-#endif
-// Waves per SIMD the two-tile kernel's registers are sized for (2 or 3).
-#ifndef PA_CHUNK_TPW2_WAVES
-#define PA_CHUNK_TPW2_WAVES (PA_CHUNK_TPW2_PIPELINE ? 2 : 3)
-#endif
-// Vector ALU instructions scheduled after each MFMA in the two-tile step.
-#ifndef PA_CHUNK_VALU_PER_MFMA
-#define PA_CHUNK_VALU_PER_MFMA 6
-#endif
 // Column tiles (16 columns each) per wave for more than 8 tiles per kv
 // head: 2 (on 4 waves) or 1 (on 8 waves).
 #ifndef PA_CHUNK_TILES_PER_WAVE
@@ -76,17 +58,9 @@
 
 namespace pa {
 
-namespace {
-
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002;    // vector ALU, MFMA excluded
-constexpr int kSchedMfma = 0x008;
-
-}  // namespace
-
 template <int NW, int R, int TPW, TilePolicy kPolicy>
 __global__ __launch_bounds__(NW * kWave)
-__attribute__((amdgpu_waves_per_eu(TPW > 1 ? PA_CHUNK_TPW2_WAVES : NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(TPW > 1 ? 3 : NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
 void chunk_mfma_kernel(DecodeParams P) {
   static_assert(kPieces % NW == 0, "pieces must divide over the waves");
   static_assert(R >= 3 && R <= 4, "ring of 3 or 4 slots");
@@ -329,29 +303,11 @@ void chunk_mfma_kernel(DecodeParams P) {
   auto softmax = [&](int t, const float (&x)[8]) {
     return softmax_with(t, x, rows_vmax(lane_max(x)));
   };
-  // Raw logits of tile t (S^T of blocks A and B), masked where kMask (a
-  // wave-uniform bool, or a constant type) says the pair needs it.
-  auto logits = [&](int t, const f32x4_t& sa, const f32x4_t& sb, int blk, bool b_live, auto kMask,
-                    float (&x)[8]) {
+  // Raw logits of tile t (S^T of blocks A then B).
+  auto logits = [&](const f32x4_t& sa, const f32x4_t& sb, float (&x)[8]) {
     const float v[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = v[i];
-    if (static_cast<bool>(kMask)) mask_logits(t, x, blk, b_live);
-  };
-  // Pins the probabilities in registers at this point: otherwise the
-  // compiler sinks their exponentials past the rescale branch below, into
-  // the block of the PV products, and the pipeline's stages merge.
-  auto pin = [](Probs& pr) {
-    uint4 u = __builtin_bit_cast(uint4, pr.pop);
-    asm volatile("" : "+v"(u.x), "+v"(u.y), "+v"(u.z), "+v"(u.w));
-    pr.pop = __builtin_bit_cast(bf16x8_t, u);
-  };
-  // The accumulators of tile t to the new reference, where any column's moved.
-  auto rescale = [&](int t, const Probs& pr) {
-    if (__builtin_amdgcn_ballot_w64(pr.up) != 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[t][e] *= pr.alpha;
-    }
   };
 
   // One pair of blocks in slot d, for each of the wave's tiles: S^T of both
@@ -360,14 +316,13 @@ void chunk_mfma_kernel(DecodeParams P) {
   // K = 32 contraction: contraction slots 8 rg + 0..3 are block A's tokens
   // 4 rg + 0..3 and slots 8 rg + 4..7 block B's, so a lane's own
   // probabilities are its B operand as they stand. The K and V operands are
-  // read once for all the wave's tiles.
-  //
-  // The matrix cores and the vector ALU run side by side only where one
-  // wave's instruction stream alternates between them (it issues in order),
-  // so with two tiles the step is laid out as a pipeline: tile 0's softmax
-  // goes between tile 1's QK products, tile 1's softmax between tile 0's PV
-  // products (the scheduling group barriers below fix that interleave).
-  auto consume_pair = [&](int d, int blk, bool b_live, auto kMask) {
+  // read once for all the wave's tiles. Pairs that reach a column's causal
+  // limit, or whose block B is past the partition, are masked (a
+  // wave-uniform branch, taken on few pairs).
+  auto consume = [&](int d, int blk, bool b_live) {
+    bool edge = !b_live;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) edge |= blk * kBlock + 2 * kBlock > ctx_min[t];
     const char* src = slot(d);
     f32x4_t sa[TPW], sb[TPW];
 #pragma unroll
@@ -375,26 +330,16 @@ void chunk_mfma_kernel(DecodeParams P) {
       sa[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       sb[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    // K operands, each read once for the wave's tiles; in the pipeline,
-    // tile 0's products come first.
-    constexpr bool kTileMajor = TPW == 2 && PA_CHUNK_TPW2_PIPELINE;
-    bf16x8_t ka[4], kb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int o = col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16;
-      ka[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + o));
-      kb[kk] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + kTileBytes + o));
+      const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + o));
+      const bf16x8_t kb =
+          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + kTileBytes + o));
 #pragma unroll
-      for (int t = 0; t < (kTileMajor ? 1 : TPW); ++t) {
-        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[t][kk], sa[t], 0, 0, 0);
-        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qop[t][kk], sb[t], 0, 0, 0);
-      }
-    }
-    if constexpr (kTileMajor) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        sa[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qop[1][kk], sa[1], 0, 0, 0);
-        sb[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[kk], qop[1][kk], sb[1], 0, 0, 0);
+      for (int t = 0; t < TPW; ++t) {
+        sa[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop[t][kk], sa[t], 0, 0, 0);
+        sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[t][kk], sb[t], 0, 0, 0);
       }
     }
     if constexpr (TPW == 1) {
@@ -403,23 +348,26 @@ void chunk_mfma_kernel(DecodeParams P) {
 #pragma unroll
       for (int et = 0; et < 8; ++et) vop[et] = v_operand(src, et);
       float x0[8];
-      logits(0, sa[0], sb[0], blk, b_live, kMask, x0);
+      logits(sa[0], sb[0], x0);
+      if (edge) mask_logits(0, x0, blk, b_live);
       const Probs p0 = softmax(0, x0);
-      rescale(0, p0);
+      if (__builtin_amdgcn_ballot_w64(p0.up) != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[0][e] *= p0.alpha;
+      }
 #pragma unroll
       for (int et = 0; et < 8; ++et)
         acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p0.pop, acc[0][et], 0, 0, 0);
-    } else if constexpr (!PA_CHUNK_TPW2_PIPELINE) {
-      // Both softmaxes, then each V operand read just before its two MFMAs
-      // (registers are short with two tiles).
-#if PA_CHUNK_TPW2_JOINT
-      // Both tiles' softmax in one block (their dependency chains overlap),
-      // then one branch rescales both where either's reference moved (the
-      // other's alpha is then exactly 1).
+    } else {
+      // Both tiles' softmax in one basic block (one mask branch, and the two
+      // dependency chains overlap), one branch that rescales both where
+      // either's reference moved (the other's alpha is then exactly 1), then
+      // each V operand read just before its two MFMAs (registers are short
+      // with two tiles).
       float x0[8], x1[8];
-      logits(0, sa[0], sb[0], blk, false, std::false_type{}, x0);
-      logits(1, sa[1], sb[1], blk, false, std::false_type{}, x1);
-      if (static_cast<bool>(kMask)) {  // one branch for both tiles
+      logits(sa[0], sb[0], x0);
+      logits(sa[1], sb[1], x1);
+      if (edge) {
         mask_logits(0, x0, blk, b_live);
         mask_logits(1, x1, blk, b_live);
       }
@@ -434,69 +382,12 @@ void chunk_mfma_kernel(DecodeParams P) {
           acc[1][e] *= p1.alpha;
         }
       }
-#else
-      float x0[8], x1[8];
-      logits(0, sa[0], sb[0], blk, b_live, kMask, x0);
-      const Probs p0 = softmax(0, x0);
-      rescale(0, p0);
-      logits(1, sa[1], sb[1], blk, b_live, kMask, x1);
-      const Probs p1 = softmax(1, x1);
-      rescale(1, p1);
-#endif
 #pragma unroll
       for (int et = 0; et < 8; ++et) {
         const bf16x8_t v = v_operand(src, et);
         acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p0.pop, acc[0][et], 0, 0, 0);
         acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p1.pop, acc[1][et], 0, 0, 0);
       }
-    } else {
-      float x0[8], x1[8];
-      logits(0, sa[0], sb[0], blk, b_live, kMask, x0);
-      Probs p0 = softmax(0, x0);
-      bf16x8_t vop[8];
-#pragma unroll
-      for (int et = 0; et < 8; ++et) vop[et] = v_operand(src, et);
-      // Tile 0's QK products, then each of tile 1's with a share of tile
-      // 0's softmax; the V reads go in the second half, as K operands die.
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, PA_CHUNK_VALU_PER_MFMA, 0);
-      }
-      pin(p0);
-      rescale(0, p0);
-      logits(1, sa[1], sb[1], blk, b_live, kMask, x1);
-      Probs p1 = softmax(1, x1);
-#pragma unroll
-      for (int et = 0; et < 8; ++et)
-        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p0.pop, acc[0][et], 0, 0, 0);
-      // Each of tile 0's PV products with a share of tile 1's softmax.
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, PA_CHUNK_VALU_PER_MFMA, 0);
-      }
-      pin(p1);
-      rescale(1, p1);
-#pragma unroll
-      for (int et = 0; et < 8; ++et)
-        acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p1.pop, acc[1][et], 0, 0, 0);
-    }
-  };
-  // Steps whose pair reaches a column's causal limit, or whose block B is
-  // past the partition, take the masked form (wave-uniform); with two tiles
-  // the whole step is duplicated, so that no branch cuts its pipeline.
-  auto consume = [&](int d, int blk, bool b_live) {
-    bool edge = !b_live;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) edge |= blk * kBlock + 2 * kBlock > ctx_min[t];
-    if constexpr (TPW == 1 || !PA_CHUNK_TPW2_PIPELINE) {
-      consume_pair(d, blk, b_live, edge);  // a branch inside the softmax
-    } else if (edge) {
-      consume_pair(d, blk, b_live, std::true_type{});
-    } else {
-      consume_pair(d, blk, true, std::false_type{});
     }
   };
 
