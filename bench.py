@@ -44,6 +44,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 DECODE_SOURCES = ["paged_kv_cache_410_amd/csrc/decode_valu.hip",
                   "paged_kv_cache_410_amd/csrc/decode_mfma.hip",
                   "paged_kv_cache_410_amd/csrc/chunk_mfma.hip",
+                  "paged_kv_cache_410_amd/csrc/chunk_ring.h",
                   "paged_kv_cache_410_amd/csrc/decode_reduce.hip",
                   "paged_kv_cache_410_amd/csrc/pa_device.h",
                   "paged_kv_cache_410_amd/csrc/pa_launch.h",
