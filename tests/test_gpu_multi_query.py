@@ -165,3 +165,38 @@ def test_two_tiles_per_wave_keep_their_own_max(pa, big_tile, partition):
     err = max_abs_err(out, expect)
     say(f"    max abs err {err:.3e}")
     assert err <= TOL[spec.dtype]
+
+
+@pytest.mark.parametrize("name", ["mq_gqa8", "mq_gqa8_short", "mq_mha", "mq_single", "mq_long"])
+@pytest.mark.parametrize("partition", [0, 64])
+def test_bad_block_ids_poison_only_their_rows(pa, name, partition):
+    # A block id outside the pool, or negative, in a block every row of its
+    # sequence attends to: that sequence's rows come out NaN, nothing is read
+    # out of bounds, and every other row keeps its bits. The kernels cover
+    # two tiles per wave (mq_gqa8), one tile per wave on 2 or 4 waves
+    # (mq_gqa8_short, mq_mha), the matrix-core decode kernel (mq_single), and
+    # an id in the second 64-block chunk of a long unsplit row (mq_long).
+    say(f"[multi-query bad block ids] {name} partition={partition}")
+    st = Step(CHUNKS[name], oracle_full=False)
+    st.run_cache_ops(pa)
+    good = st.multi(pa, partition=partition)
+    bt = st.block_tables.clone()
+    qs = st.tb.query_start
+    B = st.spec.B
+    j0 = 70 if name == "mq_long" else 0
+    assert int(st.tb.context_lens[0]) > 16 * j0
+    bt[0, j0] = st.tb.NB + 5
+    bad = [0]
+    if B >= 3:
+        bt[2, 0] = -7
+        bad.append(2)
+    out = pa.multi_query(st.q, st.k_cache, st.v_cache, bt, st.context_lens, st.query_start,
+                         st.spec.scale, st.max_ctx, st.max_q, partition=partition)
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    for s in range(B):
+        rows = slice(int(qs[s]), int(qs[s + 1]))
+        if s in bad:
+            assert torch.isnan(o[rows]).all(), s
+        else:
+            assert torch.equal(out[rows].view(torch.int16).cpu(), good[rows].view(torch.int16).cpu()), s
