@@ -41,9 +41,13 @@
 #include "pa_device.h"
 #include "pa_launch.h"
 
-// Waves per workgroup and K/V tiles in flight per wave.
+// Waves per workgroup (split contexts, and unsplit ones) and K/V tiles in
+// flight per wave.
 #ifndef PA_MFMA_WAVES
 #define PA_MFMA_WAVES 4
+#endif
+#ifndef PA_MFMA_WAVES_UNSPLIT
+#define PA_MFMA_WAVES_UNSPLIT 8
 #endif
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 2
@@ -312,15 +316,23 @@ void decode_mfma_kernel(DecodeParams P) {
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   // several column tiles per kv head: the chunk kernel, whose waves share each block
   if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
-  constexpr int NW = PA_MFMA_WAVES;
   constexpr int DEPTH = PA_MFMA_DEPTH;
-  const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B), block(NW * kWave);
-  if (p.shared_kv)
-    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared>), grid, block, 0,
-                       stream, p);
+  auto go = [&](auto nw) {
+    constexpr int NW = decltype(nw)::value;
+    const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B), block(NW * kWave);
+    if (p.shared_kv)
+      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared>), grid, block, 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream>), grid, block, 0,
+                         stream, p);
+  };
+  // A whole context per workgroup: more waves, each with a longer share of
+  // its blocks. Split contexts (a partition's few blocks): fewer.
+  if (p.n_parts == 1)
+    go(std::integral_constant<int, PA_MFMA_WAVES_UNSPLIT>{});
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream>), grid, block, 0,
-                       stream, p);
+    go(std::integral_constant<int, PA_MFMA_WAVES>{});
   return hipGetLastError();
 }
 
