@@ -396,8 +396,8 @@ void chunk_mfma_kernel(DecodeParams P) {
   // it (the R - 2 pairs issued after it may stay in flight), then a barrier
   // makes every wave's pieces visible and shows that every wave is done with
   // pair j - 1, whose slot takes pair j + R - 1. Block ids are read 64 at a
-  // time (lane i holds the chunk's i-th id, broadcast with readlane); the
-  // ring drains at each chunk's end.
+  // time: lane i holds the chunk's i-th block (its pool offset and byte
+  // count, read per pair with readlane). The ring drains at each chunk's end.
   const int nk = max(0, blk_end - blk_begin);
   for (int c0 = 0; c0 < nk; c0 += kWave) {
     const int cn = min(kWave, nk - c0);  // blocks in this chunk
