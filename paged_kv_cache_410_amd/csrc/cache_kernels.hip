@@ -90,27 +90,45 @@ __global__ void append_kv_kernel(const uint4* __restrict__ k_new, const uint4* _
   v_cache[dst] = vx;
 }
 
-// grid.y = pair, grid.z = 0 (K) / 1 (V); grid.x strides over the block's chunks.
-__global__ void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
-                                   const int32_t* __restrict__ pairs, int32_t NB,
-                                   int64_t chunks_per_block) {
+// Copy-on-write copies: grid.y = pair, grid.z = 0 (K) / 1 (V); workgroup x
+// of a pair takes U consecutive 4 KiB pieces of the block (256 threads x 16 B
+// each) and issues all its loads before its first store, so the whole copy is
+// in flight at once and each workgroup makes one round trip.
+#ifndef PA_COPY_UNROLL
+#define PA_COPY_UNROLL 4
+#endif
+#ifndef PA_COPY_NT
+#define PA_COPY_NT 0
+#endif
+constexpr int kCopyThreads = 256;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <int U, bool kNT>
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    u32x4_t* __restrict__ k_cache, u32x4_t* __restrict__ v_cache, const int32_t* __restrict__ pairs,
+    int32_t NB, int64_t chunks_per_block) {
   const int32_t src = pairs[2 * blockIdx.y];
   const int32_t dst = pairs[2 * blockIdx.y + 1];
   if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
-  uint4* base = blockIdx.z ? v_cache : k_cache;
-  const uint4* from = base + (int64_t)src * chunks_per_block;
-  uint4* to = base + (int64_t)dst * chunks_per_block;
-  constexpr int kUnroll = 4;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < chunks_per_block; i += kUnroll * stride) {
-    uint4 v[kUnroll];
+  u32x4_t* base = blockIdx.z ? v_cache : k_cache;
+  const u32x4_t* from = base + (int64_t)src * chunks_per_block;
+  u32x4_t* to = base + (int64_t)dst * chunks_per_block;
+  const int64_t i0 = (int64_t)blockIdx.x * (U * kCopyThreads) + threadIdx.x;
+  u32x4_t v[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = from[i + u * stride];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) to[i + u * stride] = v[u];
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = i0 + u * kCopyThreads;
+    if (i < chunks_per_block) v[u] = kNT ? __builtin_nontemporal_load(from + i) : from[i];
   }
-  for (; i < chunks_per_block; i += stride) to[i] = from[i];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = i0 + u * kCopyThreads;
+    if (i < chunks_per_block) {
+      if (kNT)
+        __builtin_nontemporal_store(v[u], to + i);
+      else
+        to[i] = v[u];
+    }
+  }
 }
 
 hipError_t launch_slot_mapping(int32_t* out, const int32_t* bt, const int32_t* seq_ids,
@@ -151,13 +169,12 @@ hipError_t launch_append_kv(const void* k_new, const void* v_new, void* k_cache,
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t n,
                               int32_t NB, size_t block_bytes, hipStream_t stream) {
+  constexpr int U = PA_COPY_UNROLL;
   const int64_t chunks = (int64_t)(block_bytes / 16);
-  const int threads = 256;
-  // about 4 chunks (64 B) per thread per pass: a 128 KiB block takes 8 workgroups
-  int64_t gx = (chunks + threads * 4 - 1) / (threads * 4);
-  if (gx < 1) gx = 1;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n, 2), dim3(threads), 0,
-                     stream, (uint4*)k_cache, (uint4*)v_cache, pairs, NB, chunks);
+  const int64_t gx = (chunks + U * kCopyThreads - 1) / (U * kCopyThreads);
+  hipLaunchKernelGGL((copy_blocks_kernel<U, PA_COPY_NT != 0>), dim3((unsigned)gx, (unsigned)n, 2),
+                     dim3(kCopyThreads), 0, stream, (u32x4_t*)k_cache, (u32x4_t*)v_cache, pairs,
+                     NB, chunks);
   return hipGetLastError();
 }
 
