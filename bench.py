@@ -198,6 +198,11 @@ def main():
                          "sequential-table launches would mix into the attention kernel's "
                          "statistics)")
     ap.add_argument("--no-controls", action="store_true", help="same as --controls none")
+    ap.add_argument("--no-group", action="store_true",
+                    help="attend over blocks shared by several sequences once per sequence "
+                         "(pa_decode) instead of once per group of sharers (pa_decode_shared)")
+    ap.add_argument("--shared-partition", type=int, default=0,
+                    help="partition length of the shared part in pa_decode_shared (0 = none)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed; the "
                          "replayed step then sets value and ms_per_step")
@@ -262,8 +267,41 @@ def main():
         dst = torch.from_numpy(tb.pairs[:, 1].astype(np.int64)).to(dev)
         k_saved, v_saved = k_cache[dst].clone(), v_cache[dst].clone()
 
+    # Blocks shared by several sequences: read once per group of sharers.
+    groups = None
+    if shared_kv and not spec.chunk and not args.no_group and spec.dtype == "bf16" \
+            and spec.D == 128:
+        max_group = 16 // (spec.Hq // spec.Hkv)
+        gs, sh = pa.shared_groups(tb.block_tables, tb.context_lens, max_group)
+        if sh.any():
+            # once grouped, do blocks still repeat (a prefix shared by several
+            # groups)? Then the caches serve the repeats, else stream.
+            reads = []
+            for j in range(len(gs) - 1):
+                a, b = int(gs[j]), int(gs[j + 1])
+                nsh = int(sh[a]) // 16
+                reads += tb.block_tables[a, :nsh].tolist()
+                for s_ in range(a, b):
+                    reads += tb.block_tables[s_, nsh:(int(tb.context_lens[s_]) + 15) // 16].tolist()
+            group_repeats = len(set(reads)) < len(reads)
+            sp = args.shared_partition
+            groups = dict(group_start=torch.from_numpy(gs).to(dev),
+                          seq_shared=torch.from_numpy(sh).to(dev), max_group=max_group,
+                          max_shared=int(sh.max()), partition=sp, repeats=group_repeats,
+                          workspace=torch.empty(pa.decode_shared_workspace_bytes(
+                              spec.B, spec.Hq, spec.D, int(sh.max()), sp), dtype=torch.uint8,
+                              device=dev))
+            log(f"[bench] {len(gs) - 1} groups of sharers, shared tokens "
+                f"{sorted(set(sh.tolist()))}, shared-part partition {sp}")
+
     def attend(tables, dest, shared):
-        if spec.chunk:
+        if groups is not None and tables is bt:
+            pa.decode_shared(q, k_cache, v_cache, tables, cl, groups["group_start"],
+                             groups["seq_shared"], spec.scale, max_ctx, groups["max_group"],
+                             groups["max_shared"], partition=groups["partition"], out=dest,
+                             workspace=groups["workspace"],
+                             shared_kv=shared and groups["repeats"])
+        elif spec.chunk:
             pa.multi_query(q, k_cache, v_cache, tables, cl, qs, spec.scale, max_ctx, max_q,
                            partition=partition, out=dest, workspace=workspace, shared_kv=shared)
         else:
@@ -455,6 +493,11 @@ def main():
                    "max_ctx": max_ctx, "mean_ctx": round(float(tb.context_lens.mean()), 1),
                    "pool_blocks": tb.NB, "new_tokens": T, "query_rows": rows,
                    "cow_pairs": len(tb.pairs), "shared_kv": shared_kv,
+                   "shared_groups": (None if groups is None else
+                                     dict(groups=int(groups["group_start"].shape[0] - 1),
+                                          max_shared=groups["max_shared"],
+                                          shared_partition=groups["partition"],
+                                          blocks_repeat_across_groups=groups["repeats"])),
                    "parallelism": "none (one GPU)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(T / (ms_step * 1e-3), 1),
@@ -467,8 +510,10 @@ def main():
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": traffic, "kernel": "attention (one launch per step"
-                     + (", plus the partition merge)" if ws_bytes else ")"),
+                     "traffic": traffic,
+                     "kernel": ("pa_decode_shared (group pass, tail pass, merge)"
+                                if groups is not None else "attention (one launch per step"
+                                + (", plus the partition merge)" if ws_bytes else ")")),
                      "traffic_note": why, "intensity_flop_per_byte": round(intensity, 2)},
         "cpu_baseline": cpu,
         "parity_max_abs_err_vs_oracle": parity,

@@ -264,6 +264,78 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
                     pa_dtype dt, hipStream_t stream);
 
 /*
+ * pa_decode_shared — pa_decode for a batch whose sequences share leading
+ * blocks (parallel samples of one prompt, beams, a common prefix), reading
+ * each shared block once per group of sharers instead of once per sequence.
+ *
+ * [P1] section 3 / [P3] mechanism paragraph: sequences forked from one
+ * prompt, or requests with a common prefix, point their tables at the same
+ * physical blocks. The result is pa_decode's, up to the order of summation:
+ * attention over 0 .. L-1 splits into the shared tokens 0 .. S_s-1 and the
+ * sequence's own S_s .. L-1, and the two online-softmax partials are merged
+ * by log-sum-exp weights as between split-context partitions.
+ *
+ *   group_start  int32 [n_groups + 1], device: group j is the sequences
+ *                group_start[j] .. group_start[j+1]-1 (consecutive, at least
+ *                one, at most max_group); the groups cover 0 .. B-1 in order
+ *   seq_shared   int32 [B], device: S_s, the leading tokens sequence s shares
+ *                with its group: a multiple of bs, the same for every member,
+ *                at most context_lens[s]; the members' block_tables agree on
+ *                the first S_s / bs entries (0 for a sequence that shares
+ *                nothing)
+ *   max_group    host bound on the group sizes; max_group * (Hq / Hkv) <= 16
+ *   max_shared   host bound on every S_s (a multiple of bs, <= max_ctx)
+ *   partition    tokens per partition of the shared part (0 = one partition;
+ *                else a positive multiple of bs); each sequence's own tokens
+ *                are one partition
+ *   workspace    at least pa_decode_shared_workspace_bytes(B, Hq, D,
+ *                max_shared, partition) bytes, 256-byte aligned (may be NULL
+ *                when that is 0)
+ * Other arguments and error rows as pa_decode. Two launches: the shared part
+ * of every group (one read of its blocks for all members' query heads, on
+ * the matrix cores, into the workspace), then every sequence's own tokens,
+ * merged with its shared part into the final row. Supported for
+ * bf16 with D = 128 (else PA_EUNSUPPORTED). A shared length that is negative,
+ * not a multiple of bs or beyond the table gives that sequence an all-NaN
+ * row (the group pass takes the first member's, so a bad one there gives the
+ * whole group NaN rows). Member tables that disagree on the shared entries
+ * are not detected (the group's first member's blocks are used for all);
+ * members whose shared lengths differ get undefined rows (no read leaves the
+ * workspace). B == 0 is a no-op.
+ */
+size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
+                                        int32_t max_shared, int32_t partition);
+pa_status pa_decode_shared(void* out, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens,
+                           const int32_t* group_start, const int32_t* seq_shared,
+                           int32_t B, int32_t n_groups, int32_t max_group,
+                           int32_t max_shared, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                           int32_t max_ctx, float scale, int32_t partition,
+                           void* workspace, size_t workspace_bytes,
+                           uint32_t flags, pa_dtype dt, hipStream_t stream);
+
+/*
+ * pa_shared_groups — the groups and shared lengths pa_decode_shared takes,
+ * from the block tables (HOST memory; the block manager's view).
+ *
+ * [P1] section 3: sharers of a block point their tables at the same physical
+ * block. Scans the sequences in order and starts a group at sequence s; the
+ * next sequence joins while the group has fewer than max_group members and
+ * its table agrees with the group's first member's on at least one leading
+ * block that lies whole inside both contexts. The group's shared length is
+ * bs times the number of leading whole blocks on which every member agrees;
+ * a group of one shares nothing (0). Writes group_start [B + 1 at most, the
+ * first *n_groups + 1 entries used] and seq_shared [B]. Table entries past a
+ * sequence's context are not read.
+ */
+pa_status pa_shared_groups(const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t MB, int32_t bs, int32_t max_group,
+                           int32_t* group_start, int32_t* seq_shared,
+                           int32_t* n_groups);
+
+/*
  * pa_multi_query — causal attention of several new tokens per sequence over
  * the paged cache (a prompt processed in chunks, or several drafted tokens
  * checked in one pass).

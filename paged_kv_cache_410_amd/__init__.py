@@ -27,7 +27,8 @@ from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PA_KV_SHARED, PAError, check, l
 __all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "check_slots", "check_pairs",
            "check_tables", "decode", "multi_query", "shares_blocks",
            "decode_workspace_bytes",
-           "default_partition", "BlockManager", "PAError"]
+           "default_partition", "BlockManager", "PAError", "shared_groups", "decode_shared",
+           "decode_shared_workspace_bytes"]
 
 BLOCK_SIZE = 16
 
@@ -248,6 +249,68 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx, part
                               block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs,
                               NB, MB, int(max_ctx), float(scale), int(partition), ws_ptr, ws_bytes,
                               PA_KV_SHARED if shared_kv else 0, _dt(q), _stream(dev)), "pa_decode")
+    return out
+
+
+def shared_groups(block_tables, context_lens, max_group):
+    """Groups of consecutive sequences that share leading blocks, from host
+    tables (pa_shared_groups): (group_start int32 [n_groups + 1], seq_shared
+    int32 [B]) as numpy arrays."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if bt.ndim != 2 or cl.shape != (bt.shape[0],):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    B, MB = bt.shape
+    gs = np.zeros(B + 1, np.int32)
+    sh = np.zeros(B, np.int32)
+    n = ctypes.c_int32(0)
+    check(lib().pa_shared_groups(bt.ctypes.data, cl.ctypes.data, B, MB, 16, int(max_group),
+                                 gs.ctypes.data, sh.ctypes.data, ctypes.byref(n)),
+          "pa_shared_groups")
+    return gs[:n.value + 1].copy(), sh
+
+
+def decode_shared_workspace_bytes(B, Hq, D, max_shared, partition):
+    return int(lib().pa_decode_shared_workspace_bytes(B, Hq, D, max_shared, partition))
+
+
+def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, seq_shared,
+                  scale, max_ctx, max_group, max_shared, partition=0, out=None, workspace=None,
+                  shared_kv=True):
+    """pa_decode for sequences that share leading blocks (pa_decode_shared):
+    group_start int32 [n_groups + 1] and seq_shared int32 [B] on the device,
+    as shared_groups() gives them; max_group and max_shared bound them.
+    partition splits the shared part (0 = one partition)."""
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                    (group_start, "group_start"), (seq_shared, "seq_shared")):
+        _i32(t, name)
+    B, Hq, Dq = q.shape
+    if Dq != D or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [B, Hq, D] with the pools' dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,) \
+            or seq_shared.shape != (B,) or group_start.dim() != 1:
+        raise ValueError("block_tables [B, MB], context_lens and seq_shared [B], "
+                         "group_start [n_groups + 1]")
+    MB = block_tables.shape[1]
+    n_groups = group_start.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    need = decode_shared_workspace_bytes(B, Hq, D, max_shared, partition)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, group_start, seq_shared, out,
+               workspace)
+    with torch.cuda.device(dev):
+        check(lib().pa_decode_shared(
+            out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), group_start.data_ptr(),
+            seq_shared.data_ptr(), B, n_groups, int(max_group), int(max_shared), Hq, Hkv, D, bs,
+            NB, MB, int(max_ctx), float(scale), int(partition), workspace.data_ptr(), ws_bytes,
+            PA_KV_SHARED if shared_kv else 0, _dt(q), _stream(dev)), "pa_decode_shared")
     return out
 
 

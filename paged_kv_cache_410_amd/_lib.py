@@ -30,6 +30,11 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_i32, c_vp]),
+    "pa_decode_shared_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_shared": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                 c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                 c_f32, c_i32, c_vp, c_sz, c_u32, c_i32, c_vp]),
+    "pa_shared_groups": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_i32p]),
     "pa_multi_query": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
                                c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32,
                                c_vp, c_sz, c_u32, c_i32, c_vp]),

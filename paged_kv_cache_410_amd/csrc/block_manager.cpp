@@ -361,4 +361,44 @@ pa_status pa_bm_fill_tables(const pa_block_manager* bm, const int32_t* seqs, int
   return PA_OK;
 }
 
+pa_status pa_shared_groups(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t MB, int32_t bs, int32_t max_group, int32_t* group_start,
+                           int32_t* seq_shared, int32_t* n_groups) {
+  if (B < 0 || MB < 0 || bs <= 0 || max_group < 1 || !n_groups ||
+      (B > 0 && (!context_lens || !group_start || !seq_shared || (MB > 0 && !block_tables))))
+    return PA_EINVAL;
+  *n_groups = 0;
+  if (B == 0) return PA_OK;
+  int32_t ng = 0;
+  group_start[0] = 0;
+  for (int32_t s = 0; s < B;) {
+    const int32_t* first = block_tables + (size_t)s * MB;
+    // whole blocks inside the first member's context, with valid ids
+    int32_t k = context_lens[s] > 0 ? context_lens[s] / bs : 0;
+    if (k > MB) k = MB;
+    for (int32_t j = 0; j < k; ++j)
+      if (first[j] < 0) {
+        k = j;
+        break;
+      }
+    int32_t e = s + 1;
+    while (e < B && e - s < max_group && k > 0) {
+      const int32_t* row = block_tables + (size_t)e * MB;
+      int32_t full = context_lens[e] > 0 ? context_lens[e] / bs : 0;
+      int32_t lcp = 0;
+      const int32_t lim = k < full ? k : full;
+      while (lcp < lim && row[lcp] == first[lcp]) ++lcp;
+      if (lcp == 0) break;  // shares nothing with the group: next group
+      k = lcp;
+      ++e;
+    }
+    const int32_t shared = e - s > 1 ? k * bs : 0;  // a sequence alone shares nothing
+    for (int32_t i = s; i < e; ++i) seq_shared[i] = shared;
+    group_start[++ng] = e;
+    s = e;
+  }
+  *n_groups = ng;
+  return PA_OK;
+}
+
 }  // extern "C"

@@ -49,6 +49,11 @@
 #ifndef PA_MFMA_WAVES_UNSPLIT
 #define PA_MFMA_WAVES_UNSPLIT 8
 #endif
+// Waves per workgroup of the shared-prefix group pass (a group's shared
+// blocks, usually few work items: smaller workgroups all fit at once).
+#ifndef PA_MFMA_GROUP_WAVES
+#define PA_MFMA_GROUP_WAVES 4
+#endif
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 2
 #endif
@@ -83,9 +88,10 @@ void decode_mfma_kernel(DecodeParams P) {
   const int tile = gp.x % P.n_tiles;  // 16-column tile of this kv head's (row, head) pairs
   const int s = gp.z;
 
-  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
+  const ItemStart is = item_start(P, s);
+  const int32_t* bt_row = P.block_tables + (size_t)is.trow * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
-  const int blk_begin = p * bpp;
+  const int blk_begin = is.start_blk + p * bpp;
   // this wave's blocks: first, first + kStride, ...
   constexpr int kStride = NW;
   const int first = blk_begin + w;
@@ -132,10 +138,11 @@ void decode_mfma_kernel(DecodeParams P) {
   const int ctx_col = sr.row_ctx(qi);                       // this lane's column
   const int ctx_min = sr.row_ctx(c_begin / P.G);            // first column's row
   const int ctx = sr.row_ctx((c_end - 1) / P.G);            // last column's row: the longest
-  const bool bad_ctx = sr.bad;
+  const bool bad_ctx = sr.bad || is.bad || is.start_blk * kBlock > ctx;
   const int nblk = (ctx + kBlock - 1) / kBlock;
   const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
-  const int nparts_s = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
+  const int span = nblk - is.start_blk;  // blocks this pass reads (tail pass: past the shared ones)
+  const int nparts_s = bpp > 0 ? (span + bpp - 1) / bpp : (span > 0 ? 1 : 0);
   if (p >= max(nparts_s, 1)) return;  // partition past the tile's longest context
 
   float m = -INFINITY, lsum = 0.0f;
@@ -271,7 +278,7 @@ void decode_mfma_kernel(DecodeParams P) {
     const int h = g * P.G + c % P.G;
     // Partitions of this column's own context: with one, partition 0 writes
     // the final row; with several, each writes its partial.
-    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
+    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock - is.start_blk;
     const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
     if (np <= 1 ? p != 0 : p >= np) continue;
     float M = sm_m[0][qq];
@@ -289,8 +296,8 @@ void decode_mfma_kernel(DecodeParams P) {
       for (int e = 0; e < 8; ++e) ov[e] += sm_o[v][qq][8 * ch + e] * sc;
     }
     const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
-    if (np > 1) {
-      const size_t part = orow * P.n_parts + p;
+    if (np > 1 || P.always_partial) {
+      const size_t part = orow * P.n_parts + P.part_base + p;
       float* dst = P.ws_o + part * D + 8 * ch;
 #pragma unroll
       for (int e = 0; e < 8; ++e) dst[e] = any_bad ? __builtin_nanf("") : ov[e];
@@ -299,6 +306,9 @@ void decode_mfma_kernel(DecodeParams P) {
         P.ws_ml[2 * part + 1] = any_bad ? __builtin_nanf("") : L;
       }
     } else {
+      // shared-prefix tail pass: fold in the group pass's partials of this row
+      if (P.tail_pass)
+        merge_shared_partials<8>(P, is.bad ? 0 : is.start_blk * kBlock, orow, 8 * ch, D, M, L, ov);
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       float res[8];
 #pragma unroll
@@ -319,7 +329,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int DEPTH = PA_MFMA_DEPTH;
   auto go = [&](auto nw) {
     constexpr int NW = decltype(nw)::value;
-    const dim3 grid(p.Hkv * p.n_tiles, p.n_parts, p.B), block(NW * kWave);
+    const dim3 grid(p.Hkv * p.n_tiles, p.pass_parts, p.pass_items), block(NW * kWave);
     if (p.shared_kv)
       hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared>), grid, block, 0,
                          stream, p);
@@ -329,7 +339,9 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   };
   // A whole context per workgroup: more waves, each with a longer share of
   // its blocks. Split contexts (a partition's few blocks): fewer.
-  if (p.n_parts == 1)
+  if (p.group_start)
+    go(std::integral_constant<int, PA_MFMA_GROUP_WAVES>{});
+  else if (p.pass_parts == 1)
     go(std::integral_constant<int, PA_MFMA_WAVES_UNSPLIT>{});
   else
     go(std::integral_constant<int, PA_MFMA_WAVES>{});

@@ -37,6 +37,11 @@
 #ifndef PA_VALU_WAVES
 #define PA_VALU_WAVES 8
 #endif
+// Waves per workgroup of the shared-prefix tail pass (each sequence's own
+// tokens past the shared ones: short runs of blocks).
+#ifndef PA_VALU_TAIL_WAVES
+#define PA_VALU_TAIL_WAVES 4
+#endif
 #ifndef PA_VALU_DEPTH
 #define PA_VALU_DEPTH 3
 #endif
@@ -132,9 +137,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const int s = gp.z;
   const int g = h / P.G;
 
-  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
+  const ItemStart is = item_start(P, s);
+  const int32_t* bt_row = P.block_tables + (size_t)is.trow * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
-  const int blk_begin = p * bpp;
+  const int blk_begin = is.start_blk + p * bpp;
   const int first = blk_begin + w;       // this wave's blocks: first, first + NW, ...
 
   // Start-up loads, issued before anything waits on them: the wave's first 64
@@ -149,10 +155,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const uint4 qraw = ld16(reinterpret_cast<const char*>(P.q) + row_qo * sizeof(T) + c * 16);
 
   const int ctx = sr.row_ctx(i);         // tokens this row attends over
-  const bool bad_ctx = sr.bad;
+  const bool bad_ctx = sr.bad || is.bad || is.start_blk * kBlock > ctx;
   const int nblk = (ctx + kBlock - 1) / kBlock;
   const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
-  const int nparts_s = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
+  const int span = nblk - is.start_blk;  // blocks this pass reads (tail pass: past the shared ones)
+  const int nparts_s = bpp > 0 ? (span + bpp - 1) / bpp : (span > 0 ? 1 : 0);
   if (p >= max(nparts_s, 1)) return;  // partition past this row's context
 
   float qf[EPL];
@@ -295,8 +302,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   }
 
   // Lanes 0 .. LPT-1 of wave 0 hold the result for chunk c.
-  if (P.partition > 0 && nparts_s > 1) {
-    const size_t part = ((size_t)row * P.Hq + h) * P.n_parts + p;
+  if (P.always_partial || (P.partition > 0 && nparts_s > 1)) {
+    const size_t part = ((size_t)row * P.Hq + h) * P.n_parts + P.part_base + p;
     float* dst = P.ws_o + part * D + c * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dst[e] = bad ? __builtin_nanf("") : outv[e];
@@ -306,6 +313,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
     }
     return;
   }
+  // shared-prefix tail pass: fold in the group pass's partials of this row
+  if (P.tail_pass)
+    merge_shared_partials<EPL>(P, is.bad ? 0 : is.start_blk * kBlock, (size_t)row * P.Hq + h,
+                               c * EPL, D, M, L, outv);
   float res[EPL];
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // empty context -> zeros
 #pragma unroll
@@ -324,11 +335,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   }
 }
 
-template <TilePolicy kPolicy>
+template <TilePolicy kPolicy, int NW>
 hipError_t launch_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
-  constexpr int NW = PA_VALU_WAVES;
   constexpr int DEPTH = PA_VALU_DEPTH;
-  const dim3 grid(p.Hq * p.max_q, p.n_parts, p.B), block(NW * kWave);
+  const dim3 grid(p.Hq * p.max_q, p.pass_parts, p.pass_items), block(NW * kWave);
   if (dtype == 1 && D == 128)
     hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW, DEPTH, kPolicy>), grid, block, 0,
                        stream, p);
@@ -347,8 +357,11 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, int D, hipStream_t stre
 }
 
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
-  return p.shared_kv ? launch_valu<TilePolicy::kShared>(p, dtype, D, stream)
-                     : launch_valu<TilePolicy::kStream>(p, dtype, D, stream);
+  if (p.tail_pass)
+    return p.shared_kv ? launch_valu<TilePolicy::kShared, PA_VALU_TAIL_WAVES>(p, dtype, D, stream)
+                       : launch_valu<TilePolicy::kStream, PA_VALU_TAIL_WAVES>(p, dtype, D, stream);
+  return p.shared_kv ? launch_valu<TilePolicy::kShared, PA_VALU_WAVES>(p, dtype, D, stream)
+                     : launch_valu<TilePolicy::kStream, PA_VALU_WAVES>(p, dtype, D, stream);
 }
 
 }  // namespace pa

@@ -23,6 +23,12 @@ int64_t grid_parts(int32_t max_ctx, int32_t partition) {
   return ((int64_t)max_ctx + partition - 1) / partition;
 }
 
+// Partitions of the shared part of pa_decode_shared (0 when nothing is shared).
+int64_t shared_parts(int32_t max_shared, int32_t partition) {
+  if (max_shared <= 0) return 0;
+  return partition > 0 ? ((int64_t)max_shared + partition - 1) / partition : 1;
+}
+
 int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -213,6 +219,8 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   p.ctx_limit = (int32_t)(cap < max_ctx ? cap : max_ctx);
   p.partition = parts > 1 ? partition : 0;
   p.n_parts = (int32_t)parts;
+  p.pass_parts = (int32_t)parts;
+  p.pass_items = B;
   p.max_q = max_q;
   p.rows = rows;
   p.n_tiles = (int32_t)(((int64_t)max_q * p.G + 15) / 16);
@@ -250,6 +258,107 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return attention(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, B, B, 1, Hq, Hkv,
                    D, bs, NB, MB, max_ctx, scale, partition, workspace, workspace_bytes, flags, dt,
                    stream);
+}
+
+size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_shared,
+                                        int32_t partition) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || max_shared < 0 || partition < 0) return 0;
+  const int64_t nps = shared_parts(max_shared, partition);
+  if (nps == 0) return 0;
+  const size_t rows = (size_t)B * Hq * (size_t)nps;
+  return align_up(rows * 2 * sizeof(float)) + rows * (size_t)D * sizeof(float);
+}
+
+pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* group_start, const int32_t* seq_shared, int32_t B,
+                           int32_t n_groups, int32_t max_group, int32_t max_shared, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB,
+                           int32_t max_ctx, float scale, int32_t partition, void* workspace,
+                           size_t workspace_bytes, uint32_t flags, pa_dtype dt,
+                           hipStream_t stream) {
+  if (B < 0 || n_groups < 0 || max_group < 1 || max_shared < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
+      NB < 0 || MB < 0 || max_ctx < 0 || !dtype_ok(dt) || (flags & ~PA_KV_SHARED) != 0 ||
+      !__builtin_isfinite(scale))
+    return PA_EINVAL;
+  if (Hq % Hkv != 0) return PA_EINVAL;
+  if (partition < 0 || partition % kBs != 0 || max_shared % kBs != 0) return PA_EINVAL;
+  if (max_shared > max_ctx) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (D != 64 && D != 128) return PA_EUNSUPPORTED;
+  // the group pass runs on the matrix-core kernel: bf16, D = 128, one
+  // 16-column tile per kv head (members x query heads of a group)
+  const int32_t G = Hq / Hkv;
+  if (dt != PA_BF16 || D != 128 || (int64_t)max_group * G > 16) return PA_EUNSUPPORTED;
+  if (B > kMaxGridYZ || n_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
+  if (B == 0) return PA_OK;
+  if (n_groups == 0) return PA_EINVAL;
+  if (!out || !q || !k_cache || !v_cache || !context_lens || !group_start || !seq_shared ||
+      (MB > 0 && !block_tables))
+    return PA_EINVAL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_EINVAL;
+  const int64_t nps = shared_parts(max_shared, partition);
+  if (nps > kMaxGridYZ) return PA_EUNSUPPORTED;
+  const size_t need = pa_decode_shared_workspace_bytes(B, Hq, D, max_shared, partition);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
+  if (need > 0 && ((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
+
+  pa::DecodeParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.G = G;
+  p.NB = NB;
+  p.MB = MB;
+  const int64_t cap = (int64_t)MB * kBs;
+  p.ctx_limit = (int32_t)(cap < max_ctx ? cap : max_ctx);
+  p.rows = B;
+  p.qscale = scale * 1.4426950408889634f;
+  p.shared_kv = (flags & PA_KV_SHARED) ? 1 : 0;
+  p.seq_shared = seq_shared;
+  p.n_parts = nps > 0 ? (int32_t)nps : 1;  // partial slots per (row, head)
+  if (nps > 0) {
+    const size_t nrows = (size_t)B * Hq * (size_t)nps;
+    p.ws_ml = static_cast<float*>(workspace);
+    p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      align_up(nrows * 2 * sizeof(float)));
+  }
+
+  // 1. group pass: each group's shared tokens, read once for all its members
+  if (nps > 0) {
+    pa::DecodeParams g = p;
+    g.group_start = group_start;
+    g.max_q = max_group;
+    g.n_tiles = 1;
+    g.partition = nps > 1 ? partition : 0;
+    g.part_base = 0;
+    g.always_partial = 1;
+    g.pass_parts = (int32_t)nps;
+    g.pass_items = n_groups;
+    if (pa::launch_decode_mfma(g, stream) != hipSuccess) return PA_EHIP;
+  }
+  // 2. tail pass: each sequence's own tokens past its shared ones, merged
+  //    with its row's group-pass partials into the final row
+  pa::DecodeParams t = p;
+  t.tail_pass = 1;
+  t.shared_partition = nps > 1 ? partition : 0;
+  t.max_q = 1;
+  t.n_tiles = 1;
+  t.partition = 0;
+  t.pass_parts = 1;
+  t.pass_items = B;
+  const bool mfma = G >= 2;  // bf16, D = 128 here
+  if ((mfma ? pa::launch_decode_mfma(t, stream) : pa::launch_decode_valu(t, dt, D, stream)) !=
+      hipSuccess)
+    return PA_EHIP;
+  return PA_OK;
 }
 
 pa_status pa_multi_query(void* out, const void* q, const void* k_cache, const void* v_cache,

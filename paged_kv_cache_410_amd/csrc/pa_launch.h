@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa_device.h"
+
 namespace pa {
 
 // Everything a decode kernel reads. Lengths are in elements unless noted.
@@ -27,7 +29,69 @@ struct DecodeParams {
   int32_t n_tiles;              // MFMA: 16-column tiles per kv head (rows x heads per group)
   float qscale;                 // scale * log2(e): logits are kept in the log2 domain
   int32_t shared_kv;            // K/V tiles read through the caches (blocks shared by sequences)
+  // Shared-prefix decode (pa_decode_shared), else null / 0:
+  //  group pass: grid z runs over groups of consecutive sequences
+  //    (group_start[j] .. group_start[j+1]-1) that share their first
+  //    seq_shared[group_start[j]] tokens; every member row attends over
+  //    exactly those tokens, read once for the whole group;
+  //  tail pass: sequence s attends over its tokens seq_shared[s] .. ctx - 1,
+  //    merges the group pass's partials of its row and writes the final row.
+  //  The group pass writes partials: partition p goes to slot part_base + p.
+  const int32_t* group_start;   // [n_groups + 1] (group pass)
+  const int32_t* seq_shared;    // [B] shared tokens per sequence, a multiple of 16
+  int32_t tail_pass;            // 1: attend from seq_shared[s] on
+  int32_t part_base;            // first partial slot this pass writes
+  int32_t always_partial;       // write partials even for a single partition
+  int32_t shared_partition;     // tail pass: partition length of the group pass (0 = one)
+  int32_t pass_parts;           // grid y of this pass (partitions)
+  int32_t pass_items;           // grid z of this pass (sequences, or groups)
 };
+
+// Online-softmax merge of the group pass's partials of one row into a tail
+// pass's state (M, L, o: log2-domain max, sum, unnormalised dims), for the n
+// dims this lane holds, starting at dim `dim0` of the row. The group pass
+// wrote ceil(shared / shared_partition) partials (one when not split) at
+// slots 0.. of the row's n_parts.
+template <int N>
+__device__ __forceinline__ void merge_shared_partials(const DecodeParams& P, int shared_tokens,
+                                                      size_t row_head, int dim0, int D, float& M,
+                                                      float& L, float (&o)[N]) {
+  if (shared_tokens <= 0) return;
+  const int bpp = P.shared_partition / 16;
+  const int nps = bpp > 0 ? (shared_tokens / 16 + bpp - 1) / bpp : 1;
+  for (int j = 0; j < nps && j < P.n_parts; ++j) {
+    const size_t part = row_head * P.n_parts + j;
+    const float mj = P.ws_ml[2 * part], lj = P.ws_ml[2 * part + 1];
+    const float* oj = P.ws_o + part * D + dim0;
+    const SoftmaxScales sc = merge_scales(M, mj);
+    L = L * sc.a + lj * sc.b;
+#pragma unroll
+    for (int e = 0; e < N; ++e) o[e] = o[e] * sc.a + oj[e] * sc.b;
+    M = sc.m;
+  }
+}
+
+// Table row and first logical block of work item s (grid z): a sequence, or,
+// in the group pass, a group (whose shared blocks are read through its first
+// member's table). The tail pass starts at the sequence's shared tokens. An
+// out-of-range group start or shared length marks the item bad.
+struct ItemStart {
+  int trow, start_blk;
+  bool bad;
+};
+__device__ __forceinline__ ItemStart item_start(const DecodeParams& P, int s) {
+  ItemStart r{s, 0, false};
+  if (P.group_start) {
+    const int f = P.group_start[s];
+    r.bad = f < 0 || f >= P.rows;
+    r.trow = r.bad ? 0 : f;
+  } else if (P.tail_pass) {
+    const int sh = P.seq_shared[s];
+    r.bad = sh < 0 || sh % 16 != 0 || sh / 16 > P.MB;
+    r.start_blk = r.bad ? 0 : sh / 16;
+  }
+  return r;
+}
 
 // The query rows of sequence s and the context each row attends over.
 // Without query_start (decode) sequence s has one row, row s. With it, the
@@ -39,10 +103,27 @@ struct DecodeParams {
 struct SeqRows {
   int first, n, ctx;
   bool bad;
-  __device__ __forceinline__ int row_ctx(int i) const { return bad ? 0 : ctx - n + i + 1; }
+  int n_causal;  // 1: row i attends ctx - n + i + 1 tokens; 0: every row attends ctx
+  __device__ __forceinline__ int row_ctx(int i) const {
+    return bad ? 0 : n_causal ? ctx - n + i + 1 : ctx;
+  }
 };
 __device__ __forceinline__ SeqRows seq_rows(const DecodeParams& P, int s) {
   SeqRows r;
+  if (P.group_start) {
+    // group pass: group s; every row attends over the group's shared tokens
+    // (no causal offset: n is set so that row_ctx(i) = ctx for the last row,
+    // and the group kernel gives every column the same context)
+    r.first = P.group_start[s];
+    r.n = P.group_start[s + 1] - r.first;
+    const bool rows_ok = r.n >= 1 && r.n <= P.max_q && r.first >= 0 && r.first + r.n <= P.rows;
+    r.ctx = rows_ok ? P.seq_shared[r.first] : 0;
+    r.bad = !rows_ok || r.ctx < 0 || r.ctx > P.ctx_limit || r.ctx % 16 != 0;
+    if (!rows_ok) r.n = 0;
+    r.n_causal = 0;
+    return r;
+  }
+  r.n_causal = 1;
   r.first = s;
   r.n = 1;
   if (P.query_start) {

@@ -333,3 +333,105 @@ def test_native_prefix_bm_rejects_bad_arguments(palib):
     assert lib.pa_bm_append_tokens(h, s.value, None, 2, slots.ctypes.data, pair.ctypes.data,
                                    ctypes.byref(npairs)) == -1
     lib.pa_bm_destroy(h)
+
+
+# ------------------------------------------------ shared-prefix decode (host side)
+def check_groups(bt, cl, max_group, gs, sh):
+    """What pa_decode_shared needs of a grouping, and the planner's greedy
+    rule: a group ends only where the next sequence shares no leading whole
+    block with the group's first member, or the group is full."""
+    B = len(cl)
+    assert gs[0] == 0 and gs[-1] == B and np.all(np.diff(gs) >= 1)
+    assert np.diff(gs).max(initial=0) <= max_group
+    for j in range(len(gs) - 1):
+        a, b = int(gs[j]), int(gs[j + 1])
+        S = int(sh[a])
+        assert np.all(sh[a:b] == S) and S % 16 == 0
+        if b - a == 1:
+            assert S == 0
+        for s in range(a, b):
+            assert S <= cl[s]
+            assert np.array_equal(bt[s, :S // 16], bt[a, :S // 16])
+        if b < B and b - a < max_group:
+            k = min(cl[a], cl[b]) // 16
+            assert k == 0 or bt[b, 0] != bt[a, 0] or bt[a, 0] < 0
+
+
+def test_shared_groups_on_workload_tables(palib):
+    import paged_kv_cache_410_amd as pa
+    from paged_kv_cache_410_amd import workloads
+    for name, expect in (("cow", (16, 8, 1008)), ("prefix", (8, 16, 1024)), ("13b", None)):
+        spec = workloads.CONFIGS[name]
+        tb = workloads.make_tables(spec, oracle_bm.PrefixBlockManager)
+        gs, sh = pa.shared_groups(tb.block_tables, tb.context_lens, 16)
+        check_groups(tb.block_tables, tb.context_lens, 16, gs, sh)
+        if expect is None:      # nothing is shared: every sequence alone
+            assert len(gs) == spec.B + 1 and not sh.any()
+        else:
+            # copy-on-write: 16 prompts x 8 samples share each prompt's whole
+            # blocks (the last, partly filled prompt block was copied);
+            # prefix: the requests share their 1024-token prefix
+            n, size, shared = expect
+            assert len(gs) - 1 == n and np.all(np.diff(gs) == size) and np.all(sh == shared)
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(seed=st.integers(0, 2**31 - 1), max_group=st.integers(1, 6))
+def test_shared_groups_invariants_on_forked_tables(palib, seed, max_group):
+    """Tables from the oracle's manager after random forks and appends."""
+    import paged_kv_cache_410_amd as pa
+    rng = np.random.default_rng(seed)
+    bm = oracle_bm.BlockManager(400, 16, list(rng.permutation(400)))
+    seqs = []
+    for _ in range(rng.integers(1, 4)):
+        s = bm.add_seq()
+        for _ in range(rng.integers(0, 70)):
+            bm.append(s)
+        seqs.append(s)
+        for _ in range(rng.integers(0, 4)):
+            c = bm.fork(s)
+            for _ in range(rng.integers(0, 40)):
+                bm.append(c)
+            seqs.append(c)
+    MB = max(len(bm.tables[s]) for s in seqs) + 1
+    bt = np.full((len(seqs), MB), -1, np.int32)
+    for i, s in enumerate(seqs):
+        bt[i, :len(bm.tables[s])] = bm.tables[s]
+    cl = np.array([bm.seq_len(s) for s in seqs], np.int32)
+    gs, sh = pa.shared_groups(bt, cl, max_group)
+    check_groups(bt, cl, max_group, gs, sh)
+
+
+def shared_args(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, gs=FAKE, sh=FAKE, B=8, ng=2,
+             mg=4, max_shared=64, Hq=8, Hkv=8, D=128, bs=16, NB=10, MB=8, max_ctx=128,
+             scale=0.1, partition=0, ws=FAKE, ws_bytes=1 << 30, flags=0, dt=1, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "k", "v", "bt", "cl", "gs", "sh", "B", "ng", "mg",
+                           "max_shared", "Hq", "Hkv", "D", "bs", "NB", "MB", "max_ctx", "scale",
+                           "partition", "ws", "ws_bytes", "flags", "dt", "stream")]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gs=None), -1), (dict(sh=None), -1), (dict(q=None), -1), (dict(ng=0), -1),
+    (dict(mg=0), -1), (dict(max_shared=24), -1), (dict(max_shared=256), -1),
+    (dict(partition=8), -1), (dict(Hq=6, Hkv=4), -1), (dict(scale=float("nan")), -1),
+    (dict(dt=0), -2), (dict(D=64), -2), (dict(Hq=32, Hkv=4, mg=3), -2), (dict(bs=32), -2),
+    (dict(ws=None), -3), (dict(ws_bytes=100), -3), (dict(ws=FAKE + 16), -1),
+    (dict(flags=2), -1), (dict(B=70000), -2),
+])
+def test_decode_shared_rejects_bad_arguments(palib, kw, status):
+    assert palib.lib().pa_decode_shared(*shared_args(**kw)) == status
+
+
+def test_decode_shared_workspace_and_empty_batch(palib):
+    lib = palib.lib()
+    assert lib.pa_decode_shared(*shared_args(B=0, q=None, out=None)) == 0
+    # one slot of (D + 2) floats per (row, head) and shared partition: 100 tokens
+    # in partitions of 64 -> 2; nothing shared -> no workspace
+    n = lib.pa_decode_shared_workspace_bytes(4, 8, 128, 100, 64)
+    rows = 4 * 8 * 2
+    assert n == (rows * 8 + 255) // 256 * 256 + rows * 128 * 4
+    assert lib.pa_decode_shared_workspace_bytes(4, 8, 128, 100, 0) == \
+        (4 * 8 * 8 + 255) // 256 * 256 + 4 * 8 * 128 * 4
+    assert lib.pa_decode_shared_workspace_bytes(4, 8, 128, 0, 64) == 0

@@ -1,0 +1,134 @@
+"""GPU parity of pa_decode_shared: decode attention that reads each group's
+shared blocks once for all the group's sequences, then each sequence's own
+tokens, and merges the two partials.
+
+Outputs must lie within max-abs 2e-3 (fp32) / 1.5e-2 (bf16) of the fp64 oracle
+on the same inputs, as pa_decode's do. Unused pool slots are poisoned with NaN,
+so a read past a context or outside the shared part would show.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_cases import TOL, Step, max_abs_err, oracle_view, say
+from test_gpu_parity import SMALL
+from paged_kv_cache_410_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_410_amd as m
+    return m
+
+
+def groups_of(pa, st, max_group=None):
+    G = st.spec.Hq // st.spec.Hkv
+    mg = max_group or 16 // G
+    gs, sh = pa.shared_groups(st.tb.block_tables, st.tb.context_lens, mg)
+    return gs, sh, mg
+
+
+def run_shared(pa, st, gs, sh, mg, partition, context_lens=None):
+    cl = st.context_lens if context_lens is None else context_lens
+    return pa.decode_shared(st.q, st.k_cache, st.v_cache, st.block_tables, cl,
+                            torch.from_numpy(gs).cuda(), torch.from_numpy(sh).cuda(),
+                            st.spec.scale, st.max_ctx, mg, int(sh.max()), partition=partition)
+
+
+@pytest.mark.parametrize("name", ["cow_small", "cow_gqa", "prefix_small", "mha_bf16", "gqa8",
+                                  "long_mha"])
+@pytest.mark.parametrize("partition", [0, 16, 48, 512])
+def test_decode_shared_matches_oracle(pa, name, partition):
+    spec = SMALL[name]
+    st = Step(spec, poison=True)
+    st.run_cache_ops(pa)
+    gs, sh, mg = groups_of(pa, st)
+    say(f"[decode_shared] {name} partition={partition} groups={len(gs) - 1} "
+        f"shared={sorted(set(sh.tolist()))}")
+    out = run_shared(pa, st, gs, sh, mg, partition)
+    ref = st.decode(pa, partition=partition or None)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert np.all(np.isfinite(o)), "NaN-poisoned unused slots leaked into the output"
+    err = max_abs_err(out, st.expect)
+    say(f"    max abs err {err:.3e} (tol {TOL[spec.dtype]})")
+    assert err <= TOL[spec.dtype]
+    assert float((out.float() - ref.float()).abs().max()) <= TOL[spec.dtype]
+
+
+@pytest.mark.parametrize("max_group", [1, 2, 3])
+def test_decode_shared_smaller_groups(pa, max_group):
+    st = Step(SMALL["cow_small"], poison=True)
+    st.run_cache_ops(pa)
+    gs, sh, mg = groups_of(pa, st, max_group)
+    assert np.diff(gs).max() <= max_group
+    out = run_shared(pa, st, gs, sh, mg, 32)
+    torch.cuda.synchronize()
+    assert max_abs_err(out, st.expect) <= TOL["bf16"]
+
+
+def test_decode_shared_empty_tails_and_contexts(pa):
+    """A sequence whose whole context is shared (empty own part), and an empty
+    sequence in a group of its own."""
+    st = Step(SMALL["cow_small"], poison=True, oracle_full=False)
+    st.run_cache_ops(pa)
+    gs, sh, mg = groups_of(pa, st)
+    cl = st.tb.context_lens.copy()
+    members = [s for s in range(st.spec.B) if sh[s] > 0]
+    cl[members[1]] = sh[members[1]]          # nothing of its own
+    # a last, empty sequence alone: make the last group's last member a singleton
+    last = st.spec.B - 1
+    gs2 = np.concatenate([gs[:-1], [last, st.spec.B]]).astype(np.int32)
+    sh2 = sh.copy()
+    sh2[last] = 0
+    cl[last] = 0
+    expect = oracle.decode(oracle_view(st.q_bits), oracle_view(st.k_after),
+                           oracle_view(st.v_after), st.tb.block_tables, cl, st.spec.scale)
+    out = run_shared(pa, st, gs2, sh2, mg, 16, context_lens=torch.from_numpy(cl).cuda())
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert np.count_nonzero(o[last]) == 0
+    assert np.all(np.isfinite(o))
+    assert float(np.max(np.abs(o - expect))) <= TOL["bf16"]
+
+
+def test_decode_shared_bad_shared_length_poisons_only_its_row(pa):
+    st = Step(SMALL["cow_small"], oracle_full=False)
+    st.run_cache_ops(pa)
+    gs, sh, mg = groups_of(pa, st)
+    good = run_shared(pa, st, gs, sh, mg, 0).float().cpu()
+    s_bad = int(gs[0]) + 1                   # a member that is not its group's first
+    bad = sh.copy()
+    bad[s_bad] = 8                           # not a multiple of the block size
+    out = run_shared(pa, st, gs, bad, mg, 0).float().cpu()
+    assert torch.isnan(out[s_bad]).all()
+    keep = [s for s in range(st.spec.B) if s != s_bad]
+    assert torch.equal(out[keep], good[keep])
+
+
+@pytest.mark.parametrize("name", ["cow", "prefix"])
+def test_decode_shared_full_config(pa, name):
+    """Full-size sharing workloads in the launch configuration the benchmark
+    times: sampled outputs against the oracle, properties at every row."""
+    from test_gpu_full_configs import sample_rows
+    spec = workloads.CONFIGS[name]
+    st = Step(spec, values_device="cuda", oracle_full=False)
+    st.run_cache_ops(pa, fused=True)
+    gs, sh, mg = groups_of(pa, st)
+    say(f"[decode_shared full config] {name}: groups={len(gs) - 1} shared={sorted(set(sh.tolist()))}")
+    out = run_shared(pa, st, gs, sh, mg, 0)
+    torch.cuda.synchronize()
+    rows = sample_rows(st.tb, spec.Hq, 40, seed=7)
+    expect = st.oracle_decode(pairs=rows)
+    got = out.float().cpu().numpy()
+    err = max(float(np.max(np.abs(got[s, h] - expect[i]))) for i, (s, h) in enumerate(rows))
+    say(f"    sampled max abs err {err:.3e} (tol {TOL[spec.dtype]})")
+    assert err <= TOL[spec.dtype]
+    assert np.all(np.isfinite(got))
+    assert np.abs(got).max() <= 8.0
