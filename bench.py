@@ -274,20 +274,23 @@ def main():
         max_group = 16 // (spec.Hq // spec.Hkv)
         gs, sh = pa.shared_groups(tb.block_tables, tb.context_lens, max_group)
         if sh.any():
-            # once grouped, do blocks still repeat (a prefix shared by several
-            # groups)? Then the caches serve the repeats, else stream.
-            reads = []
+            # once grouped, do blocks still repeat? In the groups' shared parts
+            # (one prefix over several groups), or among the sequences' own
+            # blocks? Then that pass reads through the caches, else streams.
+            shared_reads, own_reads = [], []
             for j in range(len(gs) - 1):
                 a, b = int(gs[j]), int(gs[j + 1])
                 nsh = int(sh[a]) // 16
-                reads += tb.block_tables[a, :nsh].tolist()
+                shared_reads += tb.block_tables[a, :nsh].tolist()
                 for s_ in range(a, b):
-                    reads += tb.block_tables[s_, nsh:(int(tb.context_lens[s_]) + 15) // 16].tolist()
-            group_repeats = len(set(reads)) < len(reads)
+                    own_reads += tb.block_tables[s_, nsh:(int(tb.context_lens[s_]) + 15) // 16].tolist()
+            groups_overlap = len(set(shared_reads)) < len(shared_reads)
+            own_repeats = len(set(own_reads)) < len(own_reads)
             sp = args.shared_partition
             groups = dict(group_start=torch.from_numpy(gs).to(dev),
                           seq_shared=torch.from_numpy(sh).to(dev), max_group=max_group,
-                          max_shared=int(sh.max()), partition=sp, repeats=group_repeats,
+                          max_shared=int(sh.max()), partition=sp, own_repeats=own_repeats,
+                          groups_overlap=groups_overlap,
                           workspace=torch.empty(pa.decode_shared_workspace_bytes(
                               spec.B, spec.Hq, spec.D, int(sh.max()), sp), dtype=torch.uint8,
                               device=dev))
@@ -300,7 +303,8 @@ def main():
                              groups["seq_shared"], spec.scale, max_ctx, groups["max_group"],
                              groups["max_shared"], partition=groups["partition"], out=dest,
                              workspace=groups["workspace"],
-                             shared_kv=shared and groups["repeats"])
+                             shared_kv=shared and groups["own_repeats"],
+                             groups_overlap=shared and groups["groups_overlap"])
         elif spec.chunk:
             pa.multi_query(q, k_cache, v_cache, tables, cl, qs, spec.scale, max_ctx, max_q,
                            partition=partition, out=dest, workspace=workspace, shared_kv=shared)
@@ -497,7 +501,8 @@ def main():
                                      dict(groups=int(groups["group_start"].shape[0] - 1),
                                           max_shared=groups["max_shared"],
                                           shared_partition=groups["partition"],
-                                          blocks_repeat_across_groups=groups["repeats"])),
+                                          shared_parts_overlap=groups["groups_overlap"],
+                                          own_blocks_repeat=groups["own_repeats"])),
                    "parallelism": "none (one GPU)"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(T / (ms_step * 1e-3), 1),

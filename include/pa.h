@@ -74,6 +74,13 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
  *                 Results are the same either way; only speed differs.
  */
 #define PA_KV_SHARED 1u
+/*
+ *   PA_KV_SHARED_GROUPS  pa_decode_shared only: the shared blocks of different
+ *                 groups overlap (one prefix split over several groups); the
+ *                 group pass then reads through the caches. PA_KV_SHARED there
+ *                 applies to each sequence's own blocks (the tail pass).
+ */
+#define PA_KV_SHARED_GROUPS 2u
 
 /* Static, human-readable text for a status code. Never NULL. */
 const char* pa_status_str(pa_status s);
@@ -291,6 +298,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
  *   workspace    at least pa_decode_shared_workspace_bytes(B, Hq, D,
  *                max_shared, partition) bytes, 256-byte aligned (may be NULL
  *                when that is 0)
+ *   flags        PA_KV_SHARED (blocks past the shared part read by several
+ *                sequences) and/or PA_KV_SHARED_GROUPS (shared parts of
+ *                different groups overlap); other bits give PA_EINVAL
  * Other arguments and error rows as pa_decode. Two launches: the shared part
  * of every group (one read of its blocks for all members' query heads, on
  * the matrix cores, into the workspace), then every sequence's own tokens,

@@ -22,7 +22,8 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import PA_BF16, PA_ENOBLOCKS, PA_F32, PA_KV_SHARED, PAError, check, lib  # noqa: F401
+from ._lib import (PA_BF16, PA_ENOBLOCKS, PA_F32, PA_KV_SHARED, PA_KV_SHARED_GROUPS,  # noqa: F401
+                   PAError, check, lib)
 
 __all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "check_slots", "check_pairs",
            "check_tables", "decode", "multi_query", "shares_blocks",
@@ -276,11 +277,13 @@ def decode_shared_workspace_bytes(B, Hq, D, max_shared, partition):
 
 def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, seq_shared,
                   scale, max_ctx, max_group, max_shared, partition=0, out=None, workspace=None,
-                  shared_kv=True):
+                  shared_kv=False, groups_overlap=False):
     """pa_decode for sequences that share leading blocks (pa_decode_shared):
     group_start int32 [n_groups + 1] and seq_shared int32 [B] on the device,
     as shared_groups() gives them; max_group and max_shared bound them.
-    partition splits the shared part (0 = one partition)."""
+    partition splits the shared part (0 = one partition). shared_kv: blocks
+    past the shared parts are read by several sequences; groups_overlap: the
+    shared parts of different groups overlap (PA_KV_SHARED_GROUPS)."""
     NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
     for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"),
                     (group_start, "group_start"), (seq_shared, "seq_shared")):
@@ -310,7 +313,8 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, 
             block_tables.data_ptr(), context_lens.data_ptr(), group_start.data_ptr(),
             seq_shared.data_ptr(), B, n_groups, int(max_group), int(max_shared), Hq, Hkv, D, bs,
             NB, MB, int(max_ctx), float(scale), int(partition), workspace.data_ptr(), ws_bytes,
-            PA_KV_SHARED if shared_kv else 0, _dt(q), _stream(dev)), "pa_decode_shared")
+            (PA_KV_SHARED if shared_kv else 0) | (PA_KV_SHARED_GROUPS if groups_overlap else 0),
+            _dt(q), _stream(dev)), "pa_decode_shared")
     return out
 
 

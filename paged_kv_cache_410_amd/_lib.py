@@ -58,6 +58,7 @@ SIGNATURES = {
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOBLOCKS = 0, -1, -2, -3, -4, -5
 PA_F32, PA_BF16 = 0, 1
 PA_KV_SHARED = 1
+PA_KV_SHARED_GROUPS = 2
 
 _lib = None
 

@@ -418,7 +418,7 @@ def shared_args(**kw):
     (dict(partition=8), -1), (dict(Hq=6, Hkv=4), -1), (dict(scale=float("nan")), -1),
     (dict(dt=0), -2), (dict(D=64), -2), (dict(Hq=32, Hkv=4, mg=3), -2), (dict(bs=32), -2),
     (dict(ws=None), -3), (dict(ws_bytes=100), -3), (dict(ws=FAKE + 16), -1),
-    (dict(flags=2), -1), (dict(B=70000), -2),
+    (dict(flags=4), -1), (dict(B=70000), -2),
 ])
 def test_decode_shared_rejects_bad_arguments(palib, kw, status):
     assert palib.lib().pa_decode_shared(*shared_args(**kw)) == status

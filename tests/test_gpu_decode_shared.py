@@ -132,3 +132,19 @@ def test_decode_shared_full_config(pa, name):
     assert err <= TOL[spec.dtype]
     assert np.all(np.isfinite(got))
     assert np.abs(got).max() <= 8.0
+
+
+@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa"])
+def test_decode_shared_cache_flags_give_identical_bits(pa, name):
+    """PA_KV_SHARED and PA_KV_SHARED_GROUPS change how tiles are cached, never
+    the result."""
+    st = Step(SMALL[name], oracle_full=False)
+    st.run_cache_ops(pa)
+    gs, sh, mg = groups_of(pa, st)
+    args = (st.q, st.k_cache, st.v_cache, st.block_tables, st.context_lens,
+            torch.from_numpy(gs).cuda(), torch.from_numpy(sh).cuda(), st.spec.scale,
+            st.max_ctx, mg, int(sh.max()))
+    outs = [pa.decode_shared(*args, partition=16, shared_kv=a, groups_overlap=b)
+            for a in (False, True) for b in (False, True)]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
