@@ -37,6 +37,11 @@
 #ifndef PA_VALU_WAVES
 #define PA_VALU_WAVES 8
 #endif
+// Waves per workgroup when an unsplit grid has few work items (at most 8 per
+// compute unit): longer contexts per item, each shared by more waves.
+#ifndef PA_VALU_WAVES_FEW
+#define PA_VALU_WAVES_FEW 16
+#endif
 // Waves per workgroup of the shared-prefix tail pass (each sequence's own
 // tokens past the shared ones: short runs of blocks).
 #ifndef PA_VALU_TAIL_WAVES
@@ -345,9 +350,14 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, int D, hipStream_t stre
   else if (dtype == 1 && D == 64)
     hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW, DEPTH, kPolicy>), grid, block, 0,
                        stream, p);
-  else if (dtype == 0 && D == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW, DEPTH, kPolicy>), grid, block, 0,
-                       stream, p);
+  else if (dtype == 0 && D == 128) {
+    // fp32 rows of 128 need ~220 registers: at most 8 waves per workgroup
+    if constexpr (NW <= 8)
+      hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW, DEPTH, kPolicy>), grid, block, 0,
+                         stream, p);
+    else
+      return hipErrorInvalidValue;
+  }
   else if (dtype == 0 && D == 64)
     hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW, DEPTH, kPolicy>), grid, block, 0,
                        stream, p);
@@ -360,6 +370,9 @@ hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream
   if (p.tail_pass)
     return p.shared_kv ? launch_valu<TilePolicy::kShared, PA_VALU_TAIL_WAVES>(p, dtype, D, stream)
                        : launch_valu<TilePolicy::kStream, PA_VALU_TAIL_WAVES>(p, dtype, D, stream);
+  if (p.few_items)
+    return p.shared_kv ? launch_valu<TilePolicy::kShared, PA_VALU_WAVES_FEW>(p, dtype, D, stream)
+                       : launch_valu<TilePolicy::kStream, PA_VALU_WAVES_FEW>(p, dtype, D, stream);
   return p.shared_kv ? launch_valu<TilePolicy::kShared, PA_VALU_WAVES>(p, dtype, D, stream)
                      : launch_valu<TilePolicy::kStream, PA_VALU_WAVES>(p, dtype, D, stream);
 }

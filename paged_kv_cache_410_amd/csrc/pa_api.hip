@@ -221,6 +221,13 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   p.n_parts = (int32_t)parts;
   p.pass_parts = (int32_t)parts;
   p.pass_items = B;
+  // few long work items: wider workgroups (measured on the 7B-shape batch:
+  // 2048 (sequence, head) items, 176 vs 180 us; the 13B-shape's 5120 items
+  // keep 8 waves; fp32 rows of 128 keep 8 waves for registers)
+  p.few_items = parts == 1 && !(dt == PA_F32 && D == 128) &&
+                        (int64_t)B * Hq * max_q <= 8 * (int64_t)device_cus()
+                    ? 1
+                    : 0;
   p.max_q = max_q;
   p.rows = rows;
   p.n_tiles = (int32_t)(((int64_t)max_q * p.G + 15) / 16);

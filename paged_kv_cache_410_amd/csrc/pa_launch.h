@@ -43,6 +43,7 @@ struct DecodeParams {
   int32_t part_base;            // first partial slot this pass writes
   int32_t always_partial;       // write partials even for a single partition
   int32_t shared_partition;     // tail pass: partition length of the group pass (0 = one)
+  int32_t few_items;            // vector kernel: an unsplit grid with at most 8 items per CU
   int32_t pass_parts;           // grid y of this pass (partitions)
   int32_t pass_items;           // grid z of this pass (sequences, or groups)
 };
