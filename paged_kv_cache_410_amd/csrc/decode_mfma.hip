@@ -91,7 +91,9 @@ void decode_mfma_kernel(DecodeParams P) {
   const ItemStart is = item_start(P, s);
   const int32_t* bt_row = P.block_tables + (size_t)is.trow * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
-  const int blk_begin = is.start_blk + p * bpp;
+  // (the tail pass is unsplit and walks the same blocks as an unsplit call,
+  // from its first block past the shared ones: see k0 below)
+  const int blk_begin = p * bpp;
   // this wave's blocks: first, first + kStride, ...
   constexpr int kStride = NW;
   const int first = blk_begin + w;
@@ -238,9 +240,11 @@ void decode_mfma_kernel(DecodeParams P) {
   // This wave's blocks: first + k * kStride, k < nk, through a ring of DEPTH tiles.
   {
     const int nk = first < blk_end ? (blk_end - first + kStride - 1) / kStride : 0;
+    // tail pass: skip this wave's blocks inside the shared part
+    const int k0 = is.start_blk > first ? (is.start_blk - first + kStride - 1) / kStride : 0;
     uint4 kb[DEPTH][4], vb[DEPTH][4];
     block_pipeline<DEPTH>(
-        bt_row, first, kStride, nk, lane, ids0,
+        bt_row, first, kStride, k0, nk, lane, ids0,
         [&](int d, int b, int k, bool exists) {
           load(kb[d], vb[d], b, first + k * kStride, exists);
         },

@@ -145,7 +145,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const ItemStart is = item_start(P, s);
   const int32_t* bt_row = P.block_tables + (size_t)is.trow * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
-  const int blk_begin = is.start_blk + p * bpp;
+  // (the tail pass is unsplit and walks the same blocks as an unsplit call,
+  // from its first block past the shared ones: see k0 below)
+  const int blk_begin = p * bpp;
   const int first = blk_begin + w;       // this wave's blocks: first, first + NW, ...
 
   // Start-up loads, issued before anything waits on them: the wave's first 64
@@ -257,9 +259,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   // This wave's blocks: first + k * NW, k < nk, through a ring of DEPTH tiles.
   {
     const int nk = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
+    // tail pass: skip this wave's blocks inside the shared part
+    const int k0 = is.start_blk > first ? (is.start_blk - first + NW - 1) / NW : 0;
     uint4 kb[DEPTH][NLD], vb[DEPTH][NLD];
     block_pipeline<DEPTH>(
-        bt_row, first, NW, nk, lane, ids0,
+        bt_row, first, NW, k0, nk, lane, ids0,
         [&](int d, int b, int k, bool exists) { load(kb[d], vb[d], b, first + k * NW, exists); },
         [&](int d, int k) { consume(kb[d], vb[d], first + k * NW); });
   }

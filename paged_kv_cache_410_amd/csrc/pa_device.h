@@ -238,7 +238,7 @@ __device__ __forceinline__ void ld16_lds(rsrc_t r, void* lds, int off) {
 }
 
 // Software pipeline over the blocks one wave reads: logical blocks
-// first + k * stride, k = 0 .. n-1, of one block-table row.
+// first + k * stride of one block-table row, for k = k0 .. k1 - 1.
 //   load(slot, b, k, exists) issue the K/V tile loads of physical block b,
 //                           the wave's k-th block, into ring slot `slot`;
 //                           exists == false asks for an empty load (past the
@@ -247,14 +247,16 @@ __device__ __forceinline__ void ld16_lds(rsrc_t r, void* lds, int off) {
 // Every step refills one slot unconditionally and only the compute is
 // branched on, so the compiler sees the same loads in flight on every path
 // and waits for exactly the slot it consumes (loads complete in order).
-// Block ids are read from the table 64 at a time (lane j holds the id of the
-// chunk's j-th block, broadcast with readlane): no table read sits between
-// two tile prefetches, where it would drain the ring. Tiles are prefetched
-// DEPTH - 1 blocks ahead; the ring drains once per 64 blocks.
+// Block ids are read from the table 64 at a time (lane j of chunk c holds the
+// id of block first + (64 c + j) * stride, broadcast with readlane): no table
+// read sits between two tile prefetches, where it would drain the ring.
+// Tiles are prefetched DEPTH - 1 blocks ahead; the ring drains once per chunk.
 //
-// ids0 is the first chunk's ids, loaded by the caller (first_chunk_ids) before
-// it waits on anything else, so the table read overlaps the kernel's other
-// start-up loads.
+// ids0 is chunk 0, loaded by the caller (first_chunk_ids) before it waits on
+// anything else, so the table read overlaps the kernel's other start-up
+// loads. A wave that starts further on (k0 > 0: the shared-prefix tail pass,
+// which learns k0 only from a load of its own) still takes its ids from ids0
+// when k0 < 64.
 __device__ __forceinline__ int first_chunk_ids(const int32_t* row, int first, int stride, int lim,
                                                int lane) {
   const int i = first + lane * stride;
@@ -262,22 +264,24 @@ __device__ __forceinline__ int first_chunk_ids(const int32_t* row, int first, in
 }
 
 template <int DEPTH, typename Load, typename Consume>
-__device__ __forceinline__ void block_pipeline(const int32_t* row, int first, int stride, int n,
-                                               int lane, int ids0, Load&& load, Consume&& consume) {
-  for (int c0 = 0; c0 < n; c0 += kWave) {
-    const int cn = min(kWave, n - c0);
-    const int ids = c0 == 0 ? ids0 : (lane < cn ? row[first + (c0 + lane) * stride] : -1);
+__device__ __forceinline__ void block_pipeline(const int32_t* row, int first, int stride, int k0,
+                                               int k1, int lane, int ids0, Load&& load,
+                                               Consume&& consume) {
+  for (int c0 = k0 / kWave * kWave; c0 < k1; c0 += kWave) {
+    const int ids = c0 == 0 ? ids0 : (c0 + lane < k1 ? row[first + (c0 + lane) * stride] : -1);
+    const int lo = max(k0, c0) - c0;        // this chunk's first lane
+    const int cn = min(kWave, k1 - c0) - lo;  // and its block count
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d)
-      load(d, __builtin_amdgcn_readlane(ids, d), c0 + d, d < cn);
-    for (int k0 = 0; k0 < cn; k0 += DEPTH) {
+      load(d, __builtin_amdgcn_readlane(ids, min(lo + d, kWave - 1)), c0 + lo + d, d < cn);
+    for (int j0 = 0; j0 < cn; j0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        const int k = k0 + d;
-        const int kl = k + DEPTH - 1;
-        load((d + DEPTH - 1) % DEPTH, __builtin_amdgcn_readlane(ids, min(kl, kWave - 1)), c0 + kl,
-             kl < cn);
-        if (k < cn) consume(d, c0 + k);
+        const int j = j0 + d;
+        const int jl = j + DEPTH - 1;
+        load((d + DEPTH - 1) % DEPTH, __builtin_amdgcn_readlane(ids, min(lo + jl, kWave - 1)),
+             c0 + lo + jl, jl < cn);
+        if (j < cn) consume(d, c0 + lo + j);
       }
     }
   }
