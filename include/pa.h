@@ -207,6 +207,20 @@ pa_status pa_check_tables(const int32_t* block_tables, const int32_t* context_le
                           hipStream_t stream);
 
 /*
+ * pa_check_groups — [P1] section 3: pa_decode_shared reads a group's shared
+ * blocks once, through its first member's table. Counts the groups whose
+ * bounds are malformed (not in order from 0 to B, empty, or larger than
+ * max_group) and the members of well-formed groups whose shared length
+ * differs from the first member's, is not a multiple of bs, exceeds the
+ * member's context or table, or whose first S / bs table entries differ from
+ * the first member's. Cost O(B * MB).
+ */
+pa_status pa_check_groups(const int32_t* group_start, const int32_t* seq_shared,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t B, int32_t n_groups, int32_t max_group, int32_t MB,
+                          int32_t bs, int32_t* count, hipStream_t stream);
+
+/*
  * pa_decode_default_partition — split-context partition size (tokens) the
  * library would pick for this shape on the current device: 0 (no split) when
  * one workgroup per (sequence, kv head) already fills the GPU, else a

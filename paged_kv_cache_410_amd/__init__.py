@@ -29,7 +29,7 @@ __all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "check_slots"
            "check_tables", "decode", "multi_query", "shares_blocks",
            "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError", "shared_groups", "decode_shared",
-           "decode_shared_workspace_bytes"]
+           "decode_shared_workspace_bytes", "check_groups"]
 
 BLOCK_SIZE = 16
 
@@ -185,6 +185,19 @@ def check_tables(block_tables, context_lens, num_blocks, max_ctx):
     return _count(dev, lambda c, st: lib().pa_check_tables(
         block_tables.data_ptr(), context_lens.data_ptr(), B, MB, num_blocks, max_ctx,
         BLOCK_SIZE, c, st), "pa_check_tables")
+
+
+def check_groups(group_start, seq_shared, block_tables, context_lens, max_group):
+    """Violations of what pa_decode_shared takes on trust (pa_check_groups)."""
+    for t, name in ((group_start, "group_start"), (seq_shared, "seq_shared"),
+                    (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _i32(t, name)
+    B, MB = block_tables.shape
+    n = group_start.shape[0] - 1
+    dev = _dev(group_start, seq_shared, block_tables, context_lens)
+    return _count(dev, lambda c, st: lib().pa_check_groups(
+        group_start.data_ptr(), seq_shared.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), B, n, int(max_group), MB, 16, c, st), "pa_check_groups")
 
 
 def copy_blocks(k_cache, v_cache, pairs):

@@ -25,6 +25,8 @@ SIGNATURES = {
     "pa_check_slots": (c_i32, [c_vp, c_i32, c_vp, c_vp]),
     "pa_check_pairs": (c_i32, [c_vp, c_i32, c_i32, c_vp, c_vp]),
     "pa_check_tables": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "pa_check_groups": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
+                                c_vp]),
     "pa_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pa_decode_default_partition": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),

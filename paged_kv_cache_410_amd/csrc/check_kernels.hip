@@ -10,6 +10,10 @@
 //   - attention reads each sequence's blocks through its table (section 2):
 //     every entry below the context length must name a pool block, and the
 //     length must lie within the table and the caller's bound.
+//   - shared-prefix decode reads a group's shared blocks once, through its
+//     first member's table (section 3: sharers point at the same blocks):
+//     the groups must cover the batch in order, and every member must share
+//     the same whole blocks, inside its own context.
 // Each check is two launches on the caller's stream: one thread clears the
 // counter, then the count is added up with one atomic add per wave.
 #include "pa_device.h"
@@ -90,6 +94,47 @@ __global__ void check_tables_kernel(const int32_t* __restrict__ bt,
   count_violations(bad, count);
 }
 
+// Group j violates when its bounds are out of order or outside [0, B], when
+// it is empty or larger than max_group, or (j = 0, j = n - 1) when the groups
+// do not start at 0 and end at B. Each member s of a well-formed group
+// violates when its shared length differs from the first member's, is not a
+// multiple of 16, exceeds its context or its table, or when one of its first
+// S / 16 table entries differs from the first member's.
+__global__ void check_groups_kernel(const int32_t* __restrict__ group_start,
+                                    const int32_t* __restrict__ seq_shared,
+                                    const int32_t* __restrict__ bt,
+                                    const int32_t* __restrict__ ctx_lens, int32_t B,
+                                    int32_t n_groups, int32_t max_group, int32_t MB,
+                                    int32_t* count) {
+  const int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+  int32_t bad = 0;
+  if (j < n_groups) {
+    const int32_t a = group_start[j], b = group_start[j + 1];
+    const bool ok = a >= 0 && b <= B && b > a && b - a <= max_group && (j > 0 || a == 0) &&
+                    (j < n_groups - 1 || b == B);
+    if (!ok) {
+      bad = 1;
+    } else {
+      const int32_t S = seq_shared[a];
+      const int32_t* first = bt + (size_t)a * MB;
+      for (int32_t s = a; s < b; ++s) {
+        const int32_t Ss = seq_shared[s];
+        bool m = Ss != S || Ss < 0 || Ss % kBlock != 0 || Ss > ctx_lens[s] || Ss / kBlock > MB;
+        if (!m) {
+          const int32_t* row = bt + (size_t)s * MB;
+          for (int32_t k = 0; k < Ss / kBlock; ++k) m |= row[k] != first[k];
+        }
+        bad += m ? 1 : 0;
+      }
+    }
+  }
+  // a lane may count several members: add the wave's sum
+  int32_t sum = bad;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if ((threadIdx.x & (kWave - 1)) == 0 && sum != 0) atomicAdd(count, sum);
+}
+
 constexpr int kThreads = 256;
 
 }  // namespace
@@ -119,6 +164,18 @@ hipError_t launch_check_tables(const int32_t* bt, const int32_t* ctx_lens, int32
   if (B > 0)
     hipLaunchKernelGGL(check_tables_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads),
                        0, stream, bt, ctx_lens, B, MB, NB, ctx_limit, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_groups(const int32_t* group_start, const int32_t* seq_shared,
+                               const int32_t* bt, const int32_t* ctx_lens, int32_t B,
+                               int32_t n_groups, int32_t max_group, int32_t MB, int32_t* count,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(clear_count_kernel, dim3(1), dim3(1), 0, stream, count);
+  if (n_groups > 0)
+    hipLaunchKernelGGL(check_groups_kernel, dim3((n_groups + kThreads - 1) / kThreads),
+                       dim3(kThreads), 0, stream, group_start, seq_shared, bt, ctx_lens, B,
+                       n_groups, max_group, MB, count);
   return hipGetLastError();
 }
 

@@ -148,6 +148,20 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int
   return PA_OK;
 }
 
+pa_status pa_check_groups(const int32_t* group_start, const int32_t* seq_shared,
+                          const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                          int32_t n_groups, int32_t max_group, int32_t MB, int32_t bs,
+                          int32_t* count, hipStream_t stream) {
+  if (B < 0 || n_groups < 0 || max_group < 1 || MB < 0 || !count) return PA_EINVAL;
+  if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
+  if (n_groups > 0 && (!group_start || !seq_shared || !context_lens || (MB > 0 && !block_tables)))
+    return PA_EINVAL;
+  return pa::launch_check_groups(group_start, seq_shared, block_tables, context_lens, B, n_groups,
+                                 max_group, MB, count, stream) == hipSuccess
+             ? PA_OK
+             : PA_EHIP;
+}
+
 int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                     int32_t max_ctx) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || max_ctx <= 0) return 0;

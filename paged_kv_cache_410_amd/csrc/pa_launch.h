@@ -163,6 +163,10 @@ hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStre
 hipError_t launch_check_slots(const int32_t* slots, int32_t T, int32_t* count, hipStream_t stream);
 hipError_t launch_check_pairs(const int32_t* pairs, int32_t n, int32_t NB, int32_t* count,
                               hipStream_t stream);
+hipError_t launch_check_groups(const int32_t* group_start, const int32_t* seq_shared,
+                               const int32_t* bt, const int32_t* ctx_lens, int32_t B,
+                               int32_t n_groups, int32_t max_group, int32_t MB, int32_t* count,
+                               hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* bt, const int32_t* ctx_lens, int32_t B, int32_t MB,
                                int32_t NB, int32_t ctx_limit, int32_t* count, hipStream_t stream);
 

@@ -424,6 +424,16 @@ def test_decode_shared_rejects_bad_arguments(palib, kw, status):
     assert palib.lib().pa_decode_shared(*shared_args(**kw)) == status
 
 
+def test_check_groups_rejects_bad_arguments(palib):
+    lib = palib.lib()
+    ok = dict(gs=FAKE, sh=FAKE, bt=FAKE, cl=FAKE, B=8, n=2, mg=4, MB=8, bs=16, count=FAKE)
+    order = ("gs", "sh", "bt", "cl", "B", "n", "mg", "MB", "bs", "count")
+    for kw, status in ((dict(count=None), -1), (dict(gs=None), -1), (dict(sh=None), -1),
+                       (dict(mg=0), -1), (dict(B=-1), -1), (dict(bs=8), -2)):
+        a = dict(ok, **kw)
+        assert lib.pa_check_groups(*[a[k] for k in order], None) == status, kw
+
+
 def test_decode_shared_workspace_and_empty_batch(palib):
     lib = palib.lib()
     assert lib.pa_decode_shared(*shared_args(B=0, q=None, out=None)) == 0

@@ -122,6 +122,8 @@ def test_decode_shared_full_config(pa, name):
     st.run_cache_ops(pa, fused=True)
     gs, sh, mg = groups_of(pa, st)
     say(f"[decode_shared full config] {name}: groups={len(gs) - 1} shared={sorted(set(sh.tolist()))}")
+    assert pa.check_groups(torch.from_numpy(gs).cuda(), torch.from_numpy(sh).cuda(),
+                           st.block_tables, st.context_lens, mg) == 0
     out = run_shared(pa, st, gs, sh, mg, 0)
     torch.cuda.synchronize()
     rows = sample_rows(st.tb, spec.Hq, 40, seed=7)
@@ -148,3 +150,33 @@ def test_decode_shared_cache_flags_give_identical_bits(pa, name):
             for a in (False, True) for b in (False, True)]
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_check_groups_counts_violations(pa):
+    """pa_check_groups: zero on the planner's groups; one per planted fault."""
+    for name in ("cow_small", "prefix_small", "cow_gqa", "mha_bf16"):
+        st = Step(SMALL[name], oracle_full=False)
+        gs, sh, mg = groups_of(pa, st)
+        assert pa.check_groups(torch.from_numpy(gs).cuda(), torch.from_numpy(sh).cuda(),
+                               st.block_tables, st.context_lens, mg) == 0, name
+    st = Step(SMALL["cow_small"], oracle_full=False)
+    gs, sh, mg = groups_of(pa, st)
+    a = int(gs[0])
+    cases = []
+    bt = st.tb.block_tables.copy()
+    bt[a + 1, 0] = bt[a + 1, 0] + 1            # a member's shared entry differs
+    cases.append((gs, sh, bt, st.tb.context_lens, mg))
+    sh2 = sh.copy()
+    sh2[a + 2] -= 16                           # a member's shared length differs
+    cases.append((gs, sh2, st.tb.block_tables, st.tb.context_lens, mg))
+    cases.append((gs, sh, st.tb.block_tables, st.tb.context_lens, 2))   # groups too large
+    cl = st.tb.context_lens.copy()
+    cl[a + 3] = int(sh[a]) - 1                 # shared part beyond a member's context
+    cases.append((gs, sh, st.tb.block_tables, cl, mg))
+    expect = [1, 1, len(gs) - 1, 1]
+    for (g_, s_, b_, c_, m_), e in zip(cases, expect):
+        n = pa.check_groups(torch.from_numpy(np.ascontiguousarray(g_)).cuda(),
+                            torch.from_numpy(np.ascontiguousarray(s_)).cuda(),
+                            torch.from_numpy(np.ascontiguousarray(b_)).cuda(),
+                            torch.from_numpy(np.ascontiguousarray(c_)).cuda(), m_)
+        assert n == e, (n, e)
