@@ -180,3 +180,63 @@ def test_check_groups_counts_violations(pa):
                             torch.from_numpy(np.ascontiguousarray(b_)).cuda(),
                             torch.from_numpy(np.ascontiguousarray(c_)).cuda(), m_)
         assert n == e, (n, e)
+
+
+def fork_tree_batch(seed, Hq, Hkv, NB=600):
+    """Sequences of a random fork tree (roots, children, grandchildren), built
+    with the oracle's block manager, in the order they were made: sharing of
+    leading blocks at many depths, private tails of random length."""
+    rng = np.random.default_rng(seed)
+    bm = oracle.blockmgr.BlockManager(NB, 16, list(rng.permutation(NB)))
+    seqs = []
+    for _ in range(int(rng.integers(1, 4))):
+        root = bm.add_seq()
+        bm.append(root, int(rng.integers(1, 200)))
+        family = [root]
+        for _ in range(int(rng.integers(0, 6))):
+            parent = family[int(rng.integers(0, len(family)))]
+            child = bm.fork(parent)
+            bm.append(child, int(rng.integers(0, 60)))
+            family.append(child)
+        for sq in family:                 # the root may also grow after its forks
+            if rng.random() < 0.3:
+                bm.append(sq, int(rng.integers(1, 30)))
+        seqs += family
+    if rng.random() < 0.5:
+        seqs = [seqs[i] for i in rng.permutation(len(seqs))]   # interleaved families
+    MB = max(len(bm.tables[s]) for s in seqs) + 1
+    bt = np.full((len(seqs), MB), -1, np.int32)
+    for i, s in enumerate(seqs):
+        bt[i, :len(bm.tables[s])] = bm.tables[s]
+    cl = np.array([bm.seq_len(s) for s in seqs], np.int32)
+    D = 128
+    g = torch.Generator().manual_seed(seed)
+    k = torch.randn(NB, Hkv, 16, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(NB, Hkv, 16, D, generator=g).to(torch.bfloat16)
+    q = torch.randn(len(seqs), Hq, D, generator=g).to(torch.bfloat16)
+    return q, k, v, bt, cl
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_decode_shared_random_fork_trees(pa, seed):
+    Hq, Hkv = (8, 8) if seed % 2 == 0 else (8, 2)
+    q, k, v, bt, cl = fork_tree_batch(seed, Hq, Hkv)
+    B = len(cl)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)   # noqa: E731
+    expect = oracle.decode(bits(q), bits(k), bits(v), bt, cl, 1 / np.sqrt(128))
+    G = Hq // Hkv
+    dev = torch.device("cuda")
+    args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
+                                              torch.from_numpy(cl).to(dev)]
+    for max_group, partition in ((16 // G, 0), (2, 32), (3, 16)):
+        gs, sh = pa.shared_groups(bt, cl, max_group)
+        gs_d, sh_d = torch.from_numpy(gs).to(dev), torch.from_numpy(sh).to(dev)
+        assert pa.check_groups(gs_d, sh_d, args[3], args[4], max_group) == 0
+        out = pa.decode_shared(*args, gs_d, sh_d, 1 / np.sqrt(128), int(cl.max()), max_group,
+                               int(sh.max()), partition=partition, shared_kv=True,
+                               groups_overlap=True)
+        torch.cuda.synchronize()
+        err = max_abs_err(out, expect)
+        say(f"[decode_shared fork tree] seed={seed} B={B} groups={len(gs) - 1} "
+            f"shared={sorted(set(sh.tolist()))[:6]} max_group={max_group} err={err:.2e}")
+        assert err <= TOL["bf16"]
