@@ -304,7 +304,9 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
  *                at most context_lens[s]; the members' block_tables agree on
  *                the first S_s / bs entries (0 for a sequence that shares
  *                nothing)
- *   max_group    host bound on the group sizes; max_group * (Hq / Hkv) <= 16
+ *   max_group    host bound on the group sizes (groups of more than 16 / (Hq /
+ *                Hkv) members run on the chunk kernel, whose waves share each
+ *                block through LDS)
  *   max_shared   host bound on every S_s (a multiple of bs, <= max_ctx)
  *   partition    tokens per partition of the shared part (0 = one partition;
  *                else a positive multiple of bs); each sequence's own tokens
@@ -318,9 +320,10 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
  * Other arguments and error rows as pa_decode. Two launches: the shared part
  * of every group (one read of its blocks for all members' query heads, on
  * the matrix cores, into the workspace), then every sequence's own tokens,
- * merged with its shared part into the final row. Supported for
- * bf16 with D = 128 (else PA_EUNSUPPORTED). A shared length that is negative,
- * not a multiple of bs or beyond the table gives that sequence an all-NaN
+ * merged with its shared part into the final row. Supported for bf16 with
+ * D = 128 and Hq / Hkv <= 16 (else PA_EUNSUPPORTED). A shared length that is
+ * negative, not a multiple of bs or beyond the table gives that sequence an
+ * all-NaN
  * row (the group pass takes the first member's, so a bad one there gives the
  * whole group NaN rows). Member tables that disagree on the shared entries
  * are not detected (the group's first member's blocks are used for all);

@@ -91,7 +91,10 @@ void chunk_mfma_kernel(DecodeParams P) {
   const int g = gp.x / groups;                     // kv head
   const int tile0 = (gp.x % groups) * kTilesPerWg;  // the workgroup's first tile
 
-  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
+  // (the group pass of shared-prefix decode reads a group's shared blocks
+  // through its first member's table; this kernel runs no tail pass)
+  const ItemStart is = item_start(P, s);
+  const int32_t* bt_row = P.block_tables + (size_t)is.trow * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
   const int blk_begin = p * bpp;
   const int ids0 =
@@ -162,7 +165,7 @@ void chunk_mfma_kernel(DecodeParams P) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[t][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  bool bad = sr.bad;
+  bool bad = sr.bad || is.bad;
 
   const char* kbase = reinterpret_cast<const char*>(P.k_cache);
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
@@ -445,8 +448,8 @@ void chunk_mfma_kernel(DecodeParams P) {
     const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
     if (np <= 1 ? p != 0 : p >= np) continue;  // this column has no such partition
     const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
-    if (np > 1) {
-      const size_t part = orow * P.n_parts + p;
+    if (np > 1 || P.always_partial) {
+      const size_t part = orow * P.n_parts + P.part_base + p;
       float* dst = P.ws_o + part * kD;
 #pragma unroll
       for (int et = 0; et < 8; ++et)
@@ -482,7 +485,8 @@ hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream) {
   auto go = [&](auto nw, auto tpw) {
     constexpr int NW = decltype(nw)::value;
     constexpr int TPW = decltype(tpw)::value;
-    const dim3 grid(p.Hkv * ((p.n_tiles + NW * TPW - 1) / (NW * TPW)), p.n_parts, p.B);
+    const dim3 grid(p.Hkv * ((p.n_tiles + NW * TPW - 1) / (NW * TPW)), p.pass_parts,
+                    p.pass_items);
     hipLaunchKernelGGL((chunk_mfma_kernel<NW, R, TPW, TilePolicy::kShared>), grid,
                        dim3(NW * kWave), 0, stream, p);
   };

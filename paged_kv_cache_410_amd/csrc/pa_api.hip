@@ -307,11 +307,15 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   if (max_shared > max_ctx) return PA_EINVAL;
   if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
   if (D != 64 && D != 128) return PA_EUNSUPPORTED;
-  // the group pass runs on the matrix-core kernel: bf16, D = 128, one
-  // 16-column tile per kv head (members x query heads of a group)
+  // the group pass runs on the matrix-core kernels (bf16, D = 128): the
+  // decode kernel for one 16-column tile of (member, query head) pairs per kv
+  // head, the chunk kernel for more; the tail pass takes one tile of a
+  // sequence's query heads (G <= 16)
   const int32_t G = Hq / Hkv;
-  if (dt != PA_BF16 || D != 128 || (int64_t)max_group * G > 16) return PA_EUNSUPPORTED;
-  if (B > kMaxGridYZ || n_groups > kMaxGridYZ) return PA_EUNSUPPORTED;
+  if (dt != PA_BF16 || D != 128 || G > 16) return PA_EUNSUPPORTED;
+  if (B > kMaxGridYZ || n_groups > kMaxGridYZ || max_group > kMaxGridYZ) return PA_EUNSUPPORTED;
+  const int64_t group_tiles = ((int64_t)max_group * G + 15) / 16;
+  if ((int64_t)Hkv * group_tiles > INT32_MAX) return PA_EUNSUPPORTED;
   if (B == 0) return PA_OK;
   if (n_groups == 0) return PA_EINVAL;
   if (!out || !q || !k_cache || !v_cache || !context_lens || !group_start || !seq_shared ||
@@ -358,7 +362,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
     g.group_start = group_start;
     g.shared_kv = (flags & PA_KV_SHARED_GROUPS) ? 1 : 0;
     g.max_q = max_group;
-    g.n_tiles = 1;
+    g.n_tiles = (int32_t)group_tiles;
     g.partition = nps > 1 ? partition : 0;
     g.part_base = 0;
     g.always_partial = 1;

@@ -240,3 +240,28 @@ def test_decode_shared_random_fork_trees(pa, seed):
         say(f"[decode_shared fork tree] seed={seed} B={B} groups={len(gs) - 1} "
             f"shared={sorted(set(sh.tolist()))[:6]} max_group={max_group} err={err:.2e}")
         assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("seed", [11, 12, 13])
+@pytest.mark.parametrize("max_group", [3, 4, 8])
+def test_decode_shared_groups_past_one_tile(pa, seed, max_group):
+    """Groups whose members x query heads exceed 16 columns per kv head run
+    their shared part on the chunk kernel (8 query heads per kv head: 24, 32
+    and 64 columns)."""
+    q, k, v, bt, cl = fork_tree_batch(seed, 16, 2)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)   # noqa: E731
+    expect = oracle.decode(bits(q), bits(k), bits(v), bt, cl, 1 / np.sqrt(128))
+    dev = torch.device("cuda")
+    gs, sh = pa.shared_groups(bt, cl, max_group)
+    args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
+                                              torch.from_numpy(cl).to(dev)]
+    for partition in (0, 48):
+        out = pa.decode_shared(*args, torch.from_numpy(gs).to(dev), torch.from_numpy(sh).to(dev),
+                               1 / np.sqrt(128), int(cl.max()), max_group, int(sh.max()),
+                               partition=partition)
+        torch.cuda.synchronize()
+        err = max_abs_err(out, expect)
+        say(f"[decode_shared chunk groups] seed={seed} max_group={max_group} "
+            f"sizes={np.diff(gs).tolist()} partition={partition} err={err:.2e}")
+        assert np.all(np.isfinite(out.float().cpu().numpy()))
+        assert err <= TOL["bf16"]
