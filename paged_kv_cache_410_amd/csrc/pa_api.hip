@@ -299,8 +299,8 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
                            size_t workspace_bytes, uint32_t flags, pa_dtype dt,
                            hipStream_t stream) {
   if (B < 0 || n_groups < 0 || max_group < 1 || max_shared < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 ||
-      NB < 0 || MB < 0 || max_ctx < 0 || !dtype_ok(dt) || (flags & ~(PA_KV_SHARED | PA_KV_SHARED_GROUPS)) != 0 ||
-      !__builtin_isfinite(scale))
+      NB < 0 || MB < 0 || max_ctx < 0 || !dtype_ok(dt) ||
+      (flags & ~(PA_KV_SHARED | PA_KV_SHARED_GROUPS)) != 0 || !__builtin_isfinite(scale))
     return PA_EINVAL;
   if (Hq % Hkv != 0) return PA_EINVAL;
   if (partition < 0 || partition % kBs != 0 || max_shared % kBs != 0) return PA_EINVAL;
