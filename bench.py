@@ -201,8 +201,9 @@ def main():
     ap.add_argument("--no-group", action="store_true",
                     help="attend over blocks shared by several sequences once per sequence "
                          "(pa_decode) instead of once per group of sharers (pa_decode_shared)")
-    ap.add_argument("--shared-partition", type=int, default=0,
-                    help="partition length of the shared part in pa_decode_shared (0 = none)")
+    ap.add_argument("--shared-partition", type=int, default=None,
+                    help="partition length of the shared part in pa_decode_shared (0 = none; "
+                         "default: the library's choice)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed; the "
                          "replayed step then sets value and ms_per_step")
@@ -287,6 +288,9 @@ def main():
             groups_overlap = len(set(shared_reads)) < len(shared_reads)
             own_repeats = len(set(own_reads)) < len(own_reads)
             sp = args.shared_partition
+            if sp is None:
+                sp = int(_lib.lib().pa_decode_shared_default_partition(
+                    len(gs) - 1, spec.Hq, spec.Hkv, max_group, int(sh.max())))
             groups = dict(group_start=torch.from_numpy(gs).to(dev),
                           seq_shared=torch.from_numpy(sh).to(dev), max_group=max_group,
                           max_shared=int(sh.max()), partition=sp, own_repeats=own_repeats,

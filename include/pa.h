@@ -332,6 +332,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
  */
 size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D,
                                         int32_t max_shared, int32_t partition);
+/* A partition length for the shared part: 0 (one partition) when the group
+ * pass has at least one workgroup per compute unit of the current device,
+ * else about half of max_shared (a multiple of bs), so that the pass fills
+ * the device. 0 for arguments that give nothing to split. */
+int32_t pa_decode_shared_default_partition(int32_t n_groups, int32_t Hq,
+                                           int32_t Hkv, int32_t max_group,
+                                           int32_t max_shared);
 pa_status pa_decode_shared(void* out, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* block_tables,
                            const int32_t* context_lens,

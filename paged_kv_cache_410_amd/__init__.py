@@ -289,12 +289,13 @@ def decode_shared_workspace_bytes(B, Hq, D, max_shared, partition):
 
 
 def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, seq_shared,
-                  scale, max_ctx, max_group, max_shared, partition=0, out=None, workspace=None,
+                  scale, max_ctx, max_group, max_shared, partition=None, out=None, workspace=None,
                   shared_kv=False, groups_overlap=False):
     """pa_decode for sequences that share leading blocks (pa_decode_shared):
     group_start int32 [n_groups + 1] and seq_shared int32 [B] on the device,
     as shared_groups() gives them; max_group and max_shared bound them.
-    partition splits the shared part (0 = one partition). shared_kv: blocks
+    partition splits the shared part (0 = one partition; None = the library's
+    choice for the current device). shared_kv: blocks
     past the shared parts are read by several sequences; groups_overlap: the
     shared parts of different groups overlap (PA_KV_SHARED_GROUPS)."""
     NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
@@ -310,6 +311,10 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, 
                          "group_start [n_groups + 1]")
     MB = block_tables.shape[1]
     n_groups = group_start.shape[0] - 1
+    if partition is None:
+        with torch.cuda.device(q.device):
+            partition = int(lib().pa_decode_shared_default_partition(
+                n_groups, Hq, Hkv, int(max_group), int(max_shared)))
     if out is None:
         out = torch.empty_like(q)
     if out.shape != q.shape or out.dtype != q.dtype:

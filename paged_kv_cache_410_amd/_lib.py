@@ -33,6 +33,7 @@ SIGNATURES = {
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_i32, c_vp]),
     "pa_decode_shared_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pa_decode_shared_default_partition": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_shared": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                  c_f32, c_i32, c_vp, c_sz, c_u32, c_i32, c_vp]),

@@ -281,6 +281,22 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                    stream);
 }
 
+int32_t pa_decode_shared_default_partition(int32_t n_groups, int32_t Hq, int32_t Hkv,
+                                           int32_t max_group, int32_t max_shared) {
+  if (n_groups <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_group < 1 || max_shared <= 0)
+    return 0;
+  // group-pass workgroups: one per (group, kv head) for one 16-column tile,
+  // one per 8 tiles on the chunk kernel
+  const int64_t tiles = ((int64_t)max_group * (Hq / Hkv) + 15) / 16;
+  const int64_t items = (int64_t)n_groups * Hkv * (tiles > 1 ? (tiles + 7) / 8 : 1);
+  // at least one per CU: one partition (measured best on the 16 x 8 COW and
+  // 8 x 16 prefix MHA batches); fewer: two (a 64/8-head COW batch of 128
+  // workgroups: 39.7 us against 46.0 unsplit and 43.4 with four)
+  if (items >= device_cus()) return 0;
+  const int32_t half = (max_shared / 2 + kBs - 1) / kBs * kBs;
+  return half >= max_shared ? 0 : half;
+}
+
 size_t pa_decode_shared_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_shared,
                                         int32_t partition) {
   if (B <= 0 || Hq <= 0 || D <= 0 || max_shared < 0 || partition < 0) return 0;

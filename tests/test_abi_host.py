@@ -434,6 +434,16 @@ def test_check_groups_rejects_bad_arguments(palib):
         assert lib.pa_check_groups(*[a[k] for k in order], None) == status, kw
 
 
+def test_decode_shared_default_partition_degenerate_arguments(palib):
+    lib = palib.lib()
+    # nothing shared, no groups, or inconsistent heads: nothing to split
+    assert lib.pa_decode_shared_default_partition(16, 32, 32, 8, 0) == 0
+    assert lib.pa_decode_shared_default_partition(0, 32, 32, 8, 1008) == 0
+    assert lib.pa_decode_shared_default_partition(16, 30, 8, 8, 1008) == 0
+    # 16 tokens cannot be halved into whole blocks
+    assert lib.pa_decode_shared_default_partition(1, 8, 8, 1, 16) == 0
+
+
 def test_decode_shared_workspace_and_empty_batch(palib):
     lib = palib.lib()
     assert lib.pa_decode_shared(*shared_args(B=0, q=None, out=None)) == 0

@@ -255,7 +255,7 @@ def test_decode_shared_groups_past_one_tile(pa, seed, max_group):
     gs, sh = pa.shared_groups(bt, cl, max_group)
     args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
                                               torch.from_numpy(cl).to(dev)]
-    for partition in (0, 48):
+    for partition in (0, 48, None):
         out = pa.decode_shared(*args, torch.from_numpy(gs).to(dev), torch.from_numpy(sh).to(dev),
                                1 / np.sqrt(128), int(cl.max()), max_group, int(sh.max()),
                                partition=partition)
