@@ -265,3 +265,31 @@ def test_decode_shared_groups_past_one_tile(pa, seed, max_group):
             f"sizes={np.diff(gs).tolist()} partition={partition} err={err:.2e}")
         assert np.all(np.isfinite(out.float().cpu().numpy()))
         assert err <= TOL["bf16"]
+
+
+def test_decode_shared_malformed_groups_stay_in_bounds(pa):
+    """Group bounds outside the batch: the call completes (every read stays
+    inside its buffer), and the rows of the intact groups are those of a
+    well-formed call; the affected members' rows are undefined."""
+    q, k, v, bt, cl = fork_tree_batch(5, 8, 8)
+    gs, sh = pa.shared_groups(bt, cl, 4)
+    assert len(gs) - 1 >= 3
+    dev = torch.device("cuda")
+    args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
+                                              torch.from_numpy(cl).to(dev)]
+    B = len(cl)
+    ws_bytes = pa.decode_shared_workspace_bytes(B, 8, 128, int(sh.max()), 0)
+
+    def run(g):
+        ws = torch.full((max(ws_bytes, 4) // 4,), float("nan"), device=dev)
+        return pa.decode_shared(*args, torch.from_numpy(g).to(dev), torch.from_numpy(sh).to(dev),
+                                1 / np.sqrt(128), int(cl.max()), 4, int(sh.max()), partition=0,
+                                workspace=ws.view(torch.uint8)).float().cpu()
+
+    good = run(gs)
+    bad_gs = gs.copy()
+    bad_gs[1] = B + 5                         # groups 0 and 1 out of the batch
+    out = run(bad_gs)
+    torch.cuda.synchronize()
+    intact = np.arange(int(gs[2]), B)
+    assert torch.equal(out[intact], good[intact])
