@@ -10,12 +10,13 @@
 // block by block; partitioning long contexts across workgroups is this
 // library's way to spread one sequence over many compute units.)
 //
-// One workgroup of RW waves per (query head, query row). Every wave finds M
-// over all partitions; wave w then accumulates partitions w, w + RW, ...,
-// reading kUnroll partial rows per round trip (lane i holds w_j for the i-th
-// partition of the wave's current chunk, broadcast with readlane, while every
-// lane accumulates its own dims of the output row); the waves' sums are
-// combined through LDS.
+// One workgroup of RW waves per (query head, query row). Wave w takes
+// partitions w, w + RW, ... in rounds of kUnroll: lane i loads the (m, l) of
+// the round's i-th partition while every lane loads its dims of all the
+// round's rows, in one round trip; the wave's running max moves once per
+// round (the rows summed before are rescaled, as between blocks in the
+// decode kernels), the weights are broadcast with readlane. The waves' states
+// are merged through LDS.
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -35,7 +36,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(DecodeParams P) {
   constexpr int RW = kReduceWaves;
   constexpr int DPL = D / kWave;  // output dims per lane
-  constexpr int kUnroll = 8;
+  constexpr int kUnroll = 16;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = wave_id();
   const int h = blockIdx.x;
@@ -54,63 +55,73 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   const float* ml = P.ws_ml + 2 * base;
   const float* po = P.ws_o + base * D + lane * DPL;
 
-  float M = -INFINITY;
-  for (int j = lane; j < np; j += kWave) M = fmaxf(M, ml[2 * j]);
-  M = wave_max(M);
-  const float m_use = (M == -INFINITY) ? 0.0f : M;
-
-  // this wave's partitions: j = w + RW * i, i < nw
+  // One pass: each round, every lane loads the (m, l) of one of the wave's
+  // next kUnroll partitions while all lanes load those partitions' rows; the
+  // running max moves once per round and rescales what was summed before
+  // (the online-softmax merge), so the rows never wait for a max pass.
+  // This wave's partitions: j = w + RW * i, i < nw.
   const int nw = w < np ? (np - w + RW - 1) / RW : 0;
-  float lpart = 0.0f;
+  float Mw = -INFINITY, lw = 0.0f;
   float acc[DPL];
 #pragma unroll
   for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
-  for (int i0 = 0; i0 < nw; i0 += kWave) {
-    const int i = i0 + lane;
-    float wj = 0.0f;
-    if (i < nw) {
-      const int j = w + RW * i;
-      wj = exp2_fast(ml[2 * j] - m_use);
-      lpart += wj * ml[2 * j + 1];
+  for (int i0 = 0; i0 < nw; i0 += kUnroll) {
+    const int cnt = min(kUnroll, nw - i0);
+    float mi = -INFINITY, li = 0.0f;
+    if (lane < cnt) {
+      const int j = w + RW * (i0 + lane);
+      mi = ml[2 * j];
+      li = ml[2 * j + 1];
     }
-    const int cnt = min(kWave, nw - i0);
-    for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
-      float v[kUnroll][DPL];
+    float v[kUnroll][DPL];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int k = min(k0 + u, cnt - 1);  // repeats are weighted by 0 below
-        const float* src = po + (size_t)(w + RW * (i0 + k)) * D;
+    for (int u = 0; u < kUnroll; ++u) {
+      const int k = min(u, cnt - 1);  // repeats are weighted by 0 below
+      const float* src = po + (size_t)(w + RW * (i0 + k)) * D;
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) v[u][d] = src[d];
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const float wk = k0 + u < cnt
-                             ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), k0 + u))
-                             : 0.0f;
-#pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[d] = fmaf(wk, v[u][d], acc[d]);
-      }
+      for (int d = 0; d < DPL; ++d) v[u][d] = src[d];
     }
+    const float Mn = fmaxf(Mw, wave_max(mi));
+    const float m_use = (Mn == -INFINITY) ? 0.0f : Mn;
+    const float a = exp2_fast(Mw - m_use);  // rescale of the earlier rounds
+    const float wi = lane < cnt ? exp2_fast(mi - m_use) : 0.0f;
+    lw = lw * a + group_sum<kWave>(wi * li);
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc[d] *= a;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float wk = u < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), u))
+                               : 0.0f;
+#pragma unroll
+      for (int d = 0; d < DPL; ++d) acc[d] = fmaf(wk, v[u][d], acc[d]);
+    }
+    Mw = Mn;
   }
 
+  // The waves' states, each relative to its own max, merged through LDS.
   __shared__ float sm_acc[RW][D];
-  __shared__ float sm_l[RW];
+  __shared__ float sm_l[RW], sm_m[RW];
 #pragma unroll
   for (int d = 0; d < DPL; ++d) sm_acc[w][lane * DPL + d] = acc[d];
-  const float lw = group_sum<kWave>(lpart);
-  if (lane == 0) sm_l[w] = lw;
+  if (lane == 0) {
+    sm_l[w] = lw;
+    sm_m[w] = Mw;
+  }
   __syncthreads();
   if (w != 0) return;
+  float M = sm_m[0];
+#pragma unroll
+  for (int v = 1; v < RW; ++v) M = fmaxf(M, sm_m[v]);
+  const float m_use = (M == -INFINITY) ? 0.0f : M;
   float L = 0.0f;
 #pragma unroll
-  for (int v = 0; v < RW; ++v) L += sm_l[v];
+  for (int d = 0; d < DPL; ++d) acc[d] = 0.0f;
 #pragma unroll
-  for (int d = 0; d < DPL; ++d) {
-    float t = 0.0f;
+  for (int v = 0; v < RW; ++v) {
+    const float sc = exp2_fast(sm_m[v] - m_use);
+    L += sm_l[v] * sc;
 #pragma unroll
-    for (int v = 0; v < RW; ++v) t += sm_acc[v][lane * DPL + d];
-    acc[d] = t;
+    for (int d = 0; d < DPL; ++d) acc[d] += sm_acc[v][lane * DPL + d] * sc;
   }
   const float inv = 1.0f / L;
   char* out = reinterpret_cast<char*>(P.out) + (((size_t)row * P.Hq + h) * D + lane * DPL) * sizeof(T);
