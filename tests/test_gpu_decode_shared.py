@@ -293,3 +293,28 @@ def test_decode_shared_malformed_groups_stay_in_bounds(pa):
     torch.cuda.synchronize()
     intact = np.arange(int(gs[2]), B)
     assert torch.equal(out[intact], good[intact])
+
+
+@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa"])
+def test_decode_shared_permutation_invariant_and_deterministic(pa, name):
+    """The blocks relabelled by a random permutation of the pool (pools and
+    tables alike) give bitwise the same outputs, as does a second run:
+    nothing in the arithmetic order depends on physical block ids."""
+    st = Step(SMALL[name], oracle_full=False)
+    st.run_cache_ops(pa)
+    gs, sh, mg = groups_of(pa, st)
+    out1 = run_shared(pa, st, gs, sh, mg, 32)
+    out2 = run_shared(pa, st, gs, sh, mg, 32)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(st.tb.NB)               # old block b -> new block perm[b]
+    inv = np.argsort(perm)
+    bt = st.tb.block_tables.copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    idx = torch.from_numpy(inv).cuda()
+    k2, v2 = st.k_cache[idx].contiguous(), st.v_cache[idx].contiguous()
+    out3 = pa.decode_shared(st.q, k2, v2, torch.from_numpy(bt).cuda(), st.context_lens,
+                            torch.from_numpy(gs).cuda(), torch.from_numpy(sh).cuda(),
+                            st.spec.scale, st.max_ctx, mg, int(sh.max()), partition=32)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
