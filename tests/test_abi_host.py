@@ -455,3 +455,32 @@ def test_decode_shared_workspace_and_empty_batch(palib):
     assert lib.pa_decode_shared_workspace_bytes(4, 8, 128, 100, 0) == \
         (4 * 8 * 8 + 255) // 256 * 256 + 4 * 8 * 128 * 4
     assert lib.pa_decode_shared_workspace_bytes(4, 8, 128, 0, 64) == 0
+
+
+def test_shared_groups_edge_cases(palib):
+    """Empty batch; empty contexts; negative entries end the shared run;
+    only whole blocks inside every member's context are shared; a group stops
+    at max_group."""
+    import paged_kv_cache_410_amd as pa
+    gs, sh = pa.shared_groups(np.zeros((0, 4), np.int32), np.zeros(0, np.int32), 4)
+    assert gs.tolist() == [0] and sh.size == 0
+    bt = np.array([[5, 6, 7, -1],
+                   [5, 6, 8, -1],       # shares blocks 5, 6 with row 0
+                   [5, 6, -1, -1],      # context 20: only block 5 lies whole inside it
+                   [9, -1, -1, -1],     # shares nothing with row 0: a new group
+                   [9, 3, -1, -1],
+                   [0, -1, -1, -1],     # empty context: alone
+                   [-1, -1, -1, -1]], np.int32)
+    cl = np.array([40, 45, 20, 16, 30, 0, 0], np.int32)
+    gs, sh = pa.shared_groups(bt, cl, 4)
+    assert gs.tolist() == [0, 3, 5, 6, 7]
+    assert sh.tolist() == [16, 16, 16, 16, 16, 0, 0]
+    check_groups(bt, cl, 4, gs, sh)
+    gs2, sh2 = pa.shared_groups(bt, cl, 2)       # the first group is cut at two
+    assert gs2.tolist() == [0, 2, 3, 5, 6, 7]
+    assert sh2.tolist() == [32, 32, 0, 16, 16, 0, 0]
+    check_groups(bt, cl, 2, gs2, sh2)
+    # a negative entry inside the first member's context ends its shared run
+    bt3 = np.array([[5, -1, 7], [5, -1, 7]], np.int32)
+    gs3, sh3 = pa.shared_groups(bt3, np.array([48, 48], np.int32), 4)
+    assert gs3.tolist() == [0, 2] and sh3.tolist() == [16, 16]
