@@ -185,8 +185,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="13b",
-                    choices=["tiny", "7b", "13b", "gqa", "cow", "prefix", "13b_verify4",
-                             "gqa_chunk512"])
+                    choices=["tiny", "7b", "13b", "gqa", "cow", "cow_gqa8", "prefix",
+                             "13b_verify4", "gqa_chunk512"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-context partition in tokens (default: the library's choice, "
                          "or the workload's own)")
@@ -275,7 +275,9 @@ def main():
     groups = None
     if shared_kv and not spec.chunk and not args.no_group and spec.dtype == "bf16" \
             and spec.D == 128:
-        max_group = 16 // (spec.Hq // spec.Hkv)
+        # groups of up to 16 sequences (past 16 columns per kv head the group
+        # pass runs on the chunk kernel)
+        max_group = 16
         gs, sh = pa.shared_groups(tb.block_tables, tb.context_lens, max_group)
         if sh.any():
             # once grouped, do blocks still repeat? In the groups' shared parts

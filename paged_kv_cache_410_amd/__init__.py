@@ -29,7 +29,8 @@ __all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "check_slots"
            "check_tables", "decode", "multi_query", "shares_blocks",
            "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError", "shared_groups", "decode_shared",
-           "decode_shared_workspace_bytes", "check_groups"]
+           "decode_shared_workspace_bytes", "check_groups",
+           "decode_shared_default_partition"]
 
 BLOCK_SIZE = 16
 
@@ -284,6 +285,11 @@ def shared_groups(block_tables, context_lens, max_group):
     return gs[:n.value + 1].copy(), sh
 
 
+def decode_shared_default_partition(n_groups, Hq, Hkv, max_group, max_shared):
+    return int(lib().pa_decode_shared_default_partition(n_groups, Hq, Hkv, max_group,
+                                                        max_shared))
+
+
 def decode_shared_workspace_bytes(B, Hq, D, max_shared, partition):
     return int(lib().pa_decode_shared_workspace_bytes(B, Hq, D, max_shared, partition))
 
@@ -313,8 +319,8 @@ def decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, 
     n_groups = group_start.shape[0] - 1
     if partition is None:
         with torch.cuda.device(q.device):
-            partition = int(lib().pa_decode_shared_default_partition(
-                n_groups, Hq, Hkv, int(max_group), int(max_shared)))
+            partition = decode_shared_default_partition(n_groups, Hq, Hkv, int(max_group),
+                                                        int(max_shared))
     if out is None:
         out = torch.empty_like(q)
     if out.shape != q.shape or out.dtype != q.dtype:

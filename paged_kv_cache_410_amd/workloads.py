@@ -87,6 +87,11 @@ CONFIGS = {
                 cow=dict(prompts=16, samples=8, prompt_len=1024, r_max=15, tail_lo=1, tail_hi=256)),
     # several new tokens per sequence (multi-query attention, causal within the chunk)
     # requests sharing one system prompt through the prefix cache
+    # the COW batch on a 64/8-head GQA layer: 8 samples x 8 query heads share
+    # each prompt block (a study workload for the shared-prefix decode)
+    "cow_gqa8": Spec("cow_gqa8", "bf16", 128, 64, 8, 128, seed=9, lengths=("cow",),
+                     cow=dict(prompts=16, samples=8, prompt_len=1024, r_max=15, tail_lo=1,
+                              tail_hi=256)),
     "prefix": Spec("prefix", "bf16", 128, 32, 32, 128, seed=7, lengths=("prefix",),
                    prefix=dict(shared=1024, tail_lo=16, tail_hi=512, vocab=32000)),
     "13b_verify4": Spec("13b_verify4", "bf16", 128, 40, 40, 128, seed=5,

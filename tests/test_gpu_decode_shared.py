@@ -112,7 +112,7 @@ def test_decode_shared_bad_shared_length_poisons_only_its_row(pa):
     assert torch.equal(out[keep], good[keep])
 
 
-@pytest.mark.parametrize("name", ["cow", "prefix"])
+@pytest.mark.parametrize("name", ["cow", "prefix", "cow_gqa8"])
 def test_decode_shared_full_config(pa, name):
     """Full-size sharing workloads in the launch configuration the benchmark
     times: sampled outputs against the oracle, properties at every row."""
@@ -120,11 +120,12 @@ def test_decode_shared_full_config(pa, name):
     spec = workloads.CONFIGS[name]
     st = Step(spec, values_device="cuda", oracle_full=False)
     st.run_cache_ops(pa, fused=True)
-    gs, sh, mg = groups_of(pa, st)
+    gs, sh, mg = groups_of(pa, st, 16)                      # as the benchmark groups
     say(f"[decode_shared full config] {name}: groups={len(gs) - 1} shared={sorted(set(sh.tolist()))}")
     assert pa.check_groups(torch.from_numpy(gs).cuda(), torch.from_numpy(sh).cuda(),
                            st.block_tables, st.context_lens, mg) == 0
-    out = run_shared(pa, st, gs, sh, mg, 0)
+    part = pa.decode_shared_default_partition(len(gs) - 1, spec.Hq, spec.Hkv, mg, int(sh.max()))
+    out = run_shared(pa, st, gs, sh, mg, part)              # the bench's launch
     torch.cuda.synchronize()
     rows = sample_rows(st.tb, spec.Hq, 40, seed=7)
     expect = st.oracle_decode(pairs=rows)
