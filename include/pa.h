@@ -233,8 +233,9 @@ int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv,
  * pa_decode_workspace_bytes — device workspace pa_decode (rows = B) or
  * pa_multi_query (rows = Tq) needs for this split: 0 when partition == 0 or
  * max_ctx <= partition, otherwise room for per-partition partial results
- * (fp32 running max, sum and unnormalised output row per (query row, query
- * head, partition)).
+ * (per (query row, query head, partition): the fp32 running max and sum, and
+ * the partition's output row normalised by its own sum, in the I/O dtype;
+ * sized for fp32 rows).
  */
 size_t pa_decode_workspace_bytes(int32_t rows, int32_t Hq, int32_t D,
                                  int32_t max_ctx, int32_t partition);

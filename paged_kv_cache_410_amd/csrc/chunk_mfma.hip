@@ -449,8 +449,8 @@ void chunk_mfma_kernel(DecodeParams P) {
     if (np <= 1 ? p != 0 : p >= np) continue;  // this column has no such partition
     const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
     if (np > 1 || P.always_partial) {
-      const size_t part = orow * P.n_parts + P.part_base + p;
-      float* dst = P.ws_o + part * kD;
+      const size_t part = part_slot(P, sr.first + i, h, P.part_base + p);
+      float* dst = static_cast<float*>(P.ws_o) + part * kD;  // fp32 rows (part_f32)
 #pragma unroll
       for (int et = 0; et < 8; ++et)
         *reinterpret_cast<float4*>(dst + 16 * et + 4 * rg) =

@@ -299,20 +299,33 @@ void decode_mfma_kernel(DecodeParams P) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ov[e] += sm_o[v][qq][8 * ch + e] * sc;
     }
-    const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
+    const size_t row = (size_t)(sr.first + i);
+    // Several partitions of this column's context, or the group pass of a
+    // shared prefix: write this partition's partial and its (m, l); else the
+    // final row (the tail pass first folds in the group pass's partials of
+    // the row).
     if (np > 1 || P.always_partial) {
-      const size_t part = orow * P.n_parts + P.part_base + p;
-      float* dst = P.ws_o + part * D + 8 * ch;
+      // fp16 partial (see PartScale); the 16 lanes of a column form one DPP row
+      float amax = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dst[e] = any_bad ? __builtin_nanf("") : ov[e];
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(ov[e]));
+      const PartScale ps = part_scale_f16(M, L, group_max<16>(amax));
+      uint4 u;
+      u.x = pack_f16x2(ov[0] * ps.mul, ov[1] * ps.mul);
+      u.y = pack_f16x2(ov[2] * ps.mul, ov[3] * ps.mul);
+      u.z = pack_f16x2(ov[4] * ps.mul, ov[5] * ps.mul);
+      u.w = pack_f16x2(ov[6] * ps.mul, ov[7] * ps.mul);
+      if (any_bad) u = make_uint4(0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u);  // NaN
+      const size_t part = part_slot(P, row, h, P.part_base + p);
+      st16(static_cast<char*>(P.ws_o) + (part * D + 8 * ch) * 2, u);
       if (ch == 0) {
-        P.ws_ml[2 * part] = any_bad ? 0.0f : M;
-        P.ws_ml[2 * part + 1] = any_bad ? __builtin_nanf("") : L;
+        P.ws_ml[2 * part] = any_bad ? 0.0f : ps.m;
+        P.ws_ml[2 * part + 1] = any_bad ? __builtin_nanf("") : ps.l;
       }
     } else {
-      // shared-prefix tail pass: fold in the group pass's partials of this row
       if (P.tail_pass)
-        merge_shared_partials<8>(P, is.bad ? 0 : is.start_blk * kBlock, orow, 8 * ch, D, M, L, ov);
+        merge_shared_partials<uint16_t, 8>(P, is.bad ? 0 : is.start_blk * kBlock, row, h, 8 * ch,
+                                           D, M, L, ov);
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       float res[8];
 #pragma unroll
@@ -322,7 +335,7 @@ void decode_mfma_kernel(DecodeParams P) {
       u.y = pack_bf16x2(res[2], res[3]);
       u.z = pack_bf16x2(res[4], res[5]);
       u.w = pack_bf16x2(res[6], res[7]);
-      st16(reinterpret_cast<char*>(P.out) + (orow * D + 8 * ch) * 2, u);
+      st16(reinterpret_cast<char*>(P.out) + ((row * P.Hq + h) * D + 8 * ch) * 2, u);
     }
   }
 }

@@ -2,8 +2,9 @@
 // (sequence, query head) into the final output row.
 //
 // Each partition j left (m_j, l_j, O_j): its running max and softmax sum in
-// the log2 domain and its unnormalised output row. With M = max_j m_j and
-// w_j = 2^(m_j - M), the full-context result is
+// the log2 domain and its unnormalised output row (for bf16 I/O an fp16 row
+// of an equivalent, rescaled state). With M = max_j m_j and w_j = 2^(m_j - M),
+// the full-context result is
 //     out = (sum_j w_j O_j) / (sum_j w_j l_j),
 // the same online-softmax rescaling the decode kernels apply between blocks,
 // applied once more between partitions. (The pages describe attention run
@@ -32,7 +33,9 @@ __device__ __forceinline__ float wave_max(float x) {
   return rows_max(x);
 }
 
-template <typename T, int D>
+// T: the output's element type; E: the partial rows' (fp16, or fp32 when
+// P.part_f32), chosen at launch.
+template <typename T, typename E, int D>
 __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(DecodeParams P) {
   constexpr int RW = kReduceWaves;
   constexpr int DPL = D / kWave;  // output dims per lane
@@ -51,9 +54,11 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   if (np <= 1) return;  // the attention kernel wrote the final row itself
 
   const int row = sr.first + i;
-  const size_t base = ((size_t)row * P.Hq + h) * P.n_parts;
+  // partial j of this row and head sits at slot part_slot(row, h, j): Hq slots apart
+  const size_t base = part_slot(P, row, h, 0);
+  const size_t jstride = P.Hq;
   const float* ml = P.ws_ml + 2 * base;
-  const float* po = P.ws_o + base * D + lane * DPL;
+  const E* po = static_cast<const E*>(P.ws_o) + base * D + lane * DPL;
 
   // One pass: each round, every lane loads the (m, l) of one of the wave's
   // next kUnroll partitions while all lanes load those partitions' rows; the
@@ -70,16 +75,16 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
     float mi = -INFINITY, li = 0.0f;
     if (lane < cnt) {
       const int j = w + RW * (i0 + lane);
-      mi = ml[2 * j];
-      li = ml[2 * j + 1];
+      mi = ml[2 * j * jstride];
+      li = ml[2 * j * jstride + 1];
     }
     float v[kUnroll][DPL];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int k = min(u, cnt - 1);  // repeats are weighted by 0 below
-      const float* src = po + (size_t)(w + RW * (i0 + k)) * D;
+      const E* src = po + (size_t)(w + RW * (i0 + k)) * jstride * D;
 #pragma unroll
-      for (int d = 0; d < DPL; ++d) v[u][d] = src[d];
+      for (int d = 0; d < DPL; ++d) v[u][d] = elem_f32(src[d]);
     }
     const float Mn = fmaxf(Mw, wave_max(mi));
     const float m_use = (Mn == -INFINITY) ? 0.0f : Mn;
@@ -140,14 +145,19 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
   const dim3 grid(p.Hq, p.max_q, p.B), block(kReduceWaves * kWave);
-  if (dtype == 1 && D == 128)
-    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, 128>), grid, block, 0, stream, p);
+  // bf16 output: fp16 partial rows, or fp32 ones from the chunk kernel
+  if (dtype == 1 && D == 128 && !p.part_f32)
+    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, _Float16, 128>), grid, block, 0, stream, p);
+  else if (dtype == 1 && D == 128)
+    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, float, 128>), grid, block, 0, stream, p);
+  else if (dtype == 1 && D == 64 && !p.part_f32)
+    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, _Float16, 64>), grid, block, 0, stream, p);
   else if (dtype == 1 && D == 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, 64>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, float, 64>), grid, block, 0, stream, p);
   else if (dtype == 0 && D == 128)
-    hipLaunchKernelGGL((decode_reduce_kernel<float, 128>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<float, float, 128>), grid, block, 0, stream, p);
   else if (dtype == 0 && D == 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<float, 64>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<float, float, 64>), grid, block, 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

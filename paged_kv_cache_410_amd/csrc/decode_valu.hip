@@ -310,26 +310,49 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
     for (int e = 0; e < EPL; ++e) outv[e] = o[e];
   }
 
-  // Lanes 0 .. LPT-1 of wave 0 hold the result for chunk c.
-  if (P.always_partial || (P.partition > 0 && nparts_s > 1)) {
-    const size_t part = ((size_t)row * P.Hq + h) * P.n_parts + P.part_base + p;
-    float* dst = P.ws_o + part * D + c * EPL;
+  // Lanes 0 .. LPT-1 of wave 0 hold the result for chunk c. One partition of
+  // several (or the group pass of a shared prefix): the partial and its
+  // (m, l). Else the final row; the shared-prefix tail pass first folds in the
+  // group pass's partials of the row.
+  const bool to_partial = P.always_partial || (P.partition > 0 && nparts_s > 1);
+  float mul;  // applied to every dim below
+  if (to_partial) {
+    mul = 1.0f;  // fp32 partials: the unnormalised state itself
+    if constexpr (sizeof(T) == 2) {
+      // fp16 partial (see PartScale); the row's LPT lanes are lanes 0 .. LPT-1
+      float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dst[e] = bad ? __builtin_nanf("") : outv[e];
+      for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(outv[e]));
+      const PartScale ps = part_scale_f16(M, L, group_max<LPT>(amax));
+      mul = ps.mul;
+      M = ps.m;
+      L = ps.l;
+    }
+  } else {
+    if (P.tail_pass)
+      merge_shared_partials<T, EPL>(P, is.bad ? 0 : is.start_blk * kBlock, row, h, c * EPL, D, M,
+                                    L, outv);
+    mul = L > 0.0f ? 1.0f / L : 0.0f;  // empty context -> zeros
+  }
+  float res[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) res[e] = bad ? __builtin_nanf("") : outv[e] * mul;
+  if (to_partial) {
+    const size_t part = part_slot(P, row, h, P.part_base + p);
+    char* dst = static_cast<char*>(P.ws_o) + part * D * sizeof(T) + c * 16;
     if (c == 0) {
       P.ws_ml[2 * part] = bad ? 0.0f : M;
       P.ws_ml[2 * part + 1] = bad ? __builtin_nanf("") : L;
     }
+    if constexpr (sizeof(T) == 2) {
+      st16(dst, make_uint4(pack_f16x2(res[0], res[1]), pack_f16x2(res[2], res[3]),
+                           pack_f16x2(res[4], res[5]), pack_f16x2(res[6], res[7])));
+    } else {
+      st16(dst, make_uint4(__float_as_uint(res[0]), __float_as_uint(res[1]),
+                           __float_as_uint(res[2]), __float_as_uint(res[3])));
+    }
     return;
   }
-  // shared-prefix tail pass: fold in the group pass's partials of this row
-  if (P.tail_pass)
-    merge_shared_partials<EPL>(P, is.bad ? 0 : is.start_blk * kBlock, (size_t)row * P.Hq + h,
-                               c * EPL, D, M, L, outv);
-  float res[EPL];
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;  // empty context -> zeros
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) res[e] = bad ? __builtin_nanf("") : outv[e] * inv;
   char* out = reinterpret_cast<char*>(P.out) + row_qo * sizeof(T) + c * 16;
   if constexpr (sizeof(T) == 2) {
     uint4 u;

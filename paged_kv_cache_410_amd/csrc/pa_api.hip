@@ -179,6 +179,8 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_c
   const int64_t parts = grid_parts(max_ctx, partition);
   if (parts <= 1) return 0;
   const size_t rows = (size_t)B * Hq * (size_t)parts;
+  // (m, l) in fp32, then the rows; a row takes D elements of the I/O dtype,
+  // sized here for fp32 so that one size serves both dtypes
   return align_up(rows * 2 * sizeof(float)) + rows * (size_t)D * sizeof(float);
 }
 
@@ -250,7 +252,7 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   if (parts > 1) {
     const size_t nrows = (size_t)rows * Hq * (size_t)parts;
     p.ws_ml = static_cast<float*>(workspace);
-    p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(nrows * 2 * sizeof(float)));
+    p.ws_o = static_cast<char*>(workspace) + align_up(nrows * 2 * sizeof(float));
   }
 
   // The matrix-core kernel serves a kv head's columns (query rows x group
@@ -258,6 +260,7 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   // row) goes to the vector kernel.
   const bool mfma = dt == PA_BF16 && D == 128 && (p.G >= 2 || max_q >= 2);
   if (mfma && (int64_t)Hkv * p.n_tiles > INT32_MAX) return PA_EUNSUPPORTED;
+  p.part_f32 = dt == PA_F32 || (mfma && p.n_tiles > 1);  // fp32 I/O, or the chunk kernel
   hipError_t err = mfma ? pa::launch_decode_mfma(p, stream) : pa::launch_decode_valu(p, dt, D, stream);
   if (err != hipSuccess) return PA_EHIP;
   if (parts > 1) {
@@ -368,8 +371,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   if (nps > 0) {
     const size_t nrows = (size_t)B * Hq * (size_t)nps;
     p.ws_ml = static_cast<float*>(workspace);
-    p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      align_up(nrows * 2 * sizeof(float)));
+    p.ws_o = static_cast<char*>(workspace) + align_up(nrows * 2 * sizeof(float));
   }
 
   // 1. group pass: each group's shared tokens, read once for all its members
@@ -379,6 +381,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
     g.shared_kv = (flags & PA_KV_SHARED_GROUPS) ? 1 : 0;
     g.max_q = max_group;
     g.n_tiles = (int32_t)group_tiles;
+    g.part_f32 = group_tiles > 1;  // the chunk kernel writes fp32 partials
     g.partition = nps > 1 ? partition : 0;
     g.part_base = 0;
     g.always_partial = 1;
@@ -393,6 +396,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   t.shared_partition = nps > 1 ? partition : 0;
   t.max_q = 1;
   t.n_tiles = 1;
+  t.part_f32 = group_tiles > 1;  // as the group pass wrote them
   t.partition = 0;
   t.pass_parts = 1;
   t.pass_items = B;

@@ -92,6 +92,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Max over aligned groups of N consecutive lanes (N = 8 or 16), as group_sum.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(N == 8 || N == 16, "group size");
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  return x;
+}
+
 // Max over the 4 rows of the wave (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float rows_max(float x) {
   LanePair p = pair16(x);

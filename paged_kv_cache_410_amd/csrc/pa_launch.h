@@ -18,8 +18,9 @@ struct DecodeParams {
   const int32_t* block_tables;  // [B][MB]
   const int32_t* context_lens;  // [B]
   const int32_t* query_start;   // [B + 1] query rows per sequence, or null: one row per sequence
-  float* ws_ml;                 // split only: [B][Hq][n_parts][2] = (m, l), log2 domain
-  float* ws_o;                  // split only: [B][Hq][n_parts][D], unnormalised
+  float* ws_ml;                 // split only: [rows][n_parts][Hq][2] = (m, l), log2 domain
+  void* ws_o;                   // split only: [rows][n_parts][Hq][D]: fp32 rows (unnormalised)
+                                // when part_f32, else scaled fp16 rows (PartScale)
   int32_t B, Hq, Hkv, G, NB, MB;
   int32_t ctx_limit;            // min(max_ctx, MB * 16): larger contexts are rejected
   int32_t partition;            // tokens per partition; 0 = one partition per sequence
@@ -46,28 +47,84 @@ struct DecodeParams {
   int32_t few_items;            // vector kernel: an unsplit grid with at most 8 items per CU
   int32_t pass_parts;           // grid y of this pass (partitions)
   int32_t pass_items;           // grid z of this pass (sequences, or groups)
+  int32_t part_f32;             // partial rows are fp32: fp32 I/O, or written by the chunk
+                                // kernel (whose registers leave no room for the fp16 epilogue)
 };
+
+// Slot of partial j of query row `row`, query head h (x2 floats in ws_ml, xD in
+// ws_o). Partition-major within a row: the heads of one kv group, which one
+// workgroup finishes together, write one contiguous range instead of a
+// scattered piece per head (scattered partial stores cost several times
+// their bytes in the decode kernels' time).
+__device__ __forceinline__ size_t part_slot(const DecodeParams& P, size_t row, int h, int j) {
+  return (row * P.n_parts + j) * P.Hq + h;
+}
+
+// Element type of the partial rows for I/O dtype T (float, or bf16 bits).
+template <typename T>
+struct PartElem {
+  using type = float;
+};
+template <>
+struct PartElem<uint16_t> {
+  using type = _Float16;
+};
+__device__ __forceinline__ float elem_f32(float x) { return x; }
+__device__ __forceinline__ float elem_f32(_Float16 x) { return (float)x; }
+
+// A partial of bf16 attention (max m, sum l, unnormalised row o, all in the
+// log2-domain state of the online softmax) is stored in fp16 as
+//   z = o / c,  (m', l') = (m + log2 c, l / c),  c = l * 2^k,
+// an equivalent state: raising a state's max by log2 c multiplies its weight
+// 2^(m - M) in every later merge by c, which the division of o and l by c
+// undoes, so the merge kernel and the tail pass take it like any other partial. o / l is a
+// convex combination of V rows, so |z| <= max |v| * 2^-k; k > 0 only when that
+// bound passes 2^15, which keeps z inside fp16's range (largest finite 65504).
+// fp16's 11-bit significand leaves the final bf16 rounding as the dominant
+// error. amax is the row's max |o|.
+struct PartScale {
+  float mul, m, l;  // store o * mul, and (m, l)
+};
+__device__ __forceinline__ PartScale part_scale_f16(float m, float l, float amax) {
+  if (!(l > 0.0f)) return {0.0f, m, l};  // no token: zero row, weight 0
+  const float y = amax / l;
+  int k = 0;
+  if (y >= 32768.0f) k = (int)((__float_as_uint(y) >> 23) & 0xffu) - 127 - 14;  // y / 2^k < 2^15
+  const float inv_pow = __uint_as_float((uint32_t)(127 - k) << 23);                // 2^-k
+  return {inv_pow / l, m + __builtin_amdgcn_logf(l) + (float)k, inv_pow};
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // Online-softmax merge of the group pass's partials of one row into a tail
 // pass's state (M, L, o: log2-domain max, sum, unnormalised dims), for the n
-// dims this lane holds, starting at dim `dim0` of the row. The group pass
+// dims this lane holds, starting at dim `dim0` of (row, head h). The group pass
 // wrote ceil(shared / shared_partition) partials (one when not split) at
 // slots 0.. of the row's n_parts.
-template <int N>
+template <typename T, int N>
 __device__ __forceinline__ void merge_shared_partials(const DecodeParams& P, int shared_tokens,
-                                                      size_t row_head, int dim0, int D, float& M,
+                                                      size_t row, int h, int dim0, int D, float& M,
                                                       float& L, float (&o)[N]) {
   if (shared_tokens <= 0) return;
   const int bpp = P.shared_partition / 16;
   const int nps = bpp > 0 ? (shared_tokens / 16 + bpp - 1) / bpp : 1;
   for (int j = 0; j < nps && j < P.n_parts; ++j) {
-    const size_t part = row_head * P.n_parts + j;
+    const size_t part = part_slot(P, row, h, j);
     const float mj = P.ws_ml[2 * part], lj = P.ws_ml[2 * part + 1];
-    const float* oj = P.ws_o + part * D + dim0;
     const SoftmaxScales sc = merge_scales(M, mj);
     L = L * sc.a + lj * sc.b;
+    if (P.part_f32) {
+      const float* oj = static_cast<const float*>(P.ws_o) + part * D + dim0;
 #pragma unroll
-    for (int e = 0; e < N; ++e) o[e] = o[e] * sc.a + oj[e] * sc.b;
+      for (int e = 0; e < N; ++e) o[e] = o[e] * sc.a + oj[e] * sc.b;
+    } else {
+      const auto* oj = static_cast<const typename PartElem<T>::type*>(P.ws_o) + part * D + dim0;
+#pragma unroll
+      for (int e = 0; e < N; ++e) o[e] = o[e] * sc.a + elem_f32(oj[e]) * sc.b;
+    }
     M = sc.m;
   }
 }
