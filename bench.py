@@ -204,9 +204,10 @@ def main():
     ap.add_argument("--shared-partition", type=int, default=None,
                     help="partition length of the shared part in pa_decode_shared (0 = none; "
                          "default: the library's choice)")
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=1,
                     help="time the attention call with HIP events on every n-th timed step "
-                         "(a pair of events between two kernels lengthens that step)")
+                         "(a pair of events between two kernels lengthens that step by a few "
+                         "microseconds; 1 = every step)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed; the "
                          "replayed step then sets value and ms_per_step")
@@ -276,35 +277,21 @@ def main():
     if shared_kv and not spec.chunk and not args.no_group and spec.dtype == "bf16" \
             and spec.D == 128:
         # groups of up to 16 sequences (past 16 columns per kv head the group
-        # pass runs on the chunk kernel)
-        max_group = 16
-        gs, sh = pa.shared_groups(tb.block_tables, tb.context_lens, max_group)
-        if sh.any():
-            # once grouped, do blocks still repeat? In the groups' shared parts
-            # (one prefix over several groups), or among the sequences' own
-            # blocks? Then that pass reads through the caches, else streams.
-            shared_reads, own_reads = [], []
-            for j in range(len(gs) - 1):
-                a, b = int(gs[j]), int(gs[j + 1])
-                nsh = int(sh[a]) // 16
-                shared_reads += tb.block_tables[a, :nsh].tolist()
-                for s_ in range(a, b):
-                    own_reads += tb.block_tables[s_, nsh:(int(tb.context_lens[s_]) + 15) // 16].tolist()
-            groups_overlap = len(set(shared_reads)) < len(shared_reads)
-            own_repeats = len(set(own_reads)) < len(own_reads)
-            sp = args.shared_partition
-            if sp is None:
-                sp = int(_lib.lib().pa_decode_shared_default_partition(
-                    len(gs) - 1, spec.Hq, spec.Hkv, max_group, int(sh.max())))
-            groups = dict(group_start=torch.from_numpy(gs).to(dev),
-                          seq_shared=torch.from_numpy(sh).to(dev), max_group=max_group,
-                          max_shared=int(sh.max()), partition=sp, own_repeats=own_repeats,
-                          groups_overlap=groups_overlap,
-                          workspace=torch.empty(pa.decode_shared_workspace_bytes(
-                              spec.B, spec.Hq, spec.D, int(sh.max()), sp), dtype=torch.uint8,
-                              device=dev))
-            log(f"[bench] {len(gs) - 1} groups of sharers, shared tokens "
-                f"{sorted(set(sh.tolist()))}, shared-part partition {sp}")
+        # pass runs on the chunk kernel); once grouped, a pass reads through
+        # the caches only where blocks still repeat within it
+        plan = pa.shared_plan(tb.block_tables, tb.context_lens, spec.Hq, spec.Hkv, 16)
+        if plan is not None:
+            sp = plan["partition"] if args.shared_partition is None else args.shared_partition
+            groups = dict(group_start=torch.from_numpy(plan["group_start"]).to(dev),
+                          seq_shared=torch.from_numpy(plan["seq_shared"]).to(dev),
+                          max_group=plan["max_group"], max_shared=plan["max_shared"],
+                          partition=sp, own_repeats=plan["shared_kv"],
+                          groups_overlap=plan["groups_overlap"],
+                          workspace=torch.empty(max(1, pa.decode_shared_workspace_bytes(
+                              spec.B, spec.Hq, spec.D, plan["max_shared"], sp)),
+                              dtype=torch.uint8, device=dev))
+            log(f"[bench] {len(plan['group_start']) - 1} groups of sharers, shared tokens "
+                f"{sorted(set(plan['seq_shared'].tolist()))}, shared-part partition {sp}")
 
     def attend(tables, dest, shared):
         if groups is not None and tables is bt:
@@ -360,6 +347,7 @@ def main():
     torch.cuda.synchronize()
     copy_ms = [e[2].elapsed_time(e[3]) for e in evs]
     write_ms = [e[3].elapsed_time(e[0]) for e in evs]
+    pass_dec_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)   # cross-check of dec_ms
     ms_step = wall * 1e3 / args.steps
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     dec_sorted = sorted(dec_ms)
@@ -487,6 +475,7 @@ def main():
         # block's used rows once; the logical rate is reported beside it.
         hbm_bytes = unique_decode_bytes(spec, tb) if shared_kv else nbytes["decode"]
         achieved = hbm_bytes / (dec_avg_ms * 1e-3) / 1e9
+    achieved_median = achieved * dec_avg_ms / dec_med_ms
     line = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) + decode tokens/sec",
         "value": round(value, 1),
@@ -520,12 +509,16 @@ def main():
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_median": round(dec_med_ms * 1e3, 2),
         "decode_us_p10_p90": [round(dec_p10_ms * 1e3, 2), round(dec_p90_ms * 1e3, 2)],
-        "decode_timed_calls": f"{len(dec_ms)} of {args.steps} timed steps (every {every})",
+        "decode_timed_calls": len(dec_ms),
+        "decode_timed_calls_note": f"{len(dec_ms)} of {args.steps} timed steps (every {every})",
+        "decode_us_median_separate_pass": round(pass_dec_ms[len(pass_dec_ms) // 2] * 1e3, 2),
         "write_us": round(sum(write_ms) / len(write_ms) * 1e3, 2),
         "copy_us": round(sum(copy_ms) / len(copy_ms) * 1e3, 2) if len(tb.pairs) else None,
         "algorithmic_bytes": nbytes,
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
+                     "achieved_median": round(achieved_median, 1),
+                     "frac_median": round(achieved_median / peak, 4),
                      "traffic": traffic,
                      "kernel": ("pa_decode_shared (group pass, tail pass, merge)"
                                 if groups is not None else "attention (one launch per step"

@@ -99,8 +99,9 @@ const char* pa_status_str(pa_status s);
  *   seq_ids       int32 [T], or NULL for seq_ids[i] = i (then T must be <= B)
  *   positions     int32 [T]
  * A negative position, a position at or past MB * bs, a sequence index
- * outside [0, B) or a negative table entry gives slot -1 (the "no write"
- * marker pa_write_kv skips). T == 0 is a no-op.
+ * outside [0, B), a negative table entry or one above (INT32_MAX - 15) / 16
+ * (whose slots do not fit an int32) gives slot -1 (the "no write" marker
+ * pa_write_kv skips). T == 0 is a no-op.
  */
 pa_status pa_slot_mapping(int32_t* slot_mapping, const int32_t* block_tables,
                           const int32_t* seq_ids, const int32_t* positions,
@@ -232,10 +233,14 @@ int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv,
 /*
  * pa_decode_workspace_bytes — device workspace pa_decode (rows = B) or
  * pa_multi_query (rows = Tq) needs for this split: 0 when partition == 0 or
- * max_ctx <= partition, otherwise room for per-partition partial results
- * (per (query row, query head, partition): the fp32 running max and sum, and
- * the partition's output row normalised by its own sum, in the I/O dtype;
- * sized for fp32 rows).
+ * max_ctx <= partition, otherwise room for one partial result per (query
+ * row, query head, partition): an fp32 (max, sum) pair of the partition's
+ * online-softmax state, and a row of D elements. The row is the state's
+ * unnormalised output in fp32 for fp32 I/O and from the chunk kernel (more
+ * than 16 query columns per kv head), else an fp16 row of an equivalent
+ * rescaled state (the row divided by its sum times a power of two, the pair
+ * adjusted to match). Sized as (8 + 4 D) bytes per partial, plus alignment,
+ * for both dtypes. The contents are scratch: nothing is kept between calls.
  */
 size_t pa_decode_workspace_bytes(int32_t rows, int32_t Hq, int32_t D,
                                  int32_t max_ctx, int32_t partition);

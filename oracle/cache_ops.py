@@ -11,6 +11,9 @@ for fp32). Every operation here is a copy of bits, so results are exact.
     physical block. Position p of sequence s sits in logical block p // bs at
     offset p % bs, so its physical slot is table[s][p // bs] * bs + p % bs.
     A negative position means "no token" (padding) and maps to slot -1.
+    So does a position past the table's width, or an entry that names no
+    block: a negative one (an unused entry), or one whose slots do not fit
+    the int32 slot numbers the write takes (above (2^31 - 1 - (bs - 1)) / bs).
   * write_kv: the same section: blocks are filled as tokens are generated.
     The new token's K and V rows land in its slot, all kv heads at once:
     K[slot // bs, g, slot % bs, :] = k_new[i, g, :]. A negative slot is
@@ -23,14 +26,22 @@ for fp32). Every operation here is a copy of bits, so results are exact.
 import numpy as np
 
 
-def slot_mapping(block_tables, positions, block_size=16):
+def slot_mapping(block_tables, positions, block_size=16, seq_ids=None):
+    """Token i belongs to sequence seq_ids[i] (default: i); a sequence index
+    outside the table's rows has no slot either."""
     bt = np.asarray(block_tables, dtype=np.int64)
     pos = np.asarray(positions, dtype=np.int64)
+    rows, width = bt.shape if bt.ndim == 2 else (0, 0)
+    seq = np.arange(pos.shape[0]) if seq_ids is None else np.asarray(seq_ids, dtype=np.int64)
+    largest = (2**31 - 1 - (block_size - 1)) // block_size
     out = np.full(pos.shape, -1, dtype=np.int32)
-    for s, p in enumerate(pos):
-        if p < 0:
+    for i, (s, p) in enumerate(zip(seq.tolist(), pos.tolist())):
+        if s < 0 or s >= rows or p < 0 or p // block_size >= width:
             continue
-        out[s] = bt[s, p // block_size] * block_size + p % block_size
+        b = int(bt[s, p // block_size])
+        if b < 0 or b > largest:
+            continue
+        out[i] = b * block_size + p % block_size
     return out
 
 

@@ -30,7 +30,7 @@ __all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "check_slots"
            "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError", "shared_groups", "decode_shared",
            "decode_shared_workspace_bytes", "check_groups",
-           "decode_shared_default_partition"]
+           "decode_shared_default_partition", "shared_plan"]
 
 BLOCK_SIZE = 16
 
@@ -283,6 +283,35 @@ def shared_groups(block_tables, context_lens, max_group):
                                  gs.ctypes.data, sh.ctypes.data, ctypes.byref(n)),
           "pa_shared_groups")
     return gs[:n.value + 1].copy(), sh
+
+
+def shared_plan(block_tables, context_lens, Hq, Hkv, max_group=16):
+    """How a batch whose sequences share leading blocks is decoded with
+    decode_shared(), from host tables: the groups of sharers, the shared-part
+    partition (the library's choice for the current device) and the two cache
+    flags. After grouping, a pass reads through the caches only when blocks
+    still repeat within it: groups_overlap when the shared parts of different
+    groups overlap (one prefix over several groups), shared_kv when sequences'
+    own blocks repeat. Returns None when no sequence shares a block with its
+    group. Host numpy arrays in and out (group_start, seq_shared)."""
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    gs, sh = shared_groups(bt, cl, max_group)
+    if not sh.any():
+        return None
+    shared_reads, own_reads = [], []
+    for j in range(len(gs) - 1):
+        a, b = int(gs[j]), int(gs[j + 1])
+        nsh = int(sh[a]) // BLOCK_SIZE
+        shared_reads += bt[a, :nsh].tolist()
+        for s in range(a, b):
+            own_reads += bt[s, nsh:(int(cl[s]) + BLOCK_SIZE - 1) // BLOCK_SIZE].tolist()
+    max_shared = int(sh.max())
+    return dict(group_start=gs, seq_shared=sh, max_group=int(max_group), max_shared=max_shared,
+                partition=decode_shared_default_partition(len(gs) - 1, Hq, Hkv, max_group,
+                                                          max_shared),
+                groups_overlap=len(set(shared_reads)) < len(shared_reads),
+                shared_kv=len(set(own_reads)) < len(own_reads))
 
 
 def decode_shared_default_partition(n_groups, Hq, Hkv, max_group, max_shared):

@@ -10,7 +10,11 @@
 
 namespace pa {
 
-// slot = table[seq][p / 16] * 16 + p % 16, or -1 when there is no valid slot.
+// Largest block id whose slots all fit an int32 slot number.
+constexpr int32_t kMaxSlotBlock = (INT32_MAX - (kBlock - 1)) / kBlock;
+
+// slot = table[seq][p / 16] * 16 + p % 16, or -1 when there is no valid slot
+// (a negative table entry, or one whose slots would not fit an int32).
 __device__ __forceinline__ int32_t slot_of(const int32_t* __restrict__ bt,
                                            const int32_t* __restrict__ seq_ids,
                                            const int32_t* __restrict__ pos, int32_t i, int32_t B,
@@ -20,7 +24,7 @@ __device__ __forceinline__ int32_t slot_of(const int32_t* __restrict__ bt,
   int32_t slot = -1;
   if (s >= 0 && s < B && p >= 0 && p / kBlock < MB) {
     const int32_t b = bt[(size_t)s * MB + p / kBlock];
-    if (b >= 0) slot = b * kBlock + p % kBlock;
+    if (b >= 0 && b <= kMaxSlotBlock) slot = b * kBlock + p % kBlock;
   }
   return slot;
 }

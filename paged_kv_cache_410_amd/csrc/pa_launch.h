@@ -78,19 +78,24 @@ __device__ __forceinline__ float elem_f32(_Float16 x) { return (float)x; }
 // an equivalent state: raising a state's max by log2 c multiplies its weight
 // 2^(m - M) in every later merge by c, which the division of o and l by c
 // undoes, so the merge kernel and the tail pass take it like any other partial. o / l is a
-// convex combination of V rows, so |z| <= max |v| * 2^-k; k > 0 only when that
-// bound passes 2^15, which keeps z inside fp16's range (largest finite 65504).
-// fp16's 11-bit significand leaves the final bf16 rounding as the dominant
-// error. amax is the row's max |o|.
+// convex combination of V rows; with y = max |o / l| and k = floor(log2 y) - 14
+// the row's largest |z| lies in [2^14, 2^15), inside fp16's normal range
+// (largest finite 65504, smallest normal 2^-14) whatever the scale of V, so
+// every element keeps fp16's 11-bit significand relative to the row's largest
+// and the final bf16 rounding stays the dominant error. k is clamped to
+// [-100, 113]: 2^-k stays a normal fp32, and l' = 2^-k <= 2^100 leaves the
+// merges' fp32 sums of up to 65535 partials far from overflow (only rows
+// whose every |o / l| is below 2^-114 then keep z below fp16's normal range).
+// amax is the row's max |o|.
 struct PartScale {
   float mul, m, l;  // store o * mul, and (m, l)
 };
 __device__ __forceinline__ PartScale part_scale_f16(float m, float l, float amax) {
   if (!(l > 0.0f)) return {0.0f, m, l};  // no token: zero row, weight 0
   const float y = amax / l;
-  int k = 0;
-  if (y >= 32768.0f) k = (int)((__float_as_uint(y) >> 23) & 0xffu) - 127 - 14;  // y / 2^k < 2^15
-  const float inv_pow = __uint_as_float((uint32_t)(127 - k) << 23);                // 2^-k
+  int k = (int)((__float_as_uint(y) >> 23) & 0xffu) - 127 - 14;  // floor(log2 y) - 14
+  k = k < -100 ? -100 : (k > 113 ? 113 : k);
+  const float inv_pow = __uint_as_float((uint32_t)(127 - k) << 23);  // 2^-k
   return {inv_pow / l, m + __builtin_amdgcn_logf(l) + (float)k, inv_pow};
 }
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {

@@ -17,3 +17,12 @@ def oracle_mod():
     import oracle
     oracle.build()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    cases = sys.modules.get("gpu_cases")
+    log = getattr(cases, "PARITY_LOG", None)
+    if log:
+        terminalreporter.write_sep("-", "whole-output parity (max abs error vs the fp64 oracle)")
+        for what, err, tol in log:
+            terminalreporter.write_line(f"{what}: {err:.3e} (tolerance {tol:g})")

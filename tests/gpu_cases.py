@@ -20,6 +20,15 @@ def say(*a):
     sys.stdout.flush()
 
 
+# (what, max abs error, tolerance) of whole-output comparisons, printed in the
+# terminal summary of the run (tests/conftest.py) even when output is captured
+PARITY_LOG = []
+
+
+def record_parity(what, err, tol):
+    PARITY_LOG.append((what, float(err), float(tol)))
+
+
 def host_bits(t):
     """Raw element bits of a tensor as a numpy array (uint16 bf16 / uint32 fp32)."""
     t = t.detach().cpu().contiguous()

@@ -97,7 +97,7 @@ def test_bad_row_counts_poison_only_their_rows(pa):
     assert torch.isnan(out[qs[1]:qs[2]]).all()
     keep = torch.ones(out.shape[0], dtype=torch.bool)
     keep[qs[1]:qs[2]] = False
-    assert torch.allclose(out[keep], good[keep], atol=1e-2)
+    assert torch.equal(out[keep], good[keep])   # the intact rows keep their bits
 
 
 @pytest.mark.parametrize("name", list(CHUNKS))

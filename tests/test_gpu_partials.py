@@ -2,10 +2,12 @@
 
 A partition's partial (running max m, sum l, unnormalised row o) travels to
 the merge as an fp16 row z = o / c with (m + log2 c, l / c), c = l * 2^k: an
-equivalent online-softmax state. k > 0 only when max |o / l| passes 2^15, to
-keep z inside fp16's range. These cases scale V by powers of two far past that
-range (exact in bf16, and the attention output scales by the same power), so
-every fp16 partial takes the k > 0 branch: the vector kernel's (one query head
+equivalent online-softmax state, with k chosen so that the row's largest |z|
+lies in [2^14, 2^15). These cases scale V by powers of two far past fp16's
+range both ways (exact in bf16, and the attention output scales by the same
+power): 2^20 and 2^100 need k > 0 to stay finite, 2^-20 needs k < 0 to stay
+out of fp16's subnormals (fixed spacing 2^-24, a 6% error on rows of size
+2^-20). Every fp16 partial is covered: the vector kernel's (one query head
 per kv head; head_dim 128 and 64), the matrix-core kernel's (grouped heads)
 and the shared-prefix group pass's on that kernel. The chunk kernel (several
 query rows, one and two column tiles per wave; shared-prefix groups wider than
@@ -63,7 +65,7 @@ def check(out, st, shift):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("shift", [0, 20, 100])
+@pytest.mark.parametrize("shift", [0, 20, 100, -20])
 @pytest.mark.parametrize("partition", [64, 512])
 def test_partials_past_fp16_range(pa, name, shift, partition):
     spec = CASES[name]
@@ -74,7 +76,7 @@ def test_partials_past_fp16_range(pa, name, shift, partition):
     check(out, st, shift)
 
 
-@pytest.mark.parametrize("shift", [0, 20, 100])
+@pytest.mark.parametrize("shift", [0, 20, 100, -20])
 @pytest.mark.parametrize("partition", [0, 32])
 @pytest.mark.parametrize("max_group", [4, 8])  # 16 columns (matrix-core kernel), 32 (chunk)
 def test_shared_prefix_group_partials_past_fp16_range(pa, shift, partition, max_group):

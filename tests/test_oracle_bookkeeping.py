@@ -173,6 +173,19 @@ def test_slot_mapping_agrees_with_block_manager():
     assert cache_ops.slot_mapping(bt, pos, 16)[2] == -1
 
 
+def test_slot_mapping_entries_without_a_slot():
+    # A table entry names a physical block only when it is >= 0 and its
+    # slots fit int32 slot numbers; a position must lie inside the table.
+    big = (2**31 - 1 - 15) // 16          # 134217727: slots up to 2^31 - 1
+    bt = np.array([[5, -1, 7], [2, 3, 2**28 + 1], [big, big + 1, 0]], np.int32)
+    pos = [0, 17, 47, 48, -1, 33, 15, 16, 31, 3]
+    seq = [0, 0, 0, 0, 1, 1, 2, 2, 2, 3]
+    got = cache_ops.slot_mapping(bt, pos, 16, seq_ids=seq).tolist()
+    assert got == [80, -1, 7 * 16 + 15, -1, -1, -1, 2**31 - 1, -1, -1, -1]
+    # seq_ids default to the token index
+    assert cache_ops.slot_mapping(bt, [1, 20], 16).tolist() == [81, 3 * 16 + 4]
+
+
 @pytest.mark.parametrize("dt", [np.uint16, np.uint32])
 def test_write_kv_touches_only_its_slots(dt):
     rng = np.random.default_rng(5)
