@@ -22,9 +22,11 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every tensor argument is a DEVICE pointer owned by the caller; the
- *    library never allocates, frees or keeps device memory and keeps no state
- *    between calls (the block manager at the end is host-only and owns only
- *    host memory). Tensors are dense and row-major in the shapes given.
+ *    library never allocates or frees device memory and keeps no state
+ *    between calls, with one exception: the scratch area of
+ *    pa_decode_noalloc, reserved with the library's code on each GPU (the
+ *    block manager at the end is host-only and owns only host memory).
+ *    Tensors are dense and row-major in the shapes given.
  *  - Cache pools: k_cache and v_cache are [NB][Hkv][bs][D] each: one
  *    (block, kv head) tile is bs contiguous token rows of D elements.
  *  - Element type `dt` (PA_F32 or PA_BF16) applies to q, out, the new K/V
@@ -38,7 +40,8 @@
  *  - Device-side contents are read defensively: an out-of-range block id,
  *    slot or context length never causes an out-of-bounds access. What each
  *    call does with such entries is stated with the call.
- *  - Thread-safe and reentrant: no global mutable state.
+ *  - Thread-safe and reentrant: no global mutable state, apart from
+ *    pa_decode_noalloc's per-GPU scratch area (see there).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -289,6 +292,37 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache,
                     int32_t max_ctx, float scale, int32_t partition,
                     void* workspace, size_t workspace_bytes, uint32_t flags,
                     pa_dtype dt, hipStream_t stream);
+
+/*
+ * pa_decode_noalloc — pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, hosts that
+ * forbid hipMalloc. It takes no workspace: split-context partials go to a
+ * scratch area of PA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds
+ * on each GPU it runs on, from the loading of its code there until the
+ * process ends. The first call on a device looks up that device's copy
+ * (hipGetSymbolAddress); no call allocates or frees device memory.
+ *
+ * Arguments, results and error rows are pa_decode's, without workspace and
+ * workspace_bytes; the kernels, and so the output bits, are the same as
+ * pa_decode's with a workspace. A split whose pa_decode_workspace_bytes(B,
+ * Hq, D, max_ctx, partition) exceeds PA_NOALLOC_SCRATCH_BYTES returns
+ * PA_EWORKSPACE and launches nothing.
+ *
+ * Every call on one GPU shares that GPU's scratch area, which keeps the last
+ * call's contents. Nothing in it needs to start at zero (each call writes
+ * every partial it reads back), but calls that overlap in time on one GPU
+ * (other streams, other host threads) race on it: order them, e.g. on one
+ * stream. Unlike the other entry points, this one keeps state: the scratch
+ * area and the per-device address looked up on first use (thread-safe).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t D, int32_t bs, int32_t NB,
+                            int32_t MB, int32_t max_ctx, float scale,
+                            int32_t partition, uint32_t flags, pa_dtype dt,
+                            hipStream_t stream);
 
 /*
  * pa_decode_shared — pa_decode for a batch whose sequences share leading

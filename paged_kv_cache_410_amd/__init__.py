@@ -22,11 +22,11 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import (PA_BF16, PA_ENOBLOCKS, PA_F32, PA_KV_SHARED, PA_KV_SHARED_GROUPS,  # noqa: F401
-                   PAError, check, lib)
+from ._lib import (PA_BF16, PA_ENOBLOCKS, PA_EWORKSPACE, PA_F32, PA_KV_SHARED,  # noqa: F401
+                   PA_KV_SHARED_GROUPS, PA_NOALLOC_SCRATCH_BYTES, PAError, check, lib)
 
 __all__ = ["slot_mapping", "write_kv", "append_kv", "copy_blocks", "check_slots", "check_pairs",
-           "check_tables", "decode", "multi_query", "shares_blocks",
+           "check_tables", "decode", "decode_noalloc", "multi_query", "shares_blocks",
            "decode_workspace_bytes",
            "default_partition", "BlockManager", "PAError", "shared_groups", "decode_shared",
            "decode_shared_workspace_bytes", "check_groups",
@@ -264,6 +264,39 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx, part
                               block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs,
                               NB, MB, int(max_ctx), float(scale), int(partition), ws_ptr, ws_bytes,
                               PA_KV_SHARED if shared_kv else 0, _dt(q), _stream(dev)), "pa_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, max_ctx,
+                   partition=None, out=None, shared_kv=False):
+    """pa_decode without a workspace (pa_decode_noalloc): split-context
+    partials go to the library's per-GPU scratch area, so the C call allocates
+    nothing. Pass `out` to allocate nothing here either. Calls that overlap
+    in time on one GPU race on the scratch area."""
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _i32(block_tables, "block_tables")
+    _i32(context_lens, "context_lens")
+    B, Hq, Dq = q.shape
+    if Dq != D or q.dtype != k_cache.dtype:
+        raise ValueError("q must be [B, Hq, D] with the pools' dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    MB = block_tables.shape[1]
+    if partition is None:
+        with torch.cuda.device(q.device):
+            partition = default_partition(B, Hq, Hkv, D, max_ctx)
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, out)
+    with torch.cuda.device(dev):
+        check(lib().pa_decode_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                      v_cache.data_ptr(), block_tables.data_ptr(),
+                                      context_lens.data_ptr(), B, Hq, Hkv, D, bs, NB, MB,
+                                      int(max_ctx), float(scale), int(partition),
+                                      PA_KV_SHARED if shared_kv else 0, _dt(q), _stream(dev)),
+              "pa_decode_noalloc")
     return out
 
 

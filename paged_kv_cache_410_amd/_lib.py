@@ -32,6 +32,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                           c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_u32, c_i32, c_vp]),
+    "pa_decode_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
+                                  c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_u32, c_i32,
+                                  c_vp]),
     "pa_decode_shared_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_shared_default_partition": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pa_decode_shared": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
@@ -62,6 +65,7 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOBLOCKS = 0, -1,
 PA_F32, PA_BF16 = 0, 1
 PA_KV_SHARED = 1
 PA_KV_SHARED_GROUPS = 2
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 

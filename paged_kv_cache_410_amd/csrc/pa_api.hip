@@ -3,10 +3,43 @@
 // anything is launched; a failed check launches nothing.
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "pa.h"
 #include "pa_launch.h"
 
 namespace {
+
+// Scratch of pa_decode_noalloc: the split-context partials of callers that
+// cannot allocate. Each GPU the library runs on holds its own copy from the
+// time the library's code is loaded there until the process ends. In host
+// code `scratch` names a host-side stand-in, not device memory: only the
+// address hipGetSymbolAddress returns for the current device is passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // per device, null until looked up
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (looked up once per device).
+pa_status device_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_EUNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_EHIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return PA_OK;
+}
 
 constexpr int32_t kBs = 16;
 constexpr int32_t kMaxGridYZ = 65535;
@@ -195,7 +228,7 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
                     const int32_t* query_start, int32_t B, int32_t rows, int32_t max_q, int32_t Hq,
                     int32_t Hkv, int32_t D, int32_t bs, int32_t NB, int32_t MB, int32_t max_ctx,
                     float scale, int32_t partition, void* workspace, size_t workspace_bytes,
-                    uint32_t flags, pa_dtype dt, hipStream_t stream) {
+                    uint32_t flags, pa_dtype dt, hipStream_t stream, bool use_scratch = false) {
   if (B < 0 || rows < 0 || max_q < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || NB < 0 || MB < 0 ||
       max_ctx < 0 || !dtype_ok(dt) || (flags & ~PA_KV_SHARED) != 0 || !__builtin_isfinite(scale))
     return PA_EINVAL;
@@ -213,6 +246,13 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
 
   const int64_t parts = grid_parts(max_ctx, partition);
   const size_t need = pa_decode_workspace_bytes(rows, Hq, D, max_ctx, partition);
+  if (use_scratch && need > 0) {
+    // the library's own scratch in place of a caller's workspace
+    if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_EWORKSPACE;
+    const pa_status st = device_scratch(&workspace);
+    if (st != PA_OK) return st;
+    workspace_bytes = PA_NOALLOC_SCRATCH_BYTES;
+  }
   if (need > 0 && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
   if (need > 0 && ((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
   if (parts > kMaxGridYZ) return PA_EUNSUPPORTED;  // grid y
@@ -282,6 +322,16 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return attention(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, B, B, 1, Hq, Hkv,
                    D, bs, NB, MB, max_ctx, scale, partition, workspace, workspace_bytes, flags, dt,
                    stream);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t NB,
+                            int32_t MB, int32_t max_ctx, float scale, int32_t partition,
+                            uint32_t flags, pa_dtype dt, hipStream_t stream) {
+  return attention(out, q, k_cache, v_cache, block_tables, context_lens, nullptr, B, B, 1, Hq, Hkv,
+                   D, bs, NB, MB, max_ctx, scale, partition, nullptr, 0, flags, dt, stream,
+                   /*use_scratch=*/true);
 }
 
 int32_t pa_decode_shared_default_partition(int32_t n_groups, int32_t Hq, int32_t Hkv,

@@ -93,6 +93,29 @@ def test_decode_empty_batch_is_a_noop(palib):
     assert palib.lib().pa_decode(*decode_args(B=0, q=None, out=None)) == 0
 
 
+def noalloc_args(**kw):
+    a = decode_args(**kw)
+    del a[16:18]                               # no workspace, workspace_bytes
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(cl=None), -1), (dict(Hq=6, Hkv=4), -1), (dict(partition=24), -1),
+    (dict(bs=32), -2), (dict(D=96), -2), (dict(dt=7), -1), (dict(q=FAKE + 8), -1),
+    (dict(B=70000), -2), (dict(flags=2), -1), (dict(scale=float("nan")), -1),
+    # partials past the library's scratch area: 2 x 8 heads x 65536 partitions
+    (dict(partition=16, max_ctx=1 << 20), -3),
+])
+def test_decode_noalloc_rejects_bad_arguments(palib, kw, status):
+    # every case fails on the host, before the scratch area is looked up
+    assert palib.lib().pa_decode_noalloc(*noalloc_args(**kw)) == status
+
+
+def test_decode_noalloc_empty_batch_is_a_noop(palib):
+    assert palib.lib().pa_decode_noalloc(*noalloc_args(B=0, q=None, out=None)) == 0
+    assert palib.PA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 def multi_args(**kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, B=2, Tq=6, max_q=4,
              Hq=8, Hkv=2, D=128, bs=16, NB=10, MB=4, max_ctx=64, scale=0.1, partition=0,
