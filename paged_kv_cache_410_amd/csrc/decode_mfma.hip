@@ -57,6 +57,17 @@
 #ifndef PA_MFMA_DEPTH
 #define PA_MFMA_DEPTH 2
 #endif
+// Waves per workgroup of the group pass with the members' own blocks folded
+// in: PA_MFMA_FOLD_WAVES_FEW when the pass has at most one workgroup per
+// compute unit (the prefix batch, 256 workgroups: 105 vs 110 us with 4),
+// else PA_MFMA_FOLD_WAVES (the copy-on-write batch, 512: 4 waves 113 vs 114
+// with 8).
+#ifndef PA_MFMA_FOLD_WAVES
+#define PA_MFMA_FOLD_WAVES 4
+#endif
+#ifndef PA_MFMA_FOLD_WAVES_FEW
+#define PA_MFMA_FOLD_WAVES_FEW 8
+#endif
 // Minimum waves per SIMD the register allocation must allow.
 #ifndef PA_MFMA_MIN_WAVES
 #define PA_MFMA_MIN_WAVES 3
@@ -68,7 +79,18 @@ namespace pa {
 // takes blocks w, w + NW, ...) and merge their states through LDS. A kv head
 // with more than one tile (several query rows per sequence) goes to the
 // chunk kernel instead, whose waves share each block.
-template <int NW, int DEPTH, TilePolicy kPolicy>
+//
+// kFold (the shared-prefix group pass, one partition, one tile): after the
+// group's shared blocks (every column), each member's own blocks, read
+// through its own table row, with only that member's columns unmasked; the
+// workgroup then writes the members' final rows. Member j's own blocks
+// S_j / 16 + w, + w + NW, ... go to wave w, so the order of a member's
+// arithmetic does not depend on the other members: their blocks reach its
+// columns as masked logits, which leave its state bit for bit as it was
+// (probabilities 0, rescale by exactly 1). kTailPolicy is the cache policy of
+// the members' own blocks.
+template <int NW, int DEPTH, TilePolicy kPolicy, bool kFold = false,
+          TilePolicy kTailPolicy = kPolicy>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES)))
 void decode_mfma_kernel(DecodeParams P) {
   constexpr int D = 128;
@@ -151,7 +173,52 @@ void decode_mfma_kernel(DecodeParams P) {
   f32x4_t acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  bool bad = bad_ctx;
+  bool bad = bad_ctx;   // the whole tile (wave-uniform)
+  bool bad_me = false;  // this lane's column only (kFold: its member's own blocks)
+
+  // kFold: lane j < members holds member j's context, its first own block and
+  // how many of its own blocks this wave reads (blocks w, w + NW, ... of its
+  // run), with the exclusive prefix sum of those counts; ttot = this wave's
+  // own-block items, all members together.
+  int m_ctx = 0, m_b0 = 0, m_cum = 0, ttot = 0;
+  if constexpr (kFold) {
+    const int nm = min(sr.n, P.max_q);  // 0 when the group's bounds are malformed
+    int m_cnt = 0;
+    bool m_bad = false;
+    if (lane < nm) {
+      m_ctx = P.context_lens[sr.first + lane];
+      const int sh = P.seq_shared[sr.first + lane];
+      m_bad = m_ctx < 0 || m_ctx > P.ctx_limit || sh < 0 || sh % kBlock != 0 || sh > m_ctx;
+      m_b0 = m_bad ? 0 : sh / kBlock;
+      const int own = m_bad ? 0 : (m_ctx + kBlock - 1) / kBlock - m_b0;
+      m_cnt = own > w ? (own - w + NW - 1) / NW : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int cj = __builtin_amdgcn_readlane(m_cnt, j);
+      m_cum += j < lane ? cj : 0;
+      ttot += cj;
+    }
+    bad_me = __shfl(m_bad ? 1 : 0, qi) != 0;
+  }
+  // kFold: block id and tag (member j << 27 | logical block) of this wave's
+  // own-block item c0 + lane. Member j's items start at its prefix sum.
+  auto own_item = [&](int c0, int& id, int& tag) {
+    const int r = c0 + lane;
+    int j = 0;  // the member whose items hold r (members with none are passed over)
+#pragma unroll
+    for (int mm = 1; mm < 16; ++mm) j += r >= __builtin_amdgcn_readlane(m_cum, mm) ? 1 : 0;
+    const int b0 = __shfl(m_b0, j), cum = __shfl(m_cum, j);  // every lane takes part
+    id = -1;
+    tag = 0;
+    if (r < ttot) {
+      const int blk = b0 + w + NW * (r - cum);
+      id = P.block_tables[(size_t)(sr.first + j) * P.MB + blk];
+      tag = (j << 27) | blk;
+    }
+  };
+  int oids0 = -1, otags0 = 0;
+  if constexpr (kFold) own_item(0, oids0, otags0);  // in flight during the shared blocks
 
   const char* kbase = reinterpret_cast<const char*>(P.k_cache);
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
@@ -178,8 +245,27 @@ void decode_mfma_kernel(DecodeParams P) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) vb[j] = ld16<kPolicy>(rv, row_lane + j * kRowBytes);
   };
+  // kFold: member j's own block (tag): its rows inside the member's context;
+  // an id outside the pool spoils only that member's columns.
+  auto load_own = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, int tag, bool exists) {
+    const int j = tag >> 27, blk = tag & ((1 << 27) - 1);
+    const bool valid = b >= 0 && b < P.NB;
+    bad_me |= exists && !valid && qi == j;
+    const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
+    const int rows = min(kBlock, __builtin_amdgcn_readlane(m_ctx, j) - blk * kBlock);
+    const int bytes = exists && valid ? rows * kRowBytes : 0;
+    const rsrc_t rk = make_rsrc(kbase + off, bytes);
+    const rsrc_t rv = make_rsrc(vbase + off, bytes);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) kb[jj] = ld16<kTailPolicy>(rk, row_lane + jj * kRowBytes);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) vb[jj] = ld16<kTailPolicy>(rv, row_lane + jj * kRowBytes);
+  };
 
-  auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], int blk) {
+  // One tile: S^T, the online-softmax update and O^T += V^T P^T. When
+  // `partial`, this lane's tokens 4 rg + i at or past `lim` (tile-local) are
+  // masked.
+  auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], bool partial, int lim) {
     // Transpose K through the wave's LDS stage into the A operand layout:
     // step kk needs, in lane (rg, col), dims 32 kk + 8 rg .. + 7 (chunk
     // 4 kk + rg) of row t = col. Rows are kStageRow apart (256 B + 16 B of
@@ -195,14 +281,11 @@ void decode_mfma_kernel(DecodeParams P) {
       st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
                                                   0, 0, 0);
     }
-    const int tok0 = blk * kBlock + 4 * rg;
-    // Some column masks some row of this block (wave-uniform).
-    const bool partial = blk * kBlock + kBlock > ctx_min;
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[i] = st[i] * P.qscale;
-      if (partial && tok0 + i >= ctx_col) x[i] = -INFINITY;
+      if (partial && 4 * rg + i >= lim) x[i] = -INFINITY;
     }
     // Rows at or past the tile's longest context were not fetched (the tile's
     // buffer range ends there) and read as zeros, never as stale or NaN data.
@@ -248,7 +331,21 @@ void decode_mfma_kernel(DecodeParams P) {
         [&](int d, int b, int k, bool exists) {
           load(kb[d], vb[d], b, first + k * kStride, exists);
         },
-        [&](int d, int k) { consume(kb[d], vb[d], first + k * kStride); });
+        [&](int d, int k) {
+          const int blk = first + k * kStride;
+          // some column masks some row of this block (wave-uniform)
+          consume(kb[d], vb[d], blk * kBlock + kBlock > ctx_min, ctx_col - blk * kBlock);
+        });
+    if constexpr (kFold) {
+      list_pipeline<DEPTH>(
+          ttot, lane, oids0, otags0, own_item,
+          [&](int d, int b, int tag, bool exists) { load_own(kb[d], vb[d], b, tag, exists); },
+          [&](int d, int tag) {
+            const int j = tag >> 27, blk = tag & ((1 << 27) - 1);
+            const int lim = qi == j ? __builtin_amdgcn_readlane(m_ctx, j) - blk * kBlock : 0;
+            consume(kb[d], vb[d], true, lim);
+          });
+    }
   }
 
   lsum = rows_sum(lsum);  // per column: sum over the 4 row groups
@@ -256,6 +353,7 @@ void decode_mfma_kernel(DecodeParams P) {
   // Waves -> LDS -> one merged state per (head, dim).
   __shared__ float sm_m[NW][16], sm_l[NW][16];
   __shared__ int sm_bad[NW];
+  __shared__ int sm_badc[kFold ? NW : 1][16];  // kFold: per column
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     float* dst = &sm_o[w][col][8 * (4 * rg + i)];
@@ -266,6 +364,7 @@ void decode_mfma_kernel(DecodeParams P) {
   if (rg == 0) {
     sm_m[w][col] = m;
     sm_l[w][col] = lsum;
+    if constexpr (kFold) sm_badc[w][col] = bad_me ? 1 : 0;
   }
   if (lane == 0) sm_bad[w] = bad ? 1 : 0;
   __syncthreads();
@@ -285,6 +384,11 @@ void decode_mfma_kernel(DecodeParams P) {
     const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock - is.start_blk;
     const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
     if (np <= 1 ? p != 0 : p >= np) continue;
+    bool col_bad = any_bad;
+    if constexpr (kFold) {
+#pragma unroll
+      for (int v = 0; v < NW; ++v) col_bad |= sm_badc[v][qq] != 0;
+    }
     float M = sm_m[0][qq];
 #pragma unroll
     for (int v = 1; v < NW; ++v) M = fmaxf(M, sm_m[v][qq]);
@@ -329,7 +433,7 @@ void decode_mfma_kernel(DecodeParams P) {
       const float inv = L > 0.0f ? 1.0f / L : 0.0f;
       float res[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) res[e] = any_bad ? __builtin_nanf("") : ov[e] * inv;
+      for (int e = 0; e < 8; ++e) res[e] = col_bad ? __builtin_nanf("") : ov[e] * inv;
       uint4 u;
       u.x = pack_bf16x2(res[0], res[1]);
       u.y = pack_bf16x2(res[2], res[3]);
@@ -344,6 +448,28 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   // several column tiles per kv head: the chunk kernel, whose waves share each block
   if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
   constexpr int DEPTH = PA_MFMA_DEPTH;
+  if (p.fold_tails) {
+    // group pass with the members' own blocks folded in: the shared blocks'
+    // policy from shared_kv, the own blocks' from tail_shared_kv
+    auto fold = [&](auto nw) {
+      constexpr int NW = decltype(nw)::value;
+      constexpr TilePolicy S = TilePolicy::kShared, T = TilePolicy::kStream;
+      const dim3 grid(p.Hkv, 1, p.pass_items), block(NW * kWave);
+      if (p.shared_kv && p.tail_shared_kv)
+        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, S, true, S>), grid, block, 0, stream, p);
+      else if (p.shared_kv)
+        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, S, true, T>), grid, block, 0, stream, p);
+      else if (p.tail_shared_kv)
+        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, T, true, S>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, T, true, T>), grid, block, 0, stream, p);
+    };
+    if ((int64_t)p.Hkv * p.pass_items <= p.n_cus)
+      fold(std::integral_constant<int, PA_MFMA_FOLD_WAVES_FEW>{});
+    else
+      fold(std::integral_constant<int, PA_MFMA_FOLD_WAVES>{});
+    return hipGetLastError();
+  }
   auto go = [&](auto nw) {
     constexpr int NW = decltype(nw)::value;
     const dim3 grid(p.Hkv * p.n_tiles, p.pass_parts, p.pass_items), block(NW * kWave);

@@ -50,6 +50,11 @@
 #ifndef PA_VALU_DEPTH
 #define PA_VALU_DEPTH 3
 #endif
+// Ring depth of the tail pass: its runs of blocks are short (copy-on-write
+// batch: 57.9 us at depth 2 against 60.5 at 3).
+#ifndef PA_VALU_TAIL_DEPTH
+#define PA_VALU_TAIL_DEPTH 2
+#endif
 
 namespace pa {
 
@@ -121,7 +126,9 @@ __device__ __forceinline__ void merge_all_rows(float& m, float& l, float (&o)[EP
 
 }  // namespace
 
-template <typename T, int D, int NW, int DEPTH, TilePolicy kPolicy>
+// kTail: the shared-prefix tail pass (P.tail_pass), the only instantiations
+// that merge group-pass partials.
+template <typename T, int D, int NW, int DEPTH, TilePolicy kPolicy, bool kTail = false>
 __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P) {
   constexpr int EPL = Elem<T>::kPerChunk;  // elements per 16-byte lane chunk
   constexpr int LPT = D / EPL;             // lanes per token row
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
       L = ps.l;
     }
   } else {
-    if (P.tail_pass)
+    if constexpr (kTail)
       merge_shared_partials<T, EPL>(P, is.bad ? 0 : is.start_blk * kBlock, row, h, c * EPL, D, M,
                                     L, outv);
     mul = L > 0.0f ? 1.0f / L : 0.0f;  // empty context -> zeros
@@ -367,26 +374,25 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   }
 }
 
-template <TilePolicy kPolicy, int NW>
+template <TilePolicy kPolicy, int NW, int DEPTH = PA_VALU_DEPTH, bool kTail = false>
 hipError_t launch_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
-  constexpr int DEPTH = PA_VALU_DEPTH;
   const dim3 grid(p.Hq * p.max_q, p.pass_parts, p.pass_items), block(NW * kWave);
   if (dtype == 1 && D == 128)
-    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW, DEPTH, kPolicy>), grid, block, 0,
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 128, NW, DEPTH, kPolicy, kTail>), grid, block, 0,
                        stream, p);
   else if (dtype == 1 && D == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW, DEPTH, kPolicy>), grid, block, 0,
+    hipLaunchKernelGGL((decode_valu_kernel<uint16_t, 64, NW, DEPTH, kPolicy, kTail>), grid, block, 0,
                        stream, p);
   else if (dtype == 0 && D == 128) {
     // fp32 rows of 128 need ~220 registers: at most 8 waves per workgroup
     if constexpr (NW <= 8)
-      hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW, DEPTH, kPolicy>), grid, block, 0,
+      hipLaunchKernelGGL((decode_valu_kernel<float, 128, NW, DEPTH, kPolicy, kTail>), grid, block, 0,
                          stream, p);
     else
       return hipErrorInvalidValue;
   }
   else if (dtype == 0 && D == 64)
-    hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW, DEPTH, kPolicy>), grid, block, 0,
+    hipLaunchKernelGGL((decode_valu_kernel<float, 64, NW, DEPTH, kPolicy, kTail>), grid, block, 0,
                        stream, p);
   else
     return hipErrorInvalidValue;
@@ -394,9 +400,11 @@ hipError_t launch_valu(const DecodeParams& p, int dtype, int D, hipStream_t stre
 }
 
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
+  constexpr int TD = PA_VALU_TAIL_DEPTH;
   if (p.tail_pass)
-    return p.shared_kv ? launch_valu<TilePolicy::kShared, PA_VALU_TAIL_WAVES>(p, dtype, D, stream)
-                       : launch_valu<TilePolicy::kStream, PA_VALU_TAIL_WAVES>(p, dtype, D, stream);
+    return p.shared_kv
+               ? launch_valu<TilePolicy::kShared, PA_VALU_TAIL_WAVES, TD, true>(p, dtype, D, stream)
+               : launch_valu<TilePolicy::kStream, PA_VALU_TAIL_WAVES, TD, true>(p, dtype, D, stream);
   if (p.few_items)
     return p.shared_kv ? launch_valu<TilePolicy::kShared, PA_VALU_WAVES_FEW>(p, dtype, D, stream)
                        : launch_valu<TilePolicy::kStream, PA_VALU_WAVES_FEW>(p, dtype, D, stream);

@@ -9,6 +9,12 @@
 #include "pa.h"
 #include "pa_launch.h"
 
+// pa_decode_shared in one pass where it can (1), or always as a group pass
+// and a tail pass (0, for measurement).
+#ifndef PA_FOLD_TAILS
+#define PA_FOLD_TAILS 1
+#endif
+
 namespace {
 
 // Scratch of pa_decode_noalloc: the split-context partials of callers that
@@ -424,6 +430,24 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
     p.ws_o = static_cast<char*>(workspace) + align_up(nrows * 2 * sizeof(float));
   }
 
+  // One partition of the shared part and one column tile per kv head: a
+  // single pass, each group's workgroup reading its shared blocks and then
+  // every member's own blocks, writing the final rows (the workspace goes
+  // unused).
+  if (PA_FOLD_TAILS && nps <= 1 && group_tiles == 1) {
+    pa::DecodeParams g = p;
+    g.group_start = group_start;
+    g.fold_tails = 1;
+    g.shared_kv = (flags & PA_KV_SHARED_GROUPS) ? 1 : 0;
+    g.tail_shared_kv = (flags & PA_KV_SHARED) ? 1 : 0;
+    g.max_q = max_group;
+    g.n_tiles = 1;
+    g.partition = 0;
+    g.pass_parts = 1;
+    g.pass_items = n_groups;
+    g.n_cus = device_cus();
+    return pa::launch_decode_mfma(g, stream) == hipSuccess ? PA_OK : PA_EHIP;
+  }
   // 1. group pass: each group's shared tokens, read once for all its members
   if (nps > 0) {
     pa::DecodeParams g = p;

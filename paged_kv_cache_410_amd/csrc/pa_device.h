@@ -298,4 +298,34 @@ __device__ __forceinline__ void block_pipeline(const int32_t* row, int first, in
   }
 }
 
+// The same pipeline over a wave's items k = 0 .. k1 - 1 of any list: item k's
+// block id and a tag (what the caller needs to place it) come from
+// fetch(c0, id, tag), lane j giving item c0 + j, 64 items at a time; the
+// first 64 (ids0, tags0) are fetched by the caller, early. load(slot, id,
+// tag, exists) and consume(slot, tag) as in block_pipeline.
+template <int DEPTH, typename Fetch, typename Load, typename Consume>
+__device__ __forceinline__ void list_pipeline(int k1, int lane, int ids0, int tags0, Fetch&& fetch,
+                                              Load&& load, Consume&& consume) {
+  for (int c0 = 0; c0 < k1; c0 += kWave) {
+    int ids = ids0, tags = tags0;
+    if (c0 > 0) fetch(c0, ids, tags);
+    const int cn = min(kWave, k1 - c0);
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) {
+      const int jl = min(d, kWave - 1);
+      load(d, __builtin_amdgcn_readlane(ids, jl), __builtin_amdgcn_readlane(tags, jl), d < cn);
+    }
+    for (int j0 = 0; j0 < cn; j0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int j = j0 + d;
+        const int jl = min(j + DEPTH - 1, kWave - 1);
+        load((d + DEPTH - 1) % DEPTH, __builtin_amdgcn_readlane(ids, jl),
+             __builtin_amdgcn_readlane(tags, jl), j + DEPTH - 1 < cn);
+        if (j < cn) consume(d, __builtin_amdgcn_readlane(tags, j));
+      }
+    }
+  }
+}
+
 }  // namespace pa

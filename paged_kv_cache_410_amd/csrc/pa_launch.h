@@ -41,6 +41,11 @@ struct DecodeParams {
   const int32_t* group_start;   // [n_groups + 1] (group pass)
   const int32_t* seq_shared;    // [B] shared tokens per sequence, a multiple of 16
   int32_t tail_pass;            // 1: attend from seq_shared[s] on
+  int32_t fold_tails;           // group pass only: after the shared blocks, each member's own
+                                // blocks too (its columns alone), and the final rows: no tail
+                                // pass, no partials
+  int32_t tail_shared_kv;       // fold_tails: the members' own blocks read through the caches
+  int32_t n_cus;                // compute units of the device (launch shapes)
   int32_t part_base;            // first partial slot this pass writes
   int32_t always_partial;       // write partials even for a single partition
   int32_t shared_partition;     // tail pass: partition length of the group pass (0 = one)
