@@ -89,12 +89,16 @@ namespace pa {
 // columns as masked logits, which leave its state bit for bit as it was
 // (probabilities 0, rescale by exactly 1). kTailPolicy is the cache policy of
 // the members' own blocks.
-template <int NW, int DEPTH, TilePolicy kPolicy, bool kFold = false,
+template <int D, int NW, int DEPTH, TilePolicy kPolicy, bool kFold = false,
           TilePolicy kTailPolicy = kPolicy>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(PA_MFMA_MIN_WAVES)))
 void decode_mfma_kernel(DecodeParams P) {
-  constexpr int D = 128;
+  static_assert(D == 128 || D == 64, "head_dim");
   constexpr int kRowBytes = D * 2;
+  constexpr int kQK = D / 32;         // 16x16x32 steps of S^T over D
+  constexpr int kPiece = D / 8;       // bytes of a row per lane of a 16-lane group
+  constexpr int kTiles = D / 16;      // 16-dim output tiles of O^T
+  using Piece = typename TilePiece<kPiece>::type;
   constexpr int kPad = 4;  // LDS row padding (floats) against bank conflicts
   constexpr int kStageRow = kRowBytes + 16;  // LDS stride of a staged K row
   static_assert(kBlock * kStageRow <= 16 * (D + kPad) * 4, "K stage must fit a merge region");
@@ -140,7 +144,7 @@ void decode_mfma_kernel(DecodeParams P) {
   const int qrow = sr.first + qi;
 
   // B operand of S^T: Q[column col][32 kk + 8 rg ..], zero for padded columns.
-  bf16x8_t qop[4];
+  bf16x8_t qop[kQK];
   // LDS, one region per wave: while the wave streams its blocks, the first
   // kStageBytes hold the K tile it is transposing (below); at the end the
   // region holds the wave's merge rows (16 columns x D floats, padded). The
@@ -151,7 +155,7 @@ void decode_mfma_kernel(DecodeParams P) {
   {
     const char* qp = reinterpret_cast<const char*>(P.q) + ((size_t)qrow * P.Hq + qh) * kRowBytes;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < kQK; ++kk) {
       uint4 u = ld16(qp + (32 * kk + 8 * rg) * 2);
       if (!col_ok) u = make_uint4(0, 0, 0, 0);
       qop[kk] = __builtin_bit_cast(bf16x8_t, u);
@@ -170,9 +174,9 @@ void decode_mfma_kernel(DecodeParams P) {
   if (p >= max(nparts_s, 1)) return;  // partition past the tile's longest context
 
   float m = -INFINITY, lsum = 0.0f;
-  f32x4_t acc[8];
+  f32x4_t acc[kTiles];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = 0; e < kTiles; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   bool bad = bad_ctx;   // the whole tile (wave-uniform)
   bool bad_me = false;  // this lane's column only (kFold: its member's own blocks)
 
@@ -224,14 +228,15 @@ void decode_mfma_kernel(DecodeParams P) {
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
   const size_t head_off = (size_t)g * kBlock * kRowBytes;
   const size_t block_stride = (size_t)P.Hkv * kBlock * kRowBytes;
-  // K and V tiles are loaded alike, whole 256-byte rows per load: lane holds
-  // chunk col (dims 8 col .. 8 col + 7) of row 4 rg + j in register j.
-  const int row_lane = (4 * rg) * kRowBytes + 8 * col * 2;  // + 1 row per j
+  // K and V tiles are loaded alike, four whole rows per load: lane holds
+  // piece col (dims (kPiece / 2) col .. + kPiece / 2 - 1) of row 4 rg + j in
+  // register j.
+  const int row_lane = (4 * rg) * kRowBytes + col * kPiece;  // + 1 row per j
 
   // Issue the loads of physical block b's tile (logical block blk) into
   // (kb, vb). An id outside the pool marks the group bad and loads nothing;
   // so does a block that does not exist (an empty ring refill).
-  auto load = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, int blk, bool exists) {
+  auto load = [&](Piece (&kb)[4], Piece (&vb)[4], int b, int blk, bool exists) {
     const bool valid = b >= 0 && b < P.NB;
     bad |= exists && !valid;
     const size_t off = (size_t)(valid ? b : 0) * block_stride + head_off;
@@ -241,13 +246,13 @@ void decode_mfma_kernel(DecodeParams P) {
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kb[j] = ld16<kPolicy>(rk, row_lane + j * kRowBytes);
+    for (int j = 0; j < 4; ++j) kb[j] = ld_piece<kPolicy, kPiece>(rk, row_lane + j * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vb[j] = ld16<kPolicy>(rv, row_lane + j * kRowBytes);
+    for (int j = 0; j < 4; ++j) vb[j] = ld_piece<kPolicy, kPiece>(rv, row_lane + j * kRowBytes);
   };
   // kFold: member j's own block (tag): its rows inside the member's context;
   // an id outside the pool spoils only that member's columns.
-  auto load_own = [&](uint4 (&kb)[4], uint4 (&vb)[4], int b, int tag, bool exists) {
+  auto load_own = [&](Piece (&kb)[4], Piece (&vb)[4], int b, int tag, bool exists) {
     const int j = tag >> 27, blk = tag & ((1 << 27) - 1);
     const bool valid = b >= 0 && b < P.NB;
     bad_me |= exists && !valid && qi == j;
@@ -257,26 +262,28 @@ void decode_mfma_kernel(DecodeParams P) {
     const rsrc_t rk = make_rsrc(kbase + off, bytes);
     const rsrc_t rv = make_rsrc(vbase + off, bytes);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) kb[jj] = ld16<kTailPolicy>(rk, row_lane + jj * kRowBytes);
+    for (int jj = 0; jj < 4; ++jj)
+      kb[jj] = ld_piece<kTailPolicy, kPiece>(rk, row_lane + jj * kRowBytes);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) vb[jj] = ld16<kTailPolicy>(rv, row_lane + jj * kRowBytes);
+    for (int jj = 0; jj < 4; ++jj)
+      vb[jj] = ld_piece<kTailPolicy, kPiece>(rv, row_lane + jj * kRowBytes);
   };
 
   // One tile: S^T, the online-softmax update and O^T += V^T P^T. When
   // `partial`, this lane's tokens 4 rg + i at or past `lim` (tile-local) are
   // masked.
-  auto consume = [&](const uint4 (&kb)[4], const uint4 (&vbin)[4], bool partial, int lim) {
+  auto consume = [&](const Piece (&kb)[4], const Piece (&vbin)[4], bool partial, int lim) {
     // Transpose K through the wave's LDS stage into the A operand layout:
-    // step kk needs, in lane (rg, col), dims 32 kk + 8 rg .. + 7 (chunk
-    // 4 kk + rg) of row t = col. Rows are kStageRow apart (256 B + 16 B of
-    // padding), so both the row writes and the strided reads are free of
-    // bank conflicts.
+    // step kk needs, in lane (rg, col), dims 32 kk + 8 rg .. + 7 (16-byte
+    // chunk 4 kk + rg) of row t = col. Rows are kStageRow apart (the row plus
+    // 16 B of padding), so both the row writes and the strided reads are
+    // free of bank conflicts.
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<uint4*>(stage + (4 * rg + j) * kStageRow + col * 16) = kb[j];
+      *reinterpret_cast<Piece*>(stage + (4 * rg + j) * kStageRow + col * kPiece) = kb[j];
     f32x4_t st = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int kk = 0; kk < kQK; ++kk) {
       const uint4 ka = *reinterpret_cast<const uint4*>(stage + col * kStageRow + (4 * kk + rg) * 16);
       st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qop[kk], st,
                                                   0, 0, 0);
@@ -289,7 +296,7 @@ void decode_mfma_kernel(DecodeParams P) {
     }
     // Rows at or past the tile's longest context were not fetched (the tile's
     // buffer range ends there) and read as zeros, never as stale or NaN data.
-    const uint4 (&vb)[4] = vbin;
+    const Piece (&vb)[4] = vbin;
     const float mx = rows_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     const float m_new = fmaxf(m, mx);
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
@@ -304,13 +311,13 @@ void decode_mfma_kernel(DecodeParams P) {
     m = m_new;
     if (rescale) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+      for (int e = 0; e < kTiles; ++e) acc[e] *= alpha;
     }
     const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
     const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
     const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {  // 32-bit word k of each V chunk: dims 2k, 2k+1
+    for (int k = 0; k < kPiece / 4; ++k) {  // 32-bit word k of each V piece: dims 2k, 2k+1
       const uint32_t w0 = word(vb[0], k), w1 = word(vb[1], k);
       const uint32_t w2 = word(vb[2], k), w3 = word(vb[3], k);
       const s16x4_t a_lo = __builtin_bit_cast(s16x4_t, make_uint2(pack_lo16(w0, w1), pack_lo16(w2, w3)));
@@ -325,7 +332,7 @@ void decode_mfma_kernel(DecodeParams P) {
     const int nk = first < blk_end ? (blk_end - first + kStride - 1) / kStride : 0;
     // tail pass: skip this wave's blocks inside the shared part
     const int k0 = is.start_blk > first ? (is.start_blk - first + kStride - 1) / kStride : 0;
-    uint4 kb[DEPTH][4], vb[DEPTH][4];
+    Piece kb[DEPTH][4], vb[DEPTH][4];
     block_pipeline<DEPTH>(
         bt_row, first, kStride, k0, nk, lane, ids0,
         [&](int d, int b, int k, bool exists) {
@@ -356,10 +363,12 @@ void decode_mfma_kernel(DecodeParams P) {
   __shared__ int sm_badc[kFold ? NW : 1][16];  // kFold: per column
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float* dst = &sm_o[w][col][8 * (4 * rg + i)];
-    // tile e holds dim 8 (4 rg + i) + e
-    *reinterpret_cast<float4*>(dst) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
-    *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4][i], acc[5][i], acc[6][i], acc[7][i]);
+    float* dst = &sm_o[w][col][kTiles * (4 * rg + i)];
+    // tile e holds dim kTiles (4 rg + i) + e
+#pragma unroll
+    for (int e4 = 0; e4 < kTiles; e4 += 4)
+      *reinterpret_cast<float4*>(dst + e4) =
+          make_float4(acc[e4][i], acc[e4 + 1][i], acc[e4 + 2][i], acc[e4 + 3][i]);
   }
   if (rg == 0) {
     sm_m[w][col] = m;
@@ -372,9 +381,11 @@ void decode_mfma_kernel(DecodeParams P) {
   bool any_bad = false;
 #pragma unroll
   for (int v = 0; v < NW; ++v) any_bad |= sm_bad[v] != 0;
-  // thread -> (column qq, 8-dim chunk ch)
-  for (int t = threadIdx.x; t < 16 * 16; t += NW * kWave) {
-    const int qq = t >> 4, ch = t & 15;
+  // thread -> (column qq, 8-dim chunk ch): a column's D / 8 threads are
+  // consecutive lanes
+  constexpr int kChunks = D / 8;
+  for (int t = threadIdx.x; t < 16 * kChunks; t += NW * kWave) {
+    const int qq = t / kChunks, ch = t % kChunks;
     const int c = c_begin + qq;
     if (c >= c_end) continue;
     const int i = c / P.G;
@@ -409,11 +420,11 @@ void decode_mfma_kernel(DecodeParams P) {
     // final row (the tail pass first folds in the group pass's partials of
     // the row).
     if (np > 1 || P.always_partial) {
-      // fp16 partial (see PartScale); the 16 lanes of a column form one DPP row
+      // fp16 partial (see PartScale); a column's lanes lie in one DPP row
       float amax = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(ov[e]));
-      const PartScale ps = part_scale_f16(M, L, group_max<16>(amax));
+      const PartScale ps = part_scale_f16(M, L, group_max<kChunks>(amax));
       uint4 u;
       u.x = pack_f16x2(ov[0] * ps.mul, ov[1] * ps.mul);
       u.y = pack_f16x2(ov[2] * ps.mul, ov[3] * ps.mul);
@@ -449,20 +460,25 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
   constexpr int DEPTH = PA_MFMA_DEPTH;
   if (p.fold_tails) {
-    // group pass with the members' own blocks folded in: the shared blocks'
-    // policy from shared_kv, the own blocks' from tail_shared_kv
+    // group pass with the members' own blocks folded in (head_dim 128): the
+    // shared blocks' policy from shared_kv, the own blocks' from tail_shared_kv
+    if (p.D != 128) return hipErrorInvalidValue;
     auto fold = [&](auto nw) {
       constexpr int NW = decltype(nw)::value;
       constexpr TilePolicy S = TilePolicy::kShared, T = TilePolicy::kStream;
       const dim3 grid(p.Hkv, 1, p.pass_items), block(NW * kWave);
       if (p.shared_kv && p.tail_shared_kv)
-        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, S, true, S>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, S, true, S>), grid, block, 0,
+                           stream, p);
       else if (p.shared_kv)
-        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, S, true, T>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, S, true, T>), grid, block, 0,
+                           stream, p);
       else if (p.tail_shared_kv)
-        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, T, true, S>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, T, true, S>), grid, block, 0,
+                           stream, p);
       else
-        hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, T, true, T>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, T, true, T>), grid, block, 0,
+                           stream, p);
     };
     if ((int64_t)p.Hkv * p.pass_items <= p.n_cus)
       fold(std::integral_constant<int, PA_MFMA_FOLD_WAVES_FEW>{});
@@ -470,24 +486,33 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
       fold(std::integral_constant<int, PA_MFMA_FOLD_WAVES>{});
     return hipGetLastError();
   }
-  auto go = [&](auto nw) {
+  auto go = [&](auto d, auto nw) {
+    constexpr int HD = decltype(d)::value;
     constexpr int NW = decltype(nw)::value;
     const dim3 grid(p.Hkv * p.n_tiles, p.pass_parts, p.pass_items), block(NW * kWave);
     if (p.shared_kv)
-      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kShared>), grid, block, 0,
+      hipLaunchKernelGGL((decode_mfma_kernel<HD, NW, DEPTH, TilePolicy::kShared>), grid, block, 0,
                          stream, p);
     else
-      hipLaunchKernelGGL((decode_mfma_kernel<NW, DEPTH, TilePolicy::kStream>), grid, block, 0,
+      hipLaunchKernelGGL((decode_mfma_kernel<HD, NW, DEPTH, TilePolicy::kStream>), grid, block, 0,
                          stream, p);
   };
-  // A whole context per workgroup: more waves, each with a longer share of
-  // its blocks. Split contexts (a partition's few blocks): fewer.
-  if (p.group_start)
-    go(std::integral_constant<int, PA_MFMA_GROUP_WAVES>{});
-  else if (p.pass_parts == 1)
-    go(std::integral_constant<int, PA_MFMA_WAVES_UNSPLIT>{});
+  auto by_waves = [&](auto d) {
+    // A whole context per workgroup: more waves, each with a longer share of
+    // its blocks. Split contexts (a partition's few blocks): fewer.
+    if (p.group_start)
+      go(d, std::integral_constant<int, PA_MFMA_GROUP_WAVES>{});
+    else if (p.pass_parts == 1)
+      go(d, std::integral_constant<int, PA_MFMA_WAVES_UNSPLIT>{});
+    else
+      go(d, std::integral_constant<int, PA_MFMA_WAVES>{});
+  };
+  if (p.D == 128)
+    by_waves(std::integral_constant<int, 128>{});
+  else if (p.D == 64 && !p.group_start && !p.tail_pass)
+    by_waves(std::integral_constant<int, 64>{});
   else
-    go(std::integral_constant<int, PA_MFMA_WAVES>{});
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

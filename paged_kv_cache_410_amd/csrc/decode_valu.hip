@@ -142,7 +142,10 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const int r = lane / LPT;
   const int c = lane % LPT;
 
-  const GridPos gp = grid_pos();
+  // Grouped query heads (fp32, or head_dim 64 past one matrix-core tile): the
+  // G workgroups of one kv head's heads run on one XCD, so the K/V tiles they
+  // all read are fetched from HBM into that XCD's L2 once.
+  const GridPos gp = P.G > 1 ? grid_pos_grouped(P.G) : grid_pos();
   const int h = gp.x % P.Hq;
   const int i = gp.x / P.Hq;  // query row of the sequence (0 for decode)
   const int p = gp.y;

@@ -275,6 +275,7 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = Hq / Hkv;
+  p.D = D;
   p.NB = NB;
   p.MB = MB;
   const int64_t cap = (int64_t)MB * kBs;
@@ -303,8 +304,11 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
 
   // The matrix-core kernel serves a kv head's columns (query rows x group
   // heads) 16 at a time; a single column per kv head (one query head, one
-  // row) goes to the vector kernel.
-  const bool mfma = dt == PA_BF16 && D == 128 && (p.G >= 2 || max_q >= 2);
+  // row) goes to the vector kernel. Past 16 columns per kv head the chunk
+  // kernel takes over (head_dim 128; with head_dim 64 such calls stay on the
+  // vector kernel, one column per workgroup).
+  const bool mfma = dt == PA_BF16 && (p.G >= 2 || max_q >= 2) &&
+                    (D == 128 || (D == 64 && p.n_tiles == 1));
   if (mfma && (int64_t)Hkv * p.n_tiles > INT32_MAX) return PA_EUNSUPPORTED;
   p.part_f32 = dt == PA_F32 || (mfma && p.n_tiles > 1);  // fp32 I/O, or the chunk kernel
   hipError_t err = mfma ? pa::launch_decode_mfma(p, stream) : pa::launch_decode_valu(p, dt, D, stream);
@@ -415,6 +419,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.G = G;
+  p.D = D;
   p.NB = NB;
   p.MB = MB;
   const int64_t cap = (int64_t)MB * kBs;

@@ -36,6 +36,7 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t x, uint32_t y) {
 __device__ __forceinline__ uint32_t word(const uint4& u, int k) {
   return k == 0 ? u.x : k == 1 ? u.y : k == 2 ? u.z : u.w;
 }
+__device__ __forceinline__ uint32_t word(const uint2& u, int k) { return k == 0 ? u.x : u.y; }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -237,6 +238,28 @@ __device__ __forceinline__ uint4 ld16(rsrc_t r, int off) {
   constexpr int kAux = kPolicy == TilePolicy::kStream ? 2 : 0;  // nt bit
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux));
 }
+// A piece of a K/V row per lane: 16 bytes (head_dim 128: a 16-lane group
+// covers a 256-byte row) or 8 bytes (head_dim 64, 128-byte rows).
+template <int kBytes>
+struct TilePiece;
+template <>
+struct TilePiece<16> {
+  using type = uint4;
+};
+template <>
+struct TilePiece<8> {
+  using type = uint2;
+};
+template <TilePolicy kPolicy, int kBytes>
+__device__ __forceinline__ typename TilePiece<kBytes>::type ld_piece(rsrc_t r, int off) {
+  if constexpr (kBytes == 16) {
+    return ld16<kPolicy>(r, off);
+  } else {
+    constexpr int kAux = kPolicy == TilePolicy::kStream ? 2 : 0;  // nt bit
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAux));
+  }
+}
+
 // The same load written by the hardware straight into LDS
 // (buffer_load_dwordx4 ... lds): lane i's 16 bytes land at lds + 16 i, with
 // `lds` wave-uniform; lanes outside the resource's range write zeros. Its

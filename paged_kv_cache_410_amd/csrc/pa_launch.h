@@ -22,6 +22,7 @@ struct DecodeParams {
   void* ws_o;                   // split only: [rows][n_parts][Hq][D]: fp32 rows (unnormalised)
                                 // when part_f32, else scaled fp16 rows (PartScale)
   int32_t B, Hq, Hkv, G, NB, MB;
+  int32_t D;                    // head_dim
   int32_t ctx_limit;            // min(max_ctx, MB * 16): larger contexts are rejected
   int32_t partition;            // tokens per partition; 0 = one partition per sequence
   int32_t n_parts;              // grid extent over partitions

@@ -92,6 +92,10 @@ CONFIGS = {
     "cow_gqa8": Spec("cow_gqa8", "bf16", 128, 64, 8, 128, seed=9, lengths=("cow",),
                      cow=dict(prompts=16, samples=8, prompt_len=1024, r_max=15, tail_lo=1,
                               tail_hi=256)),
+    # the GQA batch at head_dim 64 (a study workload for the matrix-core
+    # decode kernel's 64-dim tiles)
+    "gqa_d64": Spec("gqa_d64", "bf16", 16, 64, 8, 64, seed=8, lengths=("uniform", 8192, 32768),
+                    partition=512),
     "prefix": Spec("prefix", "bf16", 128, 32, 32, 128, seed=7, lengths=("prefix",),
                    prefix=dict(shared=1024, tail_lo=16, tail_hi=512, vocab=32000)),
     "13b_verify4": Spec("13b_verify4", "bf16", 128, 40, 40, 128, seed=5,

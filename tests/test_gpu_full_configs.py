@@ -59,7 +59,8 @@ def run_step(pa, name):
     return st, out
 
 
-@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "cow", "prefix", "13b_verify4"])
+@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "gqa_d64", "cow", "prefix",
+                                  "13b_verify4"])
 def test_full_config_whole_output(pa, name):
     st, out = run_step(pa, name)
     say(f"    oracle over the whole output {tuple(out.shape)}")

@@ -43,6 +43,9 @@ CHUNKS = {
                    chunk=("uniform", 1, 12)),
     "mq_bf16_d64": Spec("mq_bf16_d64", "bf16", 3, 4, 2, 64, seed=37, lengths=("uniform", 1, 300),
                         chunk=("uniform", 1, 9)),
+    # head_dim 64 on the matrix cores: at most 16 (row, head) columns per kv head
+    "mq_bf16_d64_mfma": Spec("mq_bf16_d64_mfma", "bf16", 3, 8, 2, 64, seed=40,
+                             lengths=("uniform", 1, 700), chunk=("uniform", 1, 4)),
     # unsplit rows longer than one 64-block id chunk per wave
     "mq_long": Spec("mq_long", "bf16", 2, 2, 2, 128, seed=38, lengths=("fixed", [9000, 3000]),
                     chunk=("uniform", 2, 6)),

@@ -38,6 +38,8 @@ CASES = {
     "valu_d128": Spec("valu_d128", "bf16", 4, 4, 4, 128, seed=31, lengths=("uniform", 200, 1500)),
     "valu_d64": Spec("valu_d64", "bf16", 3, 3, 3, 64, seed=32, lengths=("uniform", 200, 1200)),
     "mfma_gqa8": Spec("mfma_gqa8", "bf16", 3, 16, 2, 128, seed=33, lengths=("uniform", 300, 3000)),
+    "mfma_gqa8_d64": Spec("mfma_gqa8_d64", "bf16", 3, 16, 2, 64, seed=37,
+                          lengths=("uniform", 300, 3000)),
     # 8 rows x 8 heads: 4 column tiles, one per wave
     "chunk_tpw1": Spec("chunk_tpw1", "bf16", 2, 16, 2, 128, seed=34,
                        lengths=("uniform", 300, 1200), chunk=("uniform", 8, 8)),
