@@ -50,6 +50,10 @@
 #ifndef PA_CHUNK_MAX_WAVES
 #define PA_CHUNK_MAX_WAVES 8
 #endif
+// Wave priority raised while a wave issues its S^T products (1), or never (0).
+#ifndef PA_CHUNK_PRIO
+#define PA_CHUNK_PRIO 0
+#endif
 // Column tiles (16 columns each) per wave for more than 8 tiles per kv
 // head: 2 (on 4 waves) or 1 (on 8 waves).
 #ifndef PA_CHUNK_TILES_PER_WAVE
@@ -333,6 +337,7 @@ void chunk_mfma_kernel(DecodeParams P) {
       sa[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       sb[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    if constexpr (PA_CHUNK_PRIO != 0) __builtin_amdgcn_s_setprio(PA_CHUNK_PRIO);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int o = col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16;
@@ -345,6 +350,7 @@ void chunk_mfma_kernel(DecodeParams P) {
         sb[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qop[t][kk], sb[t], 0, 0, 0);
       }
     }
+    if constexpr (PA_CHUNK_PRIO != 0) __builtin_amdgcn_s_setprio(0);
     if constexpr (TPW == 1) {
       // V operands read now, so that their latency passes under the softmax.
       bf16x8_t vop[8];
