@@ -432,7 +432,7 @@ void decode_mfma_kernel(DecodeParams P) {
       u.w = pack_f16x2(ov[6] * ps.mul, ov[7] * ps.mul);
       if (any_bad) u = make_uint4(0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u);  // NaN
       const size_t part = part_slot(P, row, h, P.part_base + p);
-      st16(static_cast<char*>(P.ws_o) + (part * D + 8 * ch) * 2, u);
+      store_part16(P, row, h, P.part_base + p, 2, 8 * ch * 2, u);
       if (ch == 0) {
         P.ws_ml[2 * part] = any_bad ? 0.0f : ps.m;
         P.ws_ml[2 * part + 1] = any_bad ? __builtin_nanf("") : ps.l;

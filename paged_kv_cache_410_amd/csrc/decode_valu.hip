@@ -349,17 +349,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   for (int e = 0; e < EPL; ++e) res[e] = bad ? __builtin_nanf("") : outv[e] * mul;
   if (to_partial) {
     const size_t part = part_slot(P, row, h, P.part_base + p);
-    char* dst = static_cast<char*>(P.ws_o) + part * D * sizeof(T) + c * 16;
     if (c == 0) {
       P.ws_ml[2 * part] = bad ? 0.0f : M;
       P.ws_ml[2 * part + 1] = bad ? __builtin_nanf("") : L;
     }
     if constexpr (sizeof(T) == 2) {
-      st16(dst, make_uint4(pack_f16x2(res[0], res[1]), pack_f16x2(res[2], res[3]),
-                           pack_f16x2(res[4], res[5]), pack_f16x2(res[6], res[7])));
+      store_part16(P, row, h, P.part_base + p, 2, c * 16,
+                   make_uint4(pack_f16x2(res[0], res[1]), pack_f16x2(res[2], res[3]),
+                              pack_f16x2(res[4], res[5]), pack_f16x2(res[6], res[7])));
     } else {
-      st16(dst, make_uint4(__float_as_uint(res[0]), __float_as_uint(res[1]),
-                           __float_as_uint(res[2]), __float_as_uint(res[3])));
+      store_part16(P, row, h, P.part_base + p, 4, c * 16,
+                   make_uint4(__float_as_uint(res[0]), __float_as_uint(res[1]),
+                              __float_as_uint(res[2]), __float_as_uint(res[3])));
     }
     return;
   }

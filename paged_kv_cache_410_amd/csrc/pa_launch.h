@@ -66,6 +66,40 @@ __device__ __forceinline__ size_t part_slot(const DecodeParams& P, size_t row, i
   return (row * P.n_parts + j) * P.Hq + h;
 }
 
+// Cache policy of the partial-row stores (buffer-instruction aux bits) for
+// rows of 256 bytes (head_dim 128 in fp16, 64 in fp32): 16 = sc1, device
+// scope. On the GQA workload (about 9 MB of fp16 rows per call, stored while
+// the kernel streams 1.16 GB) the default policy costs 16 us against a timing
+// probe that stores no rows (202.3 vs 186.9 us); with sc1 the call takes
+// 198.1-199.5 us (nt: 199.0-199.8, sc0: 201.9). Rows of 128 bytes (head_dim
+// 64 in fp16) keep the default: on the same batch at head_dim 64 sc1 gave
+// 121.5 us and nt 121.8 against 118.3.
+#ifndef PA_PART_STORE_AUX
+#define PA_PART_STORE_AUX 16
+#endif
+typedef unsigned int u32x4_part_t __attribute__((ext_vector_type(4)));
+
+// Store 16 bytes at byte `off` of the partial row of (row, head h, partition
+// slot j); rows are D elements of `eb` bytes. The buffer resource spans the
+// Hq rows of (row, j), which are contiguous (part_slot), so offsets stay
+// small whatever the workspace's size.
+__device__ __forceinline__ void store_part16(const DecodeParams& P, size_t row, int h, int j,
+                                             int eb, int off, const uint4& v) {
+  const int64_t row_bytes = (int64_t)P.D * eb;
+  char* base = static_cast<char*>(P.ws_o) + part_slot(P, row, 0, j) * row_bytes;
+  if ((int64_t)P.Hq * row_bytes <= INT32_MAX) {
+    const rsrc_t r = make_rsrc(base, (int)(P.Hq * row_bytes));
+    const u32x4_part_t d = __builtin_bit_cast(u32x4_part_t, v);
+    const int o = (int)(h * row_bytes) + off;
+    if (row_bytes >= 256)
+      __builtin_amdgcn_raw_buffer_store_b128(d, r, o, 0, PA_PART_STORE_AUX);
+    else
+      __builtin_amdgcn_raw_buffer_store_b128(d, r, o, 0, 0);
+  } else {
+    st16(base + h * row_bytes + off, v);
+  }
+}
+
 // Element type of the partial rows for I/O dtype T (float, or bf16 bits).
 template <typename T>
 struct PartElem {
