@@ -50,6 +50,11 @@
 #ifndef PA_VALU_DEPTH
 #define PA_VALU_DEPTH 3
 #endif
+// Grouped query heads: the workgroups of one kv head's G heads on one XCD (1),
+// or the plain round-robin order (0, for measurement).
+#ifndef PA_VALU_GROUP_XCD
+#define PA_VALU_GROUP_XCD 1
+#endif
 // Ring depth of the tail pass: its runs of blocks are short (copy-on-write
 // batch: 57.9 us at depth 2 against 60.5 at 3).
 #ifndef PA_VALU_TAIL_DEPTH
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   // Grouped query heads (fp32, or head_dim 64 past one matrix-core tile): the
   // G workgroups of one kv head's heads run on one XCD, so the K/V tiles they
   // all read are fetched from HBM into that XCD's L2 once.
-  const GridPos gp = P.G > 1 ? grid_pos_grouped(P.G) : grid_pos();
+  const GridPos gp = P.G > 1 && PA_VALU_GROUP_XCD ? grid_pos_grouped(P.G) : grid_pos();
   const int h = gp.x % P.Hq;
   const int i = gp.x / P.Hq;  // query row of the sequence (0 for decode)
   const int p = gp.y;

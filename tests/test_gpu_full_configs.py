@@ -59,7 +59,7 @@ def run_step(pa, name):
     return st, out
 
 
-@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "gqa_d64", "cow", "prefix",
+@pytest.mark.parametrize("name", ["7b", "13b", "gqa", "gqa_d64", "gqa_f32", "cow", "prefix",
                                   "13b_verify4"])
 def test_full_config_whole_output(pa, name):
     st, out = run_step(pa, name)
