@@ -8,9 +8,10 @@ input, all of it already resident in HBM:
   cache write of the step's new K/V (one fused launch) -> decode attention
   over every sequence (or causal attention of each sequence's new tokens).
 W untimed steps, then exactly K timed steps between two device
-synchronisations. HIP events on the launch stream bracket each decode call
-inside the timed region, so the decode kernel's average duration (and from it
-its achieved HBM bandwidth against the 8 TB/s peak) is measured live.
+synchronisations. HIP events on the launch stream bracket the decode call of
+every n-th timed step (20 calls by default), inside the timed region, so the
+decode kernel's average duration (and from it its achieved HBM bandwidth
+against the 8 TB/s peak) is measured live.
 
 Printed: one JSON line. `value` is the step's algorithmic HBM bytes over the
 step time (GB/s); `decode_tokens_per_s` is the step's new tokens / step time
@@ -204,10 +205,10 @@ def main():
     ap.add_argument("--shared-partition", type=int, default=None,
                     help="partition length of the shared part in pa_decode_shared (0 = none; "
                          "default: the library's choice)")
-    ap.add_argument("--event-every", type=int, default=1,
+    ap.add_argument("--event-every", type=int, default=None,
                     help="time the attention call with HIP events on every n-th timed step "
-                         "(a pair of events between two kernels lengthens that step by a few "
-                         "microseconds; 1 = every step)")
+                         "(a pair of events between two kernels lengthens that step by about "
+                         "6 microseconds; default: steps // 20, so that 20 calls are timed)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured once as a HIP graph and replayed; the "
                          "replayed step then sets value and ms_per_step")
@@ -334,7 +335,7 @@ def main():
     log(f"[bench] timing {args.steps} steps after {args.warmup} warm-up steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    every = max(1, args.event_every)
+    every = max(1, args.steps // 20 if args.event_every is None else args.event_every)
     for i in range(args.steps):
         step(evs[i] if i % every == 0 else None)
     torch.cuda.synchronize()
