@@ -44,6 +44,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # version of these no longer describe the kernel that runs.
 DECODE_SOURCES = ["paged_kv_cache_410_amd/csrc/decode_valu.hip",
                   "paged_kv_cache_410_amd/csrc/decode_mfma.hip",
+                  "paged_kv_cache_410_amd/csrc/decode_mfma_f32.hip",
                   "paged_kv_cache_410_amd/csrc/chunk_mfma.hip",
                   "paged_kv_cache_410_amd/csrc/chunk_ring.h",
                   "paged_kv_cache_410_amd/csrc/decode_reduce.hip",

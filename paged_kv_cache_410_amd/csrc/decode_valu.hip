@@ -147,7 +147,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const int r = lane / LPT;
   const int c = lane % LPT;
 
-  // Grouped query heads (fp32, or head_dim 64 past one matrix-core tile): the
+  // Grouped query heads (bf16 head_dim 64 past one matrix-core tile): the
   // G workgroups of one kv head's heads run on one XCD, so the K/V tiles they
   // all read are fetched from HBM into that XCD's L2 once.
   const GridPos gp = P.G > 1 && PA_VALU_GROUP_XCD ? grid_pos_grouped(P.G) : grid_pos();

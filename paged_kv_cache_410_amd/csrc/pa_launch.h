@@ -259,6 +259,7 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int D, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_mfma_f32(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream);
 
 // Precondition checks: count[0] = number of violating entries (two launches).

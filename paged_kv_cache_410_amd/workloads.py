@@ -96,9 +96,8 @@ CONFIGS = {
     # decode kernel's 64-dim tiles)
     "gqa_d64": Spec("gqa_d64", "bf16", 16, 64, 8, 64, seed=8, lengths=("uniform", 8192, 32768),
                     partition=512),
-    # the GQA recipe in fp32 with shorter contexts (a study workload for the
-    # vector kernel's grouped heads, whose K/V the G heads' workgroups share
-    # through one XCD's L2)
+    # the GQA recipe in fp32 with shorter contexts (a study workload for fp32
+    # grouped heads on the fp32 matrix-core kernel)
     "gqa_f32": Spec("gqa_f32", "f32", 16, 64, 8, 128, seed=10, lengths=("uniform", 2048, 8192),
                     partition=512),
     "prefix": Spec("prefix", "bf16", 128, 32, 32, 128, seed=7, lengths=("prefix",),

@@ -38,9 +38,14 @@ CHUNKS = {
                        chunk=("all",)),
     "mq_single": Spec("mq_single", "bf16", 5, 8, 2, 128, seed=35, lengths=("uniform", 1, 400),
                       chunk=("uniform", 1, 1)),
-    # vector path: fp32, and head_dim 64
+    # fp32 (the fp32 matrix-core kernel, one query head per kv head), and
+    # bf16 head_dim 64 past one tile (the vector kernel)
     "mq_f32": Spec("mq_f32", "f32", 3, 4, 4, 64, seed=36, lengths=("uniform", 1, 300),
                    chunk=("uniform", 1, 12)),
+    # fp32 on the matrix cores: up to 48 (row, head) columns per kv head, so
+    # one to three 16-column tiles
+    "mq_f32_gqa": Spec("mq_f32_gqa", "f32", 3, 8, 2, 128, seed=46, lengths=("uniform", 1, 600),
+                       chunk=("uniform", 1, 12)),
     "mq_bf16_d64": Spec("mq_bf16_d64", "bf16", 3, 4, 2, 64, seed=37, lengths=("uniform", 1, 300),
                         chunk=("uniform", 1, 9)),
     # head_dim 64 on the matrix cores: at most 16 (row, head) columns per kv head
@@ -115,11 +120,13 @@ def test_chunk_append_kv_bit_exact(pa, name):
     assert np.array_equal(host_bits(st.v_cache), st.v_after)
 
 
-@pytest.mark.parametrize("name", ["mq_gqa8", "mq_gqa8_short", "mq_single", "mq_f32"])
+@pytest.mark.parametrize("name", ["mq_gqa8", "mq_gqa8_short", "mq_single", "mq_f32",
+                                  "mq_f32_gqa", "mq_bf16_d64"])
 @pytest.mark.parametrize("scale_mul", [-1.0, 0.0])
 def test_negative_and_zero_scale(pa, name, scale_mul):
     # A negative logit scale and a zero one through every attention kernel
-    # (chunk, matrix-core decode, vector), against the oracle at that scale.
+    # (chunk, matrix-core decode in bf16 and fp32, vector), against the oracle
+    # at that scale.
     say(f"[scale x{scale_mul}] {name}")
     st = Step(CHUNKS[name], oracle_full=False)
     st.run_cache_ops(pa)
@@ -170,7 +177,8 @@ def test_two_tiles_per_wave_keep_their_own_max(pa, big_tile, partition):
     assert err <= TOL[spec.dtype]
 
 
-@pytest.mark.parametrize("name", ["mq_gqa8", "mq_gqa8_short", "mq_mha", "mq_single", "mq_long"])
+@pytest.mark.parametrize("name", ["mq_gqa8", "mq_gqa8_short", "mq_mha", "mq_single", "mq_long",
+                                  "mq_f32_gqa"])
 @pytest.mark.parametrize("partition", [0, 64])
 def test_bad_block_ids_poison_only_their_rows(pa, name, partition):
     # A block id outside the pool, or negative, in a block every row of its
@@ -178,7 +186,8 @@ def test_bad_block_ids_poison_only_their_rows(pa, name, partition):
     # out of bounds, and every other row keeps its bits. The kernels cover
     # two tiles per wave (mq_gqa8), one tile per wave on 2 or 4 waves
     # (mq_gqa8_short, mq_mha), the matrix-core decode kernel (mq_single), and
-    # an id in the second 64-block chunk of a long unsplit row (mq_long).
+    # an id in the second 64-block chunk of a long unsplit row (mq_long), and
+    # the fp32 matrix-core kernel over several tiles (mq_f32_gqa).
     say(f"[multi-query bad block ids] {name} partition={partition}")
     st = Step(CHUNKS[name], oracle_full=False)
     st.run_cache_ops(pa)

@@ -57,6 +57,15 @@ SMALL = {
     "cow_gqa": Spec("cow_gqa", "bf16", 6, 8, 2, 128, seed=22, lengths=("cow",),
                     cow=dict(prompts=2, samples=3, prompt_len=64, r_max=15, tail_lo=1,
                              tail_hi=30)),
+    # fp32 grouped heads on the matrix cores (v_mfma_f32_16x16x4_f32): 8 heads
+    # per kv head; a full 16-column tile at head_dim 64; two tiles per kv head
+    # (32 heads); unsplit rows longer than one 64-block id chunk per wave
+    "gqa8_f32": Spec("gqa8_f32", "f32", 6, 16, 2, 128, seed=42, lengths=("uniform", 1, 1500)),
+    "gqa16_f32_d64": Spec("gqa16_f32_d64", "f32", 2, 16, 1, 64, seed=43,
+                          lengths=("uniform", 1, 700)),
+    "gqa32_f32": Spec("gqa32_f32", "f32", 2, 32, 1, 128, seed=44, lengths=("uniform", 1, 500)),
+    "long_gqa_f32": Spec("long_gqa_f32", "f32", 2, 8, 2, 128, seed=45,
+                         lengths=("fixed", [2100, 9000])),
 }
 
 
@@ -143,7 +152,8 @@ def test_decode_matches_oracle(pa, name, partition):
     assert err <= TOL[spec.dtype]
 
 
-@pytest.mark.parametrize("name", ["mha_bf16", "gqa8", "tiny", "cow_small", "prefix_small"])
+@pytest.mark.parametrize("name", ["mha_bf16", "gqa8", "tiny", "cow_small", "prefix_small",
+                                  "gqa8_f32"])
 def test_cache_policy_gives_identical_bits(pa, name):
     """Streaming and cached tile loads (PA_KV_SHARED) move the same bits."""
     say(f"[cache policy] {name}")
@@ -158,8 +168,9 @@ def test_cache_policy_gives_identical_bits(pa, name):
 def test_decode_deterministic_and_permutation_invariant(pa):
     """Same inputs twice -> same bits; physical blocks moved elsewhere (tables
     remapped) -> same bits: the arithmetic order never depends on block ids."""
-    say("[decode invariance] gqa8 / mha_bf16")
-    for name, part in (("mha_bf16", 64), ("gqa8", 512), ("gqa8", 0)):
+    say("[decode invariance] gqa8 / mha_bf16 / gqa8_f32")
+    for name, part in (("mha_bf16", 64), ("gqa8", 512), ("gqa8", 0), ("gqa8_f32", 64),
+                       ("gqa8_f32", 0)):
         st = Step(SMALL[name], oracle_full=False)
         st.run_cache_ops(pa)
         a = st.decode(pa, partition=part).clone()
@@ -206,12 +217,13 @@ def test_decode_shared_blocks_equal_private_copies(pa, name):
     assert torch.equal(shared.view(torch.int16), private.view(torch.int16))
 
 
-def test_decode_bad_entries_give_nan_rows_only(pa):
+@pytest.mark.parametrize("name", ["mha_bf16", "gqa8_f32"])
+def test_decode_bad_entries_give_nan_rows_only(pa, name):
     """A context beyond max_ctx or a block id outside the pool poisons only its
     own sequence's rows (NaN), reads nothing out of bounds, and leaves the other
     rows as they were."""
-    say("[decode bad entries] mha_bf16")
-    st = Step(SMALL["mha_bf16"])
+    say(f"[decode bad entries] {name}")
+    st = Step(SMALL[name])
     st.run_cache_ops(pa)
     good = {part: st.decode(pa, partition=part).float().cpu() for part in (0, 64)}
     bt = st.block_tables.clone()
