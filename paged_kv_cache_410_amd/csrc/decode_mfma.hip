@@ -10,9 +10,10 @@
 // read once per 16 columns instead of once per column.
 //
 // Columns: the n x G (query row, head of the group) pairs of a sequence and
-// kv head, row-major, in one tile of 16 (more columns go to the chunk kernel,
-// chunk_mfma.hip, with the same layouts); one workgroup per (kv head,
-// partition, sequence). Column (i, q) attends over its row's causal prefix
+// kv head, row-major, in tiles of 16; one workgroup per (kv head, tile,
+// partition, sequence). At head_dim 128 a kv head with more than one tile
+// goes to the chunk kernel (chunk_mfma.hip, same layouts), whose waves share
+// each block. Column (i, q) attends over its row's causal prefix
 // (ctx - n + i + 1 tokens): a per-column limit masks the logits. The decode
 // step is n = 1: the columns are the G heads.
 //
@@ -76,9 +77,9 @@
 namespace pa {
 
 // The waves of a workgroup interleave the blocks of one column tile (wave w
-// takes blocks w, w + NW, ...) and merge their states through LDS. A kv head
-// with more than one tile (several query rows per sequence) goes to the
-// chunk kernel instead, whose waves share each block.
+// takes blocks w, w + NW, ...) and merge their states through LDS. At head_dim
+// 128 a kv head with more than one tile (several query rows per sequence)
+// goes to the chunk kernel instead, whose waves share each block.
 //
 // kFold (the shared-prefix group pass, one partition, one tile): after the
 // group's shared blocks (every column), each member's own blocks, read
@@ -108,7 +109,9 @@ void decode_mfma_kernel(DecodeParams P) {
   const int col = lane & 15;
   const int rg = lane >> 4;
 
-  const GridPos gp = grid_pos();
+  // Several tiles per kv head (head_dim 64 past 16 columns; the chunk kernel
+  // takes them at 128): they read the same K/V and are kept on one XCD.
+  const GridPos gp = P.n_tiles > 1 ? grid_pos_grouped(P.n_tiles) : grid_pos();
   const int p = gp.y;
   const int g = gp.x / P.n_tiles;    // kv head
   const int tile = gp.x % P.n_tiles;  // 16-column tile of this kv head's (row, head) pairs
@@ -456,8 +459,9 @@ void decode_mfma_kernel(DecodeParams P) {
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  // several column tiles per kv head: the chunk kernel, whose waves share each block
-  if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
+  // several column tiles per kv head at head_dim 128: the chunk kernel, whose
+  // waves share each block (at 64, one workgroup per tile, below)
+  if (p.n_tiles > 1 && p.D == 128) return launch_chunk_mfma(p, stream);
   constexpr int DEPTH = PA_MFMA_DEPTH;
   if (p.fold_tails) {
     // group pass with the members' own blocks folded in (head_dim 128): the

@@ -14,7 +14,10 @@
 //            one physical block (all heads, contiguous in the pool) are read
 //            close in time. A decode step has one query row per sequence;
 //            with several new tokens per sequence (query_start) each row is
-//            its own workgroup and attends over its causal prefix.
+//            its own workgroup and attends over its causal prefix. (The
+//            library sends every kv head with more than one such column,
+//            grouped heads or several rows, to the matrix-core kernels: here
+//            it serves one query head per kv head and one row per sequence.)
 //   block  = NW waves; wave w takes blocks p0 + w, p0 + w + NW, ...
 //   A (block, kv head) tile is 16 rows of D elements, contiguous in memory.
 //   One 16-byte load per lane: LPT = D*e/16 lanes cover one token row, so a
@@ -49,11 +52,6 @@
 #endif
 #ifndef PA_VALU_DEPTH
 #define PA_VALU_DEPTH 3
-#endif
-// Grouped query heads: the workgroups of one kv head's G heads on one XCD (1),
-// or the plain round-robin order (0, for measurement).
-#ifndef PA_VALU_GROUP_XCD
-#define PA_VALU_GROUP_XCD 1
 #endif
 // Ring depth of the tail pass: its runs of blocks are short (copy-on-write
 // batch: 57.9 us at depth 2 against 60.5 at 3).
@@ -147,10 +145,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_valu_kernel(DecodeParams P)
   const int r = lane / LPT;
   const int c = lane % LPT;
 
-  // Grouped query heads (bf16 head_dim 64 past one matrix-core tile): the
-  // G workgroups of one kv head's heads run on one XCD, so the K/V tiles they
-  // all read are fetched from HBM into that XCD's L2 once.
-  const GridPos gp = P.G > 1 && PA_VALU_GROUP_XCD ? grid_pos_grouped(P.G) : grid_pos();
+  const GridPos gp = grid_pos();
   const int h = gp.x % P.Hq;
   const int i = gp.x / P.Hq;  // query row of the sequence (0 for decode)
   const int p = gp.y;

@@ -39,7 +39,8 @@ CHUNKS = {
     "mq_single": Spec("mq_single", "bf16", 5, 8, 2, 128, seed=35, lengths=("uniform", 1, 400),
                       chunk=("uniform", 1, 1)),
     # fp32 (the fp32 matrix-core kernel, one query head per kv head), and
-    # bf16 head_dim 64 past one tile (the vector kernel)
+    # bf16 head_dim 64 past one tile (the matrix-core decode kernel, one
+    # workgroup per tile)
     "mq_f32": Spec("mq_f32", "f32", 3, 4, 4, 64, seed=36, lengths=("uniform", 1, 300),
                    chunk=("uniform", 1, 12)),
     # fp32 on the matrix cores: up to 48 (row, head) columns per kv head, so
@@ -48,6 +49,10 @@ CHUNKS = {
                        chunk=("uniform", 1, 12)),
     "mq_bf16_d64": Spec("mq_bf16_d64", "bf16", 3, 4, 2, 64, seed=37, lengths=("uniform", 1, 300),
                         chunk=("uniform", 1, 9)),
+    # head_dim 64 past one tile: 160 to 320 columns per kv head, 10 to 20
+    # workgroups per kv head on the matrix-core decode kernel
+    "mq_gqa8_d64": Spec("mq_gqa8_d64", "bf16", 2, 16, 2, 64, seed=48, lengths=("uniform", 100, 900),
+                        chunk=("uniform", 20, 40)),
     # head_dim 64 on the matrix cores: at most 16 (row, head) columns per kv head
     "mq_bf16_d64_mfma": Spec("mq_bf16_d64_mfma", "bf16", 3, 8, 2, 64, seed=40,
                              lengths=("uniform", 1, 700), chunk=("uniform", 1, 4)),
@@ -124,9 +129,9 @@ def test_chunk_append_kv_bit_exact(pa, name):
                                   "mq_f32_gqa", "mq_bf16_d64"])
 @pytest.mark.parametrize("scale_mul", [-1.0, 0.0])
 def test_negative_and_zero_scale(pa, name, scale_mul):
-    # A negative logit scale and a zero one through every attention kernel
-    # (chunk, matrix-core decode in bf16 and fp32, vector), against the oracle
-    # at that scale.
+    # A negative logit scale and a zero one through every multi-query kernel
+    # (chunk, matrix-core decode in bf16 at head_dim 128 and 64, fp32
+    # matrix-core), against the oracle at that scale.
     say(f"[scale x{scale_mul}] {name}")
     st = Step(CHUNKS[name], oracle_full=False)
     st.run_cache_ops(pa)
@@ -178,7 +183,7 @@ def test_two_tiles_per_wave_keep_their_own_max(pa, big_tile, partition):
 
 
 @pytest.mark.parametrize("name", ["mq_gqa8", "mq_gqa8_short", "mq_mha", "mq_single", "mq_long",
-                                  "mq_f32_gqa"])
+                                  "mq_f32_gqa", "mq_gqa8_d64"])
 @pytest.mark.parametrize("partition", [0, 64])
 def test_bad_block_ids_poison_only_their_rows(pa, name, partition):
     # A block id outside the pool, or negative, in a block every row of its
@@ -187,7 +192,8 @@ def test_bad_block_ids_poison_only_their_rows(pa, name, partition):
     # two tiles per wave (mq_gqa8), one tile per wave on 2 or 4 waves
     # (mq_gqa8_short, mq_mha), the matrix-core decode kernel (mq_single), and
     # an id in the second 64-block chunk of a long unsplit row (mq_long), and
-    # the fp32 matrix-core kernel over several tiles (mq_f32_gqa).
+    # the fp32 matrix-core kernel over several tiles (mq_f32_gqa), and the
+    # head_dim-64 matrix-core kernel over many tiles (mq_gqa8_d64).
     say(f"[multi-query bad block ids] {name} partition={partition}")
     st = Step(CHUNKS[name], oracle_full=False)
     st.run_cache_ops(pa)

@@ -8,8 +8,9 @@ range both ways (exact in bf16, and the attention output scales by the same
 power): 2^20 and 2^100 need k > 0 to stay finite, 2^-20 needs k < 0 to stay
 out of fp16's subnormals (fixed spacing 2^-24, a 6% error on rows of size
 2^-20). Every fp16 partial is covered: the vector kernel's (one query head
-per kv head; head_dim 128 and 64), the matrix-core kernel's (grouped heads)
-and the shared-prefix group pass's on that kernel. The chunk kernel (several
+per kv head; head_dim 128 and 64), the matrix-core kernel's (grouped heads;
+several tiles per kv head at head_dim 64) and the shared-prefix group pass's
+on that kernel. The chunk kernel (several
 query rows, one and two column tiles per wave; shared-prefix groups wider than
 one tile) writes fp32 partials, which the merges read as such. The output
 divided by the power must match the oracle's unscaled output to the bf16
@@ -40,6 +41,10 @@ CASES = {
     "mfma_gqa8": Spec("mfma_gqa8", "bf16", 3, 16, 2, 128, seed=33, lengths=("uniform", 300, 3000)),
     "mfma_gqa8_d64": Spec("mfma_gqa8_d64", "bf16", 3, 16, 2, 64, seed=37,
                           lengths=("uniform", 300, 3000)),
+    # head_dim 64, 3 to 5 rows x 8 heads: two or three tiles per kv head, one
+    # workgroup each on the matrix-core decode kernel (fp16 partials)
+    "mfma_d64_tiles": Spec("mfma_d64_tiles", "bf16", 2, 16, 2, 64, seed=47,
+                           lengths=("uniform", 300, 1200), chunk=("uniform", 3, 5)),
     # 8 rows x 8 heads: 4 column tiles, one per wave
     "chunk_tpw1": Spec("chunk_tpw1", "bf16", 2, 16, 2, 128, seed=34,
                        lengths=("uniform", 300, 1200), chunk=("uniform", 8, 8)),
