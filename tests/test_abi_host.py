@@ -398,6 +398,52 @@ def test_shared_groups_on_workload_tables(palib):
             assert len(gs) - 1 == n and np.all(np.diff(gs) == size) and np.all(sh == shared)
 
 
+def test_shared_plan_on_workload_tables(palib):
+    """The plan the bench takes for batches that share leading blocks: the
+    groups, the shared-part partition (the library's choice; a host with no
+    GPU counts 256 compute units) and the cache flags, set only where blocks
+    still repeat within a pass once the sharers are grouped."""
+    import paged_kv_cache_410_amd as pa
+    from paged_kv_cache_410_amd import workloads
+    plan = {}
+    for name in ("cow", "prefix", "13b", "cow_gqa8"):
+        spec = workloads.CONFIGS[name]
+        tb = workloads.make_tables(spec, oracle_bm.PrefixBlockManager)
+        plan[name] = pa.shared_plan(tb.block_tables, tb.context_lens, spec.Hq, spec.Hkv, 16)
+    assert plan["13b"] is None                   # nothing shared
+    c = plan["cow"]
+    # 16 prompts x 8 samples: 16 groups of 8 sharing 1008 tokens; 512 group
+    # workgroups fill the GPU unsplit; no block repeats within either pass
+    assert (len(c["group_start"]) - 1, c["max_shared"], c["partition"]) == (16, 1008, 0)
+    assert np.all(np.diff(c["group_start"]) == 8)
+    assert not c["groups_overlap"] and not c["shared_kv"]
+    p = plan["prefix"]
+    # one 1024-token prefix held by all 128 requests, split into 8 groups of
+    # 16: the groups' shared parts overlap, the private tails do not
+    assert (len(p["group_start"]) - 1, p["max_shared"], p["partition"]) == (8, 1024, 0)
+    assert p["groups_overlap"] and not p["shared_kv"]
+    g = plan["cow_gqa8"]
+    # 8 query heads per kv head: 16 groups x 8 kv heads = 128 group workgroups,
+    # fewer than the compute units: the shared part is split in two
+    assert len(g["group_start"]) - 1 == 16 and g["max_shared"] == 1008
+    assert g["partition"] > 0 and g["partition"] % 16 == 0 and g["partition"] < g["max_shared"]
+    assert not g["groups_overlap"] and not g["shared_kv"]
+
+
+def test_shared_plan_flags_repeated_own_blocks(palib):
+    import paged_kv_cache_410_amd as pa
+    # two sequences share blocks 5, 6 (32 tokens inside both contexts); block 7
+    # is past the shared part but read by both: own blocks repeat
+    bt = np.array([[5, 6, 7], [5, 6, 7]], np.int32)
+    plan = pa.shared_plan(bt, np.array([48, 40], np.int32), 8, 8, 16)
+    assert plan["group_start"].tolist() == [0, 2] and plan["seq_shared"].tolist() == [32, 32]
+    assert plan["shared_kv"] and not plan["groups_overlap"]
+    # the same with a private last block each
+    bt2 = np.array([[5, 6, 7], [5, 6, 8]], np.int32)
+    plan2 = pa.shared_plan(bt2, np.array([48, 40], np.int32), 8, 8, 16)
+    assert not plan2["shared_kv"] and not plan2["groups_overlap"]
+
+
 @settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
 @given(seed=st.integers(0, 2**31 - 1), max_group=st.integers(1, 6))
 def test_shared_groups_invariants_on_forked_tables(palib, seed, max_group):
