@@ -71,9 +71,11 @@ __device__ __forceinline__ size_t part_slot(const DecodeParams& P, size_t row, i
 // scope. On the GQA workload (about 9 MB of fp16 rows per call, stored while
 // the kernel streams 1.16 GB) the default policy costs 16 us against a timing
 // probe that stores no rows (202.3 vs 186.9 us); with sc1 the call takes
-// 198.1-199.5 us (nt: 199.0-199.8, sc0: 201.9). Rows of 128 bytes (head_dim
-// 64 in fp16) keep the default: on the same batch at head_dim 64 sc1 gave
-// 121.5 us and nt 121.8 against 118.3.
+// 198.1-199.5 us (nt: 199.0-199.8, sc0: 201.9). Rows of other sizes keep the
+// default: 128 bytes (head_dim 64 in fp16; on the same batch at head_dim 64
+// sc1 gave 121.5 us and nt 121.8 against 118.3) and 512 bytes (head_dim 128
+// in fp32; on the fp32 GQA batch sc1 gave 131.3 us, nt 132.5, sc1 + nt 140.2,
+// against 128.2).
 #ifndef PA_PART_STORE_AUX
 #define PA_PART_STORE_AUX 16
 #endif
@@ -91,7 +93,7 @@ __device__ __forceinline__ void store_part16(const DecodeParams& P, size_t row, 
     const rsrc_t r = make_rsrc(base, (int)(P.Hq * row_bytes));
     const u32x4_part_t d = __builtin_bit_cast(u32x4_part_t, v);
     const int o = (int)(h * row_bytes) + off;
-    if (row_bytes >= 256)
+    if (row_bytes == 256)
       __builtin_amdgcn_raw_buffer_store_b128(d, r, o, 0, PA_PART_STORE_AUX);
     else
       __builtin_amdgcn_raw_buffer_store_b128(d, r, o, 0, 0);
