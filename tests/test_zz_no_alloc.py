@@ -57,6 +57,8 @@ def test_noalloc_matches_decode_on_calls_in_a_row(pa):
     assert 0 < small < big
     f32 = check_call(pa, "tiny", 16)          # fp32 partials
     assert 0 < f32 < big
+    f32g = check_call(pa, "gqa8_f32", 64)     # fp32 matrix-core kernel, fp32 partials
+    assert f32g > 0
 
 
 def test_noalloc_without_split_and_oversized_split(pa):
