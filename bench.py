@@ -203,6 +203,8 @@ def main():
     ap.add_argument("--no-group", action="store_true",
                     help="attend over blocks shared by several sequences once per sequence "
                          "(pa_decode) instead of once per group of sharers (pa_decode_shared)")
+    ap.add_argument("--max-group", type=int, default=16,
+                    help="most sequences per group of sharers (pa_decode_shared)")
     ap.add_argument("--shared-partition", type=int, default=None,
                     help="partition length of the shared part in pa_decode_shared (0 = none; "
                          "default: the library's choice)")
@@ -281,7 +283,8 @@ def main():
         # groups of up to 16 sequences (past 16 columns per kv head the group
         # pass runs on the chunk kernel); once grouped, a pass reads through
         # the caches only where blocks still repeat within it
-        plan = pa.shared_plan(tb.block_tables, tb.context_lens, spec.Hq, spec.Hkv, 16)
+        plan = pa.shared_plan(tb.block_tables, tb.context_lens, spec.Hq, spec.Hkv,
+                              args.max_group)
         if plan is not None:
             sp = plan["partition"] if args.shared_partition is None else args.shared_partition
             groups = dict(group_start=torch.from_numpy(plan["group_start"]).to(dev),

@@ -69,6 +69,13 @@
 #ifndef PA_MFMA_FOLD_WAVES_FEW
 #define PA_MFMA_FOLD_WAVES_FEW 8
 #endif
+// Waves per workgroup of the shared-prefix tail pass (each sequence's own
+// blocks past its group's shared ones: few per sequence). The 64/8-head
+// copy-on-write batch (tails of 1-256 tokens): 4 waves 37.4 us for the call,
+// 2 waves 37.0, 8 waves 41.5.
+#ifndef PA_MFMA_TAIL_WAVES
+#define PA_MFMA_TAIL_WAVES 4
+#endif
 // Minimum waves per SIMD the register allocation must allow.
 #ifndef PA_MFMA_MIN_WAVES
 #define PA_MFMA_MIN_WAVES 3
@@ -506,6 +513,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
     // its blocks. Split contexts (a partition's few blocks): fewer.
     if (p.group_start)
       go(d, std::integral_constant<int, PA_MFMA_GROUP_WAVES>{});
+    else if (p.tail_pass)
+      go(d, std::integral_constant<int, PA_MFMA_TAIL_WAVES>{});
     else if (p.pass_parts == 1)
       go(d, std::integral_constant<int, PA_MFMA_WAVES_UNSPLIT>{});
     else
