@@ -47,6 +47,9 @@ CHUNKS = {
     # one to three 16-column tiles
     "mq_f32_gqa": Spec("mq_f32_gqa", "f32", 3, 8, 2, 128, seed=46, lengths=("uniform", 1, 600),
                        chunk=("uniform", 1, 12)),
+    # the same at head_dim 64: 20 to 36 columns, two or three tiles per kv head
+    "mq_f32_gqa_d64": Spec("mq_f32_gqa_d64", "f32", 2, 8, 2, 64, seed=49,
+                           lengths=("uniform", 40, 700), chunk=("uniform", 5, 9)),
     "mq_bf16_d64": Spec("mq_bf16_d64", "bf16", 3, 4, 2, 64, seed=37, lengths=("uniform", 1, 300),
                         chunk=("uniform", 1, 9)),
     # head_dim 64 past one tile: 160 to 320 columns per kv head, 10 to 20
