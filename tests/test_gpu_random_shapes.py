@@ -1,0 +1,67 @@
+"""GPU parity on seeded random shapes.
+
+The attention call picks its kernel from the dtype, head_dim, query heads per
+kv head, query rows per sequence and partition length: the vector kernel, the
+bf16 or fp32 matrix-core decode kernel (one workgroup per 16-column tile) or
+the chunk kernel. These cases draw those parameters from a fixed seed, so
+every run checks the same cases and a failure names its case, and compare
+each output with the fp64 oracle on the same inputs, with NaN-poisoned unused
+pool slots, under both tile cache policies (which must give the same bits).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import TOL, Step, max_abs_err, say
+from paged_kv_cache_410_amd.workloads import Spec
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_kv_cache_410_amd as m
+    return m
+
+
+def draw_cases(per_kind, seed):
+    """per_kind cases for each (dtype, head_dim); the other parameters drawn."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for dtype in ("f32", "bf16"):
+        for D in (64, 128):
+            for _ in range(per_kind):
+                k = len(cases)
+                Hkv = (1, 2, 4)[int(rng.integers(3))]
+                G = (1, 2, 3, 4, 8, 16, 32)[int(rng.integers(7))]
+                B = int(rng.integers(1, 6))
+                hi = int(rng.integers(20, 1500))
+                chunk = () if rng.random() < 0.5 else ("uniform", 1, int(rng.integers(2, 24)))
+                partition = (None, 0, 16, 64, 512)[int(rng.integers(5))]
+                name = (f"r{k}_{dtype}_d{D}_{Hkv}x{G}_b{B}_ctx{hi}"
+                        + (f"_q{chunk[2]}" if chunk else ""))
+                spec = Spec(name, dtype, B, Hkv * G, Hkv, D, seed=100 + k,
+                            lengths=("uniform", 1, hi), chunk=chunk)
+                cases.append(pytest.param(spec, partition, id=f"{name}_p{partition}"))
+    return cases
+
+
+@pytest.mark.parametrize("spec,partition", draw_cases(8, 2024))
+def test_random_shape_matches_oracle(pa, spec, partition):
+    say(f"[random shape] {spec.name} partition={partition}")
+    st = Step(spec, poison=True)
+    st.run_cache_ops(pa, fused=True, want_slots=False)
+    run = st.multi if spec.chunk else st.decode
+    out = run(pa, partition=partition, shared_kv=False)
+    cached = run(pa, partition=partition, shared_kv=True)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    assert np.all(np.isfinite(o)), "NaN-poisoned unused slots leaked into the output"
+    err = max_abs_err(out, st.expect)
+    say(f"    max abs err {err:.3e} (tol {TOL[spec.dtype]})")
+    assert err <= TOL[spec.dtype]
+    iview = torch.int16 if out.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(out.view(iview), cached.view(iview))
