@@ -137,7 +137,7 @@ def test_copy_blocks_alone_bit_exact(pa):
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("partition", [None, 0, 16, 64, 512])
+@pytest.mark.parametrize("partition", [None, 0, 16, 64, 256, 512, 1024])
 def test_decode_matches_oracle(pa, name, partition):
     spec = SMALL[name]
     say(f"[decode] {name} partition={partition}")
