@@ -81,6 +81,9 @@ def slot_mapping(block_tables, positions, seq_ids=None, out=None):
         raise ValueError("without seq_ids there is one position per sequence")
     if out is None:
         out = torch.empty(T, dtype=torch.int32, device=block_tables.device)
+    _i32(out, "out")
+    if out.shape != (T,):
+        raise ValueError("out must be [T]")
     dev = _dev(*ts, out)
     with torch.cuda.device(dev):
         check(lib().pa_slot_mapping(out.data_ptr(), block_tables.data_ptr(),
@@ -193,7 +196,12 @@ def check_groups(group_start, seq_shared, block_tables, context_lens, max_group)
     for t, name in ((group_start, "group_start"), (seq_shared, "seq_shared"),
                     (block_tables, "block_tables"), (context_lens, "context_lens")):
         _i32(t, name)
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, MB]")
     B, MB = block_tables.shape
+    if context_lens.shape != (B,) or seq_shared.shape != (B,) or group_start.dim() != 1 \
+            or group_start.shape[0] < 1:
+        raise ValueError("context_lens and seq_shared must be [B], group_start [n_groups + 1]")
     n = group_start.shape[0] - 1
     dev = _dev(group_start, seq_shared, block_tables, context_lens)
     return _count(dev, lambda c, st: lib().pa_check_groups(

@@ -553,3 +553,32 @@ def test_shared_groups_edge_cases(palib):
     bt3 = np.array([[5, -1, 7], [5, -1, 7]], np.int32)
     gs3, sh3 = pa.shared_groups(bt3, np.array([48, 48], np.int32), 4)
     assert gs3.tolist() == [0, 2] and sh3.tolist() == [16, 16]
+
+
+def test_slot_mapping_rejects_a_wrong_output_buffer():
+    # checked before any device call: a short or wide buffer never reaches
+    # the kernel
+    import torch
+
+    import paged_kv_cache_410_amd as pa
+    bt = torch.zeros((2, 3), dtype=torch.int32)
+    pos = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pa.slot_mapping(bt, pos, out=torch.empty(1, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        pa.slot_mapping(bt, pos, out=torch.empty(2, dtype=torch.int64))
+
+
+def test_check_groups_rejects_mismatched_shapes():
+    import torch
+
+    import paged_kv_cache_410_amd as pa
+    bt = torch.zeros((3, 2), dtype=torch.int32)
+    cl = torch.ones(3, dtype=torch.int32)
+    gs = torch.tensor([0, 3], dtype=torch.int32)
+    with pytest.raises(ValueError):   # seq_shared shorter than the batch
+        pa.check_groups(gs, torch.zeros(2, dtype=torch.int32), bt, cl, 4)
+    with pytest.raises(ValueError):   # context_lens shorter than the batch
+        pa.check_groups(gs, torch.zeros(3, dtype=torch.int32), bt, cl[:2], 4)
+    with pytest.raises(ValueError):   # no group bounds at all
+        pa.check_groups(gs[:0], torch.zeros(3, dtype=torch.int32), bt, cl, 4)
