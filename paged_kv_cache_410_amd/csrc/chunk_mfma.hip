@@ -1,5 +1,6 @@
 // Paged attention of many query columns per kv head on the matrix cores
-// (bf16, head_dim 128): chunked prefill, or many drafted tokens per sequence.
+// (bf16, head_dim 128 or 64): chunked prefill, or many drafted tokens per
+// sequence.
 //
 // Method: as the decode kernels ("Why OS Virtual Memory Paging Saved LLM
 // Inference" (a8q9.cn), section 2: K/V gathered block by block through the
@@ -16,10 +17,10 @@
 // tiles' online-softmax states to the end.
 //
 // The waves stream the partition's K/V blocks, two at a time, through an LDS
-// ring of R slots. A slot holds a pair of blocks A, B: K tiles (4 KiB each)
-// then V tiles, written by the loads themselves (buffer_load ... lds) in
-// sixteen 1 KiB pieces, one load instruction each, shared out over the
-// waves: every byte crosses the vector memory path once per workgroup, not
+// ring of R slots. A slot holds a pair of blocks A, B: K tiles (4 KiB each at
+// head_dim 128, 2 KiB at 64) then V tiles, written by the loads themselves
+// (buffer_load ... lds) in 1 KiB pieces (sixteen, or eight), one load
+// instruction each, shared out over the waves: every byte crosses the vector memory path once per workgroup, not
 // once per wave (the per-wave loads of a column tile kept that path busy
 // most of the time). One barrier per pair publishes the slot and frees the
 // previous one. Taking blocks in pairs makes O^T = V^T P^T one K = 32
@@ -27,16 +28,16 @@
 // K = 16 ones, and halves the softmax's per-lane work per block. Output tile
 // et of the PV product holds dims 16 et + 0..15 (row m: dim 16 et + m).
 //
-// LDS image of a tile (rows of 256 bytes, 16 chunks of 16 bytes):
-//   K row r at r * 256, its chunk c in position c ^ r: a 16-lane group loads
-//     one whole row (chunk col ^ row), and the MFMA operand reads (chunk
-//     4 kk + rg of row col) put the 16 lanes on 16 different positions of
-//     the bank width, so neither side conflicts;
-//   V row r at r * 256, its chunk c in position c ^ (2 r mod 16): the
-//     operand comes from transposing LDS reads (ds_read_b64_tr_b16), each
-//     16-lane group naming 32 bytes (chunks 2 et, 2 et + 1) of 4 rows; the
-//     swizzle puts any 8 consecutive rows' 16 chunks on 16 different
-//     positions of the bank width (with c ^ r, two rows 8 apart met).
+// LDS image of a tile (16 rows of 2 D bytes, in 16-byte chunks), row r at
+// r * 2 D, each row's chunks permuted by the swizzle of Ring (chunk_ring.h):
+//   K: the loads still read whole rows (a lane picks the chunk its position
+//     holds), and the MFMA operand reads (chunk 4 kk + rg of row col, for
+//     the 16 lanes of a row group) fall on 16 different bank groups, so
+//     neither side conflicts;
+//   V: the operand comes from transposing LDS reads (ds_read_b64_tr_b16),
+//     each 16-lane group naming 32 bytes (chunks 2 et, 2 et + 1) of 4 rows;
+//     the swizzle puts the chunk pairs of any 8 consecutive rows on
+//     different bank groups (with K's swizzle, two rows 8 apart met).
 // Lanes of a load past the block's rows inside the context write zeros.
 #include "pa_device.h"
 #include "pa_launch.h"
@@ -62,10 +63,18 @@
 
 namespace pa {
 
-template <int NW, int R, int TPW, TilePolicy kPolicy>
+template <int D, int NW, int R, int TPW, TilePolicy kPolicy>
 __global__ __launch_bounds__(NW * kWave)
 __attribute__((amdgpu_waves_per_eu(TPW > 1 ? 3 : NW >= 8 ? PA_CHUNK_MIN_WAVES : NW == 4 ? 3 : 2)))
 void chunk_mfma_kernel(DecodeParams P) {
+  using RG = Ring<D>;
+  constexpr int kRowBytes = RG::kRowBytes;
+  constexpr int kTileBytes = RG::kTileBytes;
+  constexpr int kSlotBytes = RG::kSlotBytes;
+  constexpr int kPieceBytes = RG::kPieceBytes;
+  constexpr int kPieces = RG::kPieces;
+  constexpr int kK = D / 32;  // contraction steps of S^T (32 dims each)
+  constexpr int kE = D / 16;  // 16-dim output tiles of O^T
   static_assert(kPieces % NW == 0, "pieces must divide over the waves");
   static_assert(R >= 3 && R <= 4, "ring of 3 or 4 slots");
   static_assert(TPW == 1 || TPW == 2, "one or two column tiles per wave");
@@ -126,7 +135,7 @@ void chunk_mfma_kernel(DecodeParams P) {
   // Q[column col][32 kk + 8 rg ..].
   int gc[TPW], ctx_col[TPW], ctx_min[TPW];
   bool col_ok[TPW];
-  bf16x8_t qop[TPW][4];
+  bf16x8_t qop[TPW][kK];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int cb = 16 * (tile0 + TPW * w + t);
@@ -144,7 +153,7 @@ void chunk_mfma_kernel(DecodeParams P) {
           reinterpret_cast<const char*>(P.q) + ((size_t)(sr.first + qi) * P.Hq + qh) * kRowBytes;
       const uint32_t flip = q_neg ? 0x80008000u : 0u;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < kK; ++kk) {
         uint4 u = ld16(qp + (32 * kk + 8 * rg) * 2);
         u = make_uint4(u.x ^ flip, u.y ^ flip, u.z ^ flip, u.w ^ flip);
         if (!col_ok[t]) u = make_uint4(0, 0, 0, 0);
@@ -161,13 +170,13 @@ void chunk_mfma_kernel(DecodeParams P) {
   if (p >= max(nparts_wg, 1)) return;  // partition past the workgroup's contexts
 
   float m[TPW], lsum[TPW];
-  f32x4_t acc[TPW][8];
+  f32x4_t acc[TPW][kE];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     m[t] = kNoRef;
     lsum[t] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[t][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int e = 0; e < kE; ++e) acc[t][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
   bool bad = sr.bad || is.bad;
 
@@ -176,17 +185,21 @@ void chunk_mfma_kernel(DecodeParams P) {
   const size_t head_off = (size_t)g * kTileBytes;
   const size_t block_stride = (size_t)P.Hkv * kTileBytes;
 
-  // This wave's pieces of every pair: piece q = kPer w + i holds rows
-  // 4 (q & 3) + 0..3 of tile q >> 2 (0: K of block A, 1: K of block B, 2: V
-  // of A, 3: V of B), at q KiB into the slot. K tiles keep chunk c of row r
-  // at position c ^ r, V tiles at c ^ (2 r mod 16).
+  // This wave's pieces of every pair: piece q = kPer w + i of the slot (at q
+  // KiB into it) holds kRowsPerPiece consecutive rows of tile
+  // q / kPiecesPerTile (0: K of block A, 1: K of block B, 2: V of A, 3: V of
+  // B); lane l writes position l % kChunks of row l / kChunks of the piece,
+  // so it loads the chunk that the tile's swizzle (Ring::k_pos, v_pos) puts
+  // there.
+  constexpr int kPiecesPerTile = RG::kPiecesPerTile;
   int piece_off[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int q = kPer * w + i;
-    const int r = 4 * (q & 3) + rg;
-    const int swz = q >= 8 ? (2 * r) & 14 : r;  // V tiles: c ^ (2 r mod 16); K tiles: c ^ r
-    piece_off[i] = r * kRowBytes + ((col ^ swz) & 15) * 16;
+    const int r = RG::kRowsPerPiece * (q % kPiecesPerTile) + lane / RG::kChunks;
+    const int pos = lane % RG::kChunks;
+    const bool v_tile = q / kPiecesPerTile >= 2;
+    piece_off[i] = r * kRowBytes + (v_tile ? RG::v_pos(r, pos) : RG::k_pos(r, pos)) * 16;
   }
 
   // Transposed V reads (ds_read_b64_tr_b16): in each group of 16 lanes, lane
@@ -196,12 +209,12 @@ void chunk_mfma_kernel(DecodeParams P) {
   // + 3, so it receives V[4 rg + e][16 et + col], e = 0..3: its operand of
   // output tile et, row m = col standing for dim 16 et + col. Offsets within
   // a (swizzled) V tile, per tile et:
-  int vtr_off[8];
+  int vtr_off[kE];
 #pragma unroll
-  for (int et = 0; et < 8; ++et) {
+  for (int et = 0; et < kE; ++et) {
     const int r = 4 * rg + col / 4;
     const int dim = 16 * et + 4 * (col % 4);
-    vtr_off[et] = r * kRowBytes + (((dim / 8) ^ ((2 * r) & 14)) & 15) * 16 + (dim % 8) * 2;
+    vtr_off[et] = r * kRowBytes + RG::v_pos(r, dim / 8) * 16 + (dim % 8) * 2;
   }
 
   // Load the pair of blocks at lanes i, i + 1 of the current 64-block chunk
@@ -222,9 +235,9 @@ void chunk_mfma_kernel(DecodeParams P) {
       return make_rsrc((t >= 2 ? vbase : kbase) + off, bytes);
     };
     char* dst = slot(d);
-    if constexpr (kPer <= 4) {
+    if constexpr (kPer <= kPiecesPerTile) {
       // all of the wave's pieces lie in one tile: one descriptor
-      const rsrc_t r = rsrc_of((kPer * w) >> 2);
+      const rsrc_t r = rsrc_of((kPer * w) / kPiecesPerTile);
 #pragma unroll
       for (int q = 0; q < kPer; ++q)
         ld16_lds<kPolicy>(r, dst + (kPer * w + q) * kPieceBytes, piece_off[q]);
@@ -232,7 +245,7 @@ void chunk_mfma_kernel(DecodeParams P) {
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int pc = kPer * w + q;
-        ld16_lds<kPolicy>(rsrc_of(pc >> 2), dst + pc * kPieceBytes, piece_off[q]);
+        ld16_lds<kPolicy>(rsrc_of(pc / kPiecesPerTile), dst + pc * kPieceBytes, piece_off[q]);
       }
     }
   };
@@ -339,8 +352,8 @@ void chunk_mfma_kernel(DecodeParams P) {
     }
     if constexpr (PA_CHUNK_PRIO != 0) __builtin_amdgcn_s_setprio(PA_CHUNK_PRIO);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int o = col * kRowBytes + (((4 * kk + rg) ^ col) & 15) * 16;
+    for (int kk = 0; kk < kK; ++kk) {
+      const int o = col * kRowBytes + RG::k_pos(col, 4 * kk + rg) * 16;
       const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + o));
       const bf16x8_t kb =
           __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(src + kTileBytes + o));
@@ -353,19 +366,19 @@ void chunk_mfma_kernel(DecodeParams P) {
     if constexpr (PA_CHUNK_PRIO != 0) __builtin_amdgcn_s_setprio(0);
     if constexpr (TPW == 1) {
       // V operands read now, so that their latency passes under the softmax.
-      bf16x8_t vop[8];
+      bf16x8_t vop[kE];
 #pragma unroll
-      for (int et = 0; et < 8; ++et) vop[et] = v_operand(src, et);
+      for (int et = 0; et < kE; ++et) vop[et] = v_operand(src, et);
       float x0[8];
       logits(sa[0], sb[0], x0);
       if (edge) mask_logits(0, x0, blk, b_live);
       const Probs p0 = softmax(0, x0);
       if (__builtin_amdgcn_ballot_w64(p0.up) != 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[0][e] *= p0.alpha;
+        for (int e = 0; e < kE; ++e) acc[0][e] *= p0.alpha;
       }
 #pragma unroll
-      for (int et = 0; et < 8; ++et)
+      for (int et = 0; et < kE; ++et)
         acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p0.pop, acc[0][et], 0, 0, 0);
     } else {
       // Both tiles' softmax in one basic block (one mask branch, and the two
@@ -386,13 +399,13 @@ void chunk_mfma_kernel(DecodeParams P) {
       const Probs p1 = softmax_with(1, x1, cm1);
       if (__builtin_amdgcn_ballot_w64(p0.up || p1.up) != 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < kE; ++e) {
           acc[0][e] *= p0.alpha;
           acc[1][e] *= p1.alpha;
         }
       }
 #pragma unroll
-      for (int et = 0; et < 8; ++et) {
+      for (int et = 0; et < kE; ++et) {
         const bf16x8_t v = v_operand(src, et);
         acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p0.pop, acc[0][et], 0, 0, 0);
         acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p1.pop, acc[1][et], 0, 0, 0);
@@ -456,9 +469,9 @@ void chunk_mfma_kernel(DecodeParams P) {
     const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
     if (np > 1 || P.always_partial) {
       const size_t part = part_slot(P, sr.first + i, h, P.part_base + p);
-      float* dst = static_cast<float*>(P.ws_o) + part * kD;  // fp32 rows (part_f32)
+      float* dst = static_cast<float*>(P.ws_o) + part * D;  // fp32 rows (part_f32)
 #pragma unroll
-      for (int et = 0; et < 8; ++et)
+      for (int et = 0; et < kE; ++et)
         *reinterpret_cast<float4*>(dst + 16 * et + 4 * rg) =
             bad ? make_float4(nan, nan, nan, nan)
                 : make_float4(acc[t][et][0], acc[t][et][1], acc[t][et][2], acc[t][et][3]);
@@ -469,12 +482,12 @@ void chunk_mfma_kernel(DecodeParams P) {
     } else {
       const float inv = l_col > 0.0f ? 1.0f / l_col : 0.0f;
 #pragma unroll
-      for (int et = 0; et < 8; ++et) {
+      for (int et = 0; et < kE; ++et) {
         float res[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) res[e] = bad ? nan : acc[t][et][e] * inv;
         *reinterpret_cast<uint2*>(reinterpret_cast<char*>(P.out) +
-                                  (orow * kD + 16 * et + 4 * rg) * 2) =
+                                  (orow * D + 16 * et + 4 * rg) * 2) =
             make_uint2(pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]));
       }
     }
@@ -488,23 +501,32 @@ void chunk_mfma_kernel(DecodeParams P) {
 // PA_CHUNK_TILES_PER_WAVE 1, one tile per wave on 8 waves).
 hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int R = PA_CHUNK_RING;
-  auto go = [&](auto nw, auto tpw) {
+  auto go = [&](auto d, auto nw, auto tpw) {
+    constexpr int HD = decltype(d)::value;
     constexpr int NW = decltype(nw)::value;
     constexpr int TPW = decltype(tpw)::value;
     const dim3 grid(p.Hkv * ((p.n_tiles + NW * TPW - 1) / (NW * TPW)), p.pass_parts,
                     p.pass_items);
-    hipLaunchKernelGGL((chunk_mfma_kernel<NW, R, TPW, TilePolicy::kShared>), grid,
+    hipLaunchKernelGGL((chunk_mfma_kernel<HD, NW, R, TPW, TilePolicy::kShared>), grid,
                        dim3(NW * kWave), 0, stream, p);
   };
-  using I = std::integral_constant<int, 1>;
-  if (p.n_tiles <= 2 || PA_CHUNK_MAX_WAVES == 2)
-    go(std::integral_constant<int, 2>{}, I{});
-  else if (p.n_tiles <= 4 || PA_CHUNK_MAX_WAVES == 4)
-    go(std::integral_constant<int, 4>{}, I{});
-  else if (p.n_tiles <= 8 || PA_CHUNK_TILES_PER_WAVE == 1)
-    go(std::integral_constant<int, 8>{}, I{});
+  auto by_tiles = [&](auto d) {
+    using I = std::integral_constant<int, 1>;
+    if (p.n_tiles <= 2 || PA_CHUNK_MAX_WAVES == 2)
+      go(d, std::integral_constant<int, 2>{}, I{});
+    else if (p.n_tiles <= 4 || PA_CHUNK_MAX_WAVES == 4)
+      go(d, std::integral_constant<int, 4>{}, I{});
+    else if (p.n_tiles <= 8 || PA_CHUNK_TILES_PER_WAVE == 1)
+      go(d, std::integral_constant<int, 8>{}, I{});
+    else
+      go(d, std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
+  };
+  if (p.D == 128)
+    by_tiles(std::integral_constant<int, 128>{});
+  else if (p.D == 64)
+    by_tiles(std::integral_constant<int, 64>{});
   else
-    go(std::integral_constant<int, 4>{}, std::integral_constant<int, 2>{});
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

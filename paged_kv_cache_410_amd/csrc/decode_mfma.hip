@@ -466,9 +466,9 @@ void decode_mfma_kernel(DecodeParams P) {
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
-  // several column tiles per kv head at head_dim 128: the chunk kernel, whose
-  // waves share each block (at 64, one workgroup per tile, below)
-  if (p.n_tiles > 1 && p.D == 128) return launch_chunk_mfma(p, stream);
+  // several column tiles per kv head: the chunk kernel, whose waves share
+  // each block
+  if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
   constexpr int DEPTH = PA_MFMA_DEPTH;
   if (p.fold_tails) {
     // group pass with the members' own blocks folded in (head_dim 128): the

@@ -305,14 +305,13 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   // The matrix-core kernels serve a kv head's columns (query rows x group
   // heads) 16 at a time; a single column per kv head (one query head, one
   // row) goes to the vector kernel. bf16: past 16 columns per kv head the
-  // chunk kernel takes over at head_dim 128; at 64, and in fp32, one
-  // workgroup per 16-column tile.
+  // chunk kernel takes over; in fp32, one workgroup per 16-column tile.
   const bool several = p.G >= 2 || max_q >= 2;
   const bool mfma = dt == PA_BF16 && several;
   const bool mfma32 = dt == PA_F32 && several;
   if ((mfma || mfma32) && (int64_t)Hkv * p.n_tiles > INT32_MAX) return PA_EUNSUPPORTED;
-  // fp32 I/O, or the chunk kernel (bf16, head_dim 128, several tiles)
-  p.part_f32 = dt == PA_F32 || (mfma && p.n_tiles > 1 && D == 128);
+  // fp32 I/O, or the chunk kernel (bf16, several tiles)
+  p.part_f32 = dt == PA_F32 || (mfma && p.n_tiles > 1);
   hipError_t err = mfma     ? pa::launch_decode_mfma(p, stream)
                    : mfma32 ? pa::launch_decode_mfma_f32(p, stream)
                             : pa::launch_decode_valu(p, dt, D, stream);

@@ -31,6 +31,7 @@ Workloads (lengths, seeds and draw order are fixed here):
   gqa_chunk512  bf16, 16 seqs, 64/8 heads, head_dim 128, contexts
         U[1024, 8192] whose last 512 tokens are the step's chunk (a prompt
         processed in 512-token chunks).                             seed 6
+  gqa_chunk512_d64  the same recipe at head_dim 64.                 seed 11
 
 Draw order for a seed: lengths -> free-list permutation -> q -> K pool ->
 V pool -> new K -> new V. Values are N(0, 1) in fp32, rounded to the
@@ -106,6 +107,10 @@ CONFIGS = {
                         lengths=("lognormal", 500.0, 0.7, 16, 2048), chunk=("uniform", 4, 4)),
     "gqa_chunk512": Spec("gqa_chunk512", "bf16", 16, 64, 8, 128, seed=6,
                          lengths=("uniform", 1024, 8192), chunk=("uniform", 512, 512)),
+    # the same chunks at head_dim 64 (a study workload for the chunk kernel's
+    # 128-byte rows)
+    "gqa_chunk512_d64": Spec("gqa_chunk512_d64", "bf16", 16, 64, 8, 64, seed=11,
+                             lengths=("uniform", 1024, 8192), chunk=("uniform", 512, 512)),
 }
 
 

@@ -7,8 +7,8 @@ attention of the sequence's whole history wherever its blocks sit ("Can OS
 paging techniques reduce LLM serving memory waste?", mechanism paragraph;
 "Why OS Virtual Memory Paging Saved LLM Inference", section 2). That is
 checked on every (query row, head) of every decode workload. The 512-token
-chunk workload (about 6e11 products for the whole step) is checked on every
-row and head of its 4 longest and 4 shortest sequences.
+chunk workloads (about 6e11 products for the whole step at head_dim 128) are
+checked on every row and head of their 4 longest and 4 shortest sequences.
 """
 
 import numpy as np
@@ -74,8 +74,9 @@ def test_full_config_whole_output(pa, name):
     assert err <= TOL[st.spec.dtype]
 
 
-def test_full_config_chunk512_longest_and_shortest(pa):
-    st, out = run_step(pa, "gqa_chunk512")
+@pytest.mark.parametrize("name", ["gqa_chunk512", "gqa_chunk512_d64"])
+def test_full_config_chunk512_longest_and_shortest(pa, name):
+    st, out = run_step(pa, name)
     cl = st.tb.context_lens
     qs = st.tb.query_start
     order = np.argsort(cl, kind="stable")
@@ -90,7 +91,7 @@ def test_full_config_chunk512_longest_and_shortest(pa):
     got = got[np.asarray(rows)].reshape(len(rows) * Hq, -1)
     err = float(np.max(np.abs(got - expect)))
     say(f"    max abs err {err:.3e} (tol {TOL[st.spec.dtype]})")
-    record_parity(f"gqa_chunk512 (pa_multi_query, every row of 8 of 16 sequences)", err,
+    record_parity(f"{name} (pa_multi_query, every row of 8 of 16 sequences)", err,
                   TOL[st.spec.dtype])
     assert err <= TOL[st.spec.dtype]
     # the rest of the rows: finite, and (a convex combination of N(0,1) bf16
