@@ -169,11 +169,18 @@ void chunk_mfma_kernel(DecodeParams P) {
   const int nparts_wg = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
   if (p >= max(nparts_wg, 1)) return;  // partition past the workgroup's contexts
 
-  float m[TPW], lsum[TPW];
+  // The reference m (what the probabilities are taken relative to) moves
+  // only when a column's max passes it by more than kLazy: the
+  // probabilities then stay below 2^kLazy, the result is the same up to
+  // rounding, and the accumulators are rescaled a few times per column
+  // instead of whenever its max creeps up. mlazy = m + kLazy, kept with m.
+  constexpr float kLazy = 8.0f;
+  float m[TPW], mlazy[TPW], lsum[TPW];
   f32x4_t acc[TPW][kE];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     m[t] = kNoRef;
+    mlazy[t] = kNoRef + kLazy;
     lsum[t] = 0.0f;
 #pragma unroll
     for (int e = 0; e < kE; ++e) acc[t][e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -275,53 +282,54 @@ void chunk_mfma_kernel(DecodeParams P) {
     }
   };
   // The online softmax of tile t over one pair of blocks, from its raw
-  // logits x (S^T of block A, then of block B): updates the tile's reference
-  // m and sum, and gives the probabilities as the bf16 B operand of the PV
-  // product with the factor alpha that takes the accumulators to the new
-  // reference.
-  struct Probs {
-    bf16x8_t pop;
-    float alpha;
-    bool up;
-  };
+  // logits x (S^T of block A, then of block B), in two steps: move the
+  // tile's reference where a column's max passed it (reference_from), then
+  // take the probabilities against the reference (probs).
   auto lane_max = [](const float (&x)[8]) {
     return vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])), vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
   };
-  // col_max: the column's largest raw logit over the pair (all 4 row groups).
-  auto softmax_with = [&](int t, const float (&x)[8], float col_max) -> Probs {
+  // Whether this lane's logits of tile t (lane max lm) pass the reference by
+  // more than kLazy. Where no lane of the wave does, no column's reference
+  // moves (a column's max is its lanes' largest, and rounding the product
+  // with qs > 0 keeps the order): the reference step can be skipped, since
+  // its alpha would be exactly 1.
+  auto passes = [&](int t, float lm) { return lm * qs > mlazy[t]; };
+  // col_max: the column's largest raw logit over the pair (all 4 row
+  // groups). Moves the reference if that passes it by more than kLazy and
+  // scales the tile's sum to the new reference; returns the factor alpha
+  // that takes the accumulators there (sets up when it is not 1).
+  auto reference_from = [&](int t, float col_max, bool& up) {
     const float mx = col_max * qs;  // -inf stays -inf (qs > 0)
-    // The reference m (what the probabilities are taken relative to) moves
-    // only when a column's max passes it by more than kLazy: the
-    // probabilities then stay below 2^kLazy, the result is the same up to
-    // rounding, and the accumulators are rescaled a few times per column
-    // instead of whenever its max creeps up.
-    constexpr float kLazy = 8.0f;
     const float m_new = vmax(m[t], mx);
-    const bool up = m_new > m[t] + kLazy;  // from kNoRef: any finite max
+    up = m_new > mlazy[t];  // from kNoRef: any finite max
     const float ref = up ? m_new : m[t];
     // Exactly 1 where the reference stays; 0 (or 2^-inf) from kNoRef, where
     // the accumulators hold nothing yet.
     const float alpha = exp2_fast(m[t] - ref);
+    m[t] = ref;
+    mlazy[t] = ref + kLazy;
+    lsum[t] *= alpha;
+    return alpha;
+  };
+  // Probabilities of tile t against its reference, as the bf16 B operand of
+  // the PV product, added to the tile's sum. The sum takes the
+  // probabilities as rounded for the PV product (a dot product of each bf16
+  // pair with (1, 1)): numerator and denominator see the same values, in 4
+  // instructions instead of 8.
+  auto probs = [&](int t, const float (&x)[8]) -> bf16x8_t {
     float pr[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -ref));
-    m[t] = ref;
+    for (int i = 0; i < 8; ++i) pr[i] = exp2_fast(__builtin_fmaf(x[i], qs, -m[t]));
     const uint4 w4 = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                 pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
-    // The sum takes the probabilities as rounded for the PV product (a dot
-    // product of each bf16 pair with (1, 1)): numerator and denominator see
-    // the same values, in 4 instructions instead of 8.
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float l = lsum[t] * alpha;
+    float l = lsum[t];
     l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.x), ones, l, false);
     l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.y), ones, l, false);
     l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.z), ones, l, false);
     l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w4.w), ones, l, false);
     lsum[t] = l;
-    return {__builtin_bit_cast(bf16x8_t, w4), alpha, up};
-  };
-  auto softmax = [&](int t, const float (&x)[8]) {
-    return softmax_with(t, x, rows_vmax(lane_max(x)));
+    return __builtin_bit_cast(bf16x8_t, w4);
   };
   // Raw logits of tile t (S^T of blocks A then B).
   auto logits = [&](const f32x4_t& sa, const f32x4_t& sb, float (&x)[8]) {
@@ -372,20 +380,27 @@ void chunk_mfma_kernel(DecodeParams P) {
       float x0[8];
       logits(sa[0], sb[0], x0);
       if (edge) mask_logits(0, x0, blk, b_live);
-      const Probs p0 = softmax(0, x0);
-      if (__builtin_amdgcn_ballot_w64(p0.up) != 0) {
+      const float lm0 = lane_max(x0);
+      if (__builtin_amdgcn_ballot_w64(passes(0, lm0)) != 0) {
+        bool up0;
+        const float a0 = reference_from(0, rows_vmax(lm0), up0);
+        if (__builtin_amdgcn_ballot_w64(up0) != 0) {
 #pragma unroll
-        for (int e = 0; e < kE; ++e) acc[0][e] *= p0.alpha;
+          for (int e = 0; e < kE; ++e) acc[0][e] *= a0;
+        }
       }
+      const bf16x8_t pop0 = probs(0, x0);
 #pragma unroll
       for (int et = 0; et < kE; ++et)
-        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], p0.pop, acc[0][et], 0, 0, 0);
+        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[et], pop0, acc[0][et], 0, 0, 0);
     } else {
-      // Both tiles' softmax in one basic block (one mask branch, and the two
-      // dependency chains overlap), one branch that rescales both where
-      // either's reference moved (the other's alpha is then exactly 1), then
-      // each V operand read just before its two MFMAs (registers are short
-      // with two tiles).
+      // Both tiles' softmax together (one mask branch, and the two
+      // dependency chains overlap). On most pairs one wave-wide test shows
+      // that neither tile's reference moves; otherwise both tiles' column
+      // maxima come from one lane exchange, and one branch rescales both
+      // where either's reference moved (the other's alpha is then exactly 1).
+      // Then the probabilities, and each V operand read just before its two
+      // MFMAs (registers are short with two tiles).
       float x0[8], x1[8];
       logits(sa[0], sb[0], x0);
       logits(sa[1], sb[1], x1);
@@ -393,22 +408,27 @@ void chunk_mfma_kernel(DecodeParams P) {
         mask_logits(0, x0, blk, b_live);
         mask_logits(1, x1, blk, b_live);
       }
-      float cm0, cm1;
-      rows_vmax2(lane_max(x0), lane_max(x1), cm0, cm1);
-      const Probs p0 = softmax_with(0, x0, cm0);
-      const Probs p1 = softmax_with(1, x1, cm1);
-      if (__builtin_amdgcn_ballot_w64(p0.up || p1.up) != 0) {
+      const float lm0 = lane_max(x0), lm1 = lane_max(x1);
+      if (__builtin_amdgcn_ballot_w64(passes(0, lm0) || passes(1, lm1)) != 0) {
+        float cm0, cm1;
+        rows_vmax2(lm0, lm1, cm0, cm1);
+        bool up0, up1;
+        const float a0 = reference_from(0, cm0, up0);
+        const float a1 = reference_from(1, cm1, up1);
+        if (__builtin_amdgcn_ballot_w64(up0 || up1) != 0) {
 #pragma unroll
-        for (int e = 0; e < kE; ++e) {
-          acc[0][e] *= p0.alpha;
-          acc[1][e] *= p1.alpha;
+          for (int e = 0; e < kE; ++e) {
+            acc[0][e] *= a0;
+            acc[1][e] *= a1;
+          }
         }
       }
+      const bf16x8_t pop0 = probs(0, x0), pop1 = probs(1, x1);
 #pragma unroll
       for (int et = 0; et < kE; ++et) {
         const bf16x8_t v = v_operand(src, et);
-        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p0.pop, acc[0][et], 0, 0, 0);
-        acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p1.pop, acc[1][et], 0, 0, 0);
+        acc[0][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop0, acc[0][et], 0, 0, 0);
+        acc[1][et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pop1, acc[1][et], 0, 0, 0);
       }
     }
   };
