@@ -285,8 +285,9 @@ void chunk_mfma_kernel(DecodeParams P) {
   // logits x (S^T of block A, then of block B), in two steps: move the
   // tile's reference where a column's max passed it (reference_from), then
   // take the probabilities against the reference (probs).
-  // (chained so that each pair of maxima becomes one three-input maximum:
-  // 4 instructions for 8 values)
+  //
+  // A lane's largest logit of the pair, chained so that each two maxima
+  // become one three-input maximum: 4 instructions for 8 values.
   auto lane_max = [](const float (&x)[8]) {
     const float a = vmax(vmax(x[0], x[1]), x[2]);
     const float b = vmax(vmax(x[3], x[4]), x[5]);
