@@ -361,7 +361,7 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
  * of every group (one read of its blocks for all members' query heads, on
  * the matrix cores, into the workspace), then every sequence's own tokens,
  * merged with its shared part into the final row. Supported for bf16 with
- * D = 128 and Hq / Hkv <= 16 (else PA_EUNSUPPORTED). A shared length that is
+ * Hq / Hkv <= 16 (else PA_EUNSUPPORTED). A shared length that is
  * negative, not a multiple of bs or beyond the table gives that sequence an
  * all-NaN
  * row (the group pass takes the first member's, so a bad one there gives the

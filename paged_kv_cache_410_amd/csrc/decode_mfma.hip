@@ -1,5 +1,5 @@
-// Paged attention on the matrix cores (bf16, head_dim 128): grouped query
-// heads, and several new query tokens per sequence.
+// Paged attention on the matrix cores (bf16, head_dim 128 or 64): grouped
+// query heads, and several new query tokens per sequence.
 //
 // Method: as the vector path ("Why OS Virtual Memory Paging Saved LLM
 // Inference" (a8q9.cn), section 2: K/V gathered block by block through the
@@ -11,9 +11,8 @@
 //
 // Columns: the n x G (query row, head of the group) pairs of a sequence and
 // kv head, row-major, in tiles of 16; one workgroup per (kv head, tile,
-// partition, sequence). At head_dim 128 a kv head with more than one tile
-// goes to the chunk kernel (chunk_mfma.hip, same layouts), whose waves share
-// each block. Column (i, q) attends over its row's causal prefix
+// partition, sequence). A kv head with more than one tile goes to the chunk
+// kernel (chunk_mfma.hip, same layouts), whose waves share each block. Column (i, q) attends over its row's causal prefix
 // (ctx - n + i + 1 tokens): a per-column limit masks the logits. The decode
 // step is n = 1: the columns are the G heads.
 //
@@ -84,9 +83,9 @@
 namespace pa {
 
 // The waves of a workgroup interleave the blocks of one column tile (wave w
-// takes blocks w, w + NW, ...) and merge their states through LDS. At head_dim
-// 128 a kv head with more than one tile (several query rows per sequence)
-// goes to the chunk kernel instead, whose waves share each block.
+// takes blocks w, w + NW, ...) and merge their states through LDS. A kv head
+// with more than one tile (several query rows per sequence) goes to the
+// chunk kernel instead, whose waves share each block.
 //
 // kFold (the shared-prefix group pass, one partition, one tile): after the
 // group's shared blocks (every column), each member's own blocks, read
@@ -116,8 +115,8 @@ void decode_mfma_kernel(DecodeParams P) {
   const int col = lane & 15;
   const int rg = lane >> 4;
 
-  // Several tiles per kv head (head_dim 64 past 16 columns; the chunk kernel
-  // takes them at 128): they read the same K/V and are kept on one XCD.
+  // The launcher sends a kv head with several tiles to the chunk kernel; if
+  // one came here, its tiles would read the same K/V, kept on one XCD.
   const GridPos gp = P.n_tiles > 1 ? grid_pos_grouped(P.n_tiles) : grid_pos();
   const int p = gp.y;
   const int g = gp.x / P.n_tiles;    // kv head
@@ -471,30 +470,38 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
   constexpr int DEPTH = PA_MFMA_DEPTH;
   if (p.fold_tails) {
-    // group pass with the members' own blocks folded in (head_dim 128): the
-    // shared blocks' policy from shared_kv, the own blocks' from tail_shared_kv
-    if (p.D != 128) return hipErrorInvalidValue;
-    auto fold = [&](auto nw) {
+    // group pass with the members' own blocks folded in: the shared blocks'
+    // policy from shared_kv, the own blocks' from tail_shared_kv
+    auto fold = [&](auto d, auto nw) {
+      constexpr int HD = decltype(d)::value;
       constexpr int NW = decltype(nw)::value;
       constexpr TilePolicy S = TilePolicy::kShared, T = TilePolicy::kStream;
       const dim3 grid(p.Hkv, 1, p.pass_items), block(NW * kWave);
       if (p.shared_kv && p.tail_shared_kv)
-        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, S, true, S>), grid, block, 0,
+        hipLaunchKernelGGL((decode_mfma_kernel<HD, NW, DEPTH, S, true, S>), grid, block, 0,
                            stream, p);
       else if (p.shared_kv)
-        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, S, true, T>), grid, block, 0,
+        hipLaunchKernelGGL((decode_mfma_kernel<HD, NW, DEPTH, S, true, T>), grid, block, 0,
                            stream, p);
       else if (p.tail_shared_kv)
-        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, T, true, S>), grid, block, 0,
+        hipLaunchKernelGGL((decode_mfma_kernel<HD, NW, DEPTH, T, true, S>), grid, block, 0,
                            stream, p);
       else
-        hipLaunchKernelGGL((decode_mfma_kernel<128, NW, DEPTH, T, true, T>), grid, block, 0,
+        hipLaunchKernelGGL((decode_mfma_kernel<HD, NW, DEPTH, T, true, T>), grid, block, 0,
                            stream, p);
     };
-    if ((int64_t)p.Hkv * p.pass_items <= p.n_cus)
-      fold(std::integral_constant<int, PA_MFMA_FOLD_WAVES_FEW>{});
+    auto fold_waves = [&](auto d) {
+      if ((int64_t)p.Hkv * p.pass_items <= p.n_cus)
+        fold(d, std::integral_constant<int, PA_MFMA_FOLD_WAVES_FEW>{});
+      else
+        fold(d, std::integral_constant<int, PA_MFMA_FOLD_WAVES>{});
+    };
+    if (p.D == 128)
+      fold_waves(std::integral_constant<int, 128>{});
+    else if (p.D == 64)
+      fold_waves(std::integral_constant<int, 64>{});
     else
-      fold(std::integral_constant<int, PA_MFMA_FOLD_WAVES>{});
+      return hipErrorInvalidValue;
     return hipGetLastError();
   }
   auto go = [&](auto d, auto nw) {
@@ -522,7 +529,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   };
   if (p.D == 128)
     by_waves(std::integral_constant<int, 128>{});
-  else if (p.D == 64 && !p.group_start && !p.tail_pass)
+  else if (p.D == 64)
     by_waves(std::integral_constant<int, 64>{});
   else
     return hipErrorInvalidValue;

@@ -389,12 +389,12 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   if (max_shared > max_ctx) return PA_EINVAL;
   if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
   if (D != 64 && D != 128) return PA_EUNSUPPORTED;
-  // the group pass runs on the matrix-core kernels (bf16, D = 128): the
-  // decode kernel for one 16-column tile of (member, query head) pairs per kv
-  // head, the chunk kernel for more; the tail pass takes one tile of a
-  // sequence's query heads (G <= 16)
+  // the group pass runs on the bf16 matrix-core kernels: the decode kernel
+  // for one 16-column tile of (member, query head) pairs per kv head, the
+  // chunk kernel for more; the tail pass takes one tile of a sequence's query
+  // heads (G <= 16)
   const int32_t G = Hq / Hkv;
-  if (dt != PA_BF16 || D != 128 || G > 16) return PA_EUNSUPPORTED;
+  if (dt != PA_BF16 || G > 16) return PA_EUNSUPPORTED;
   if (B > kMaxGridYZ || n_groups > kMaxGridYZ || max_group > kMaxGridYZ) return PA_EUNSUPPORTED;
   const int64_t group_tiles = ((int64_t)max_group * G + 15) / 16;
   if ((int64_t)Hkv * group_tiles > INT32_MAX) return PA_EUNSUPPORTED;
@@ -482,7 +482,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   t.partition = 0;
   t.pass_parts = 1;
   t.pass_items = B;
-  const bool mfma = G >= 2;  // bf16, D = 128 here
+  const bool mfma = G >= 2;  // bf16 here
   if ((mfma ? pa::launch_decode_mfma(t, stream) : pa::launch_decode_valu(t, dt, D, stream)) !=
       hipSuccess)
     return PA_EHIP;

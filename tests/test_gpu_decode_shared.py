@@ -42,7 +42,8 @@ def run_shared(pa, st, gs, sh, mg, partition, context_lens=None):
 
 
 @pytest.mark.parametrize("name", ["cow_small", "cow_gqa", "prefix_small", "mha_bf16", "gqa8",
-                                  "long_mha"])
+                                  "long_mha", "cow_small_d64", "cow_gqa_d64", "prefix_small_d64",
+                                  "mha_bf16_d64"])
 @pytest.mark.parametrize("partition", [0, 16, 48, 512])
 def test_decode_shared_matches_oracle(pa, name, partition):
     spec = SMALL[name]
@@ -143,7 +144,7 @@ def test_decode_shared_full_config_whole_output(pa, name):
     assert err <= TOL[spec.dtype]
 
 
-@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa"])
+@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa", "cow_gqa_d64"])
 def test_decode_shared_cache_flags_give_identical_bits(pa, name):
     """PA_KV_SHARED and PA_KV_SHARED_GROUPS change how tiles are cached, never
     the result."""
@@ -302,7 +303,7 @@ def test_decode_shared_malformed_groups_stay_in_bounds(pa):
     assert torch.equal(out[intact], good[intact])
 
 
-@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa"])
+@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa", "prefix_small_d64"])
 def test_decode_shared_permutation_invariant_and_deterministic(pa, name):
     """The blocks relabelled by a random permutation of the pool (pools and
     tables alike) give bitwise the same outputs, as does a second run:

@@ -57,6 +57,18 @@ SMALL = {
     "cow_gqa": Spec("cow_gqa", "bf16", 6, 8, 2, 128, seed=22, lengths=("cow",),
                     cow=dict(prompts=2, samples=3, prompt_len=64, r_max=15, tail_lo=1,
                              tail_hi=30)),
+    # the sharing workloads at head_dim 64, and 32 heads per kv head there
+    # (two column tiles: the chunk kernel with 128-byte rows)
+    "cow_small_d64": Spec("cow_small_d64", "bf16", 8, 4, 4, 64, seed=50, lengths=("cow",),
+                          cow=dict(prompts=2, samples=4, prompt_len=96, r_max=15, tail_lo=1,
+                                   tail_hi=40)),
+    "prefix_small_d64": Spec("prefix_small_d64", "bf16", 6, 4, 2, 64, seed=51,
+                             lengths=("prefix",),
+                             prefix=dict(shared=80, tail_lo=1, tail_hi=40, vocab=50)),
+    "cow_gqa_d64": Spec("cow_gqa_d64", "bf16", 6, 8, 2, 64, seed=52, lengths=("cow",),
+                        cow=dict(prompts=2, samples=3, prompt_len=64, r_max=15, tail_lo=1,
+                                 tail_hi=30)),
+    "gqa32_d64": Spec("gqa32_d64", "bf16", 2, 32, 1, 64, seed=53, lengths=("uniform", 1, 500)),
     # fp32 grouped heads on the matrix cores (v_mfma_f32_16x16x4_f32): 8 heads
     # per kv head; a full 16-column tile at head_dim 64; two tiles per kv head
     # (32 heads); unsplit rows longer than one 64-block id chunk per wave
