@@ -190,7 +190,7 @@ def test_check_groups_counts_violations(pa):
         assert n == e, (n, e)
 
 
-def fork_tree_batch(seed, Hq, Hkv, NB=600):
+def fork_tree_batch(seed, Hq, Hkv, NB=600, D=128):
     """Sequences of a random fork tree (roots, children, grandchildren), built
     with the oracle's block manager, in the order they were made: sharing of
     leading blocks at many depths, private tails of random length."""
@@ -217,7 +217,6 @@ def fork_tree_batch(seed, Hq, Hkv, NB=600):
     for i, s in enumerate(seqs):
         bt[i, :len(bm.tables[s])] = bm.tables[s]
     cl = np.array([bm.seq_len(s) for s in seqs], np.int32)
-    D = 128
     g = torch.Generator().manual_seed(seed)
     k = torch.randn(NB, Hkv, 16, D, generator=g).to(torch.bfloat16)
     v = torch.randn(NB, Hkv, 16, D, generator=g).to(torch.bfloat16)
@@ -225,13 +224,14 @@ def fork_tree_batch(seed, Hq, Hkv, NB=600):
     return q, k, v, bt, cl
 
 
+@pytest.mark.parametrize("D", [128, 64])
 @pytest.mark.parametrize("seed", list(range(8)))
-def test_decode_shared_random_fork_trees(pa, seed):
+def test_decode_shared_random_fork_trees(pa, seed, D):
     Hq, Hkv = (8, 8) if seed % 2 == 0 else (8, 2)
-    q, k, v, bt, cl = fork_tree_batch(seed, Hq, Hkv)
+    q, k, v, bt, cl = fork_tree_batch(seed, Hq, Hkv, D=D)
     B = len(cl)
     bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)   # noqa: E731
-    expect = oracle.decode(bits(q), bits(k), bits(v), bt, cl, 1 / np.sqrt(128))
+    expect = oracle.decode(bits(q), bits(k), bits(v), bt, cl, 1 / np.sqrt(D))
     G = Hq // Hkv
     dev = torch.device("cuda")
     args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
@@ -240,7 +240,7 @@ def test_decode_shared_random_fork_trees(pa, seed):
         gs, sh = pa.shared_groups(bt, cl, max_group)
         gs_d, sh_d = torch.from_numpy(gs).to(dev), torch.from_numpy(sh).to(dev)
         assert pa.check_groups(gs_d, sh_d, args[3], args[4], max_group) == 0
-        out = pa.decode_shared(*args, gs_d, sh_d, 1 / np.sqrt(128), int(cl.max()), max_group,
+        out = pa.decode_shared(*args, gs_d, sh_d, 1 / np.sqrt(D), int(cl.max()), max_group,
                                int(sh.max()), partition=partition, shared_kv=True,
                                groups_overlap=True)
         torch.cuda.synchronize()

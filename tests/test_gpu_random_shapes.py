@@ -49,7 +49,7 @@ def draw_cases(per_kind, seed):
     return cases
 
 
-@pytest.mark.parametrize("spec,partition", draw_cases(8, 2024))
+@pytest.mark.parametrize("spec,partition", draw_cases(12, 2024))
 def test_random_shape_matches_oracle(pa, spec, partition):
     say(f"[random shape] {spec.name} partition={partition}")
     st = Step(spec, poison=True)
