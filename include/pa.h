@@ -344,9 +344,10 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
  *                at most context_lens[s]; the members' block_tables agree on
  *                the first S_s / bs entries (0 for a sequence that shares
  *                nothing)
- *   max_group    host bound on the group sizes (groups of more than 16 / (Hq /
- *                Hkv) members run on the chunk kernel, whose waves share each
- *                block through LDS)
+ *   max_group    host bound on the group sizes (in bf16, groups of more than
+ *                16 / (Hq / Hkv) members run on the chunk kernel, whose waves
+ *                share each block through LDS; in fp32, one workgroup per 16
+ *                (member, query head) columns)
  *   max_shared   host bound on every S_s (a multiple of bs, <= max_ctx)
  *   partition    tokens per partition of the shared part (0 = one partition;
  *                else a positive multiple of bs); each sequence's own tokens
@@ -357,14 +358,16 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
  *   flags        PA_KV_SHARED (blocks past the shared part read by several
  *                sequences) and/or PA_KV_SHARED_GROUPS (shared parts of
  *                different groups overlap); other bits give PA_EINVAL
- * Other arguments and error rows as pa_decode. Two launches: the shared part
+ * Other arguments and error rows as pa_decode. In bf16, when the shared part
+ * is one partition and a group's columns fit one 16-column tile, one launch:
+ * each group's workgroup reads its shared blocks, then every member's own
+ * blocks (the workspace goes unused). Otherwise two launches: the shared part
  * of every group (one read of its blocks for all members' query heads, on
  * the matrix cores, into the workspace), then every sequence's own tokens,
- * merged with its shared part into the final row. Supported for bf16 with
- * Hq / Hkv <= 16 (else PA_EUNSUPPORTED). A shared length that is
+ * merged with its shared part into the final row. Supported for bf16 and
+ * fp32 with Hq / Hkv <= 16 (else PA_EUNSUPPORTED). A shared length that is
  * negative, not a multiple of bs or beyond the table gives that sequence an
- * all-NaN
- * row (the group pass takes the first member's, so a bad one there gives the
+ * all-NaN row (the group pass takes the first member's, so a bad one there gives the
  * whole group NaN rows). Member tables that disagree on the shared entries
  * are not detected (the group's first member's blocks are used for all);
  * members whose shared lengths differ get undefined rows (no read leaves the

@@ -10,6 +10,11 @@
 // sequence) serves a tile of the kv head's (query row, head) columns, so a
 // kv head's K/V crosses the memory path once per 16 columns instead of once
 // per column. The products are fp32 throughout (no operand is rounded).
+// It also runs the two passes of shared-prefix decode in fp32 (a8q9.cn,
+// section 3: sharers point at the same blocks): the group pass (work item =
+// a group, columns = its members' query heads, the shared blocks read once
+// through the first member's table) and the tail pass (each sequence's
+// blocks past its shared ones, merged with the group pass's partials).
 //
 // Layouts (wave64; lane = 16 * rg + col, rg = lane / 16, col = lane % 16).
 // v_mfma_f32_16x16x4_f32: A (16 x 4) lane holds A[col][rg], B (4 x 16) lane
@@ -81,7 +86,8 @@ void decode_mfma_f32_kernel(DecodeParams P) {
   const int tile = gp.x % P.n_tiles;  // 16-column tile of this kv head's (row, head) pairs
   const int s = gp.z;
 
-  const int32_t* bt_row = P.block_tables + (size_t)s * P.MB;
+  const ItemStart is = item_start(P, s);
+  const int32_t* bt_row = P.block_tables + (size_t)is.trow * P.MB;
   const int bpp = P.partition / kBlock;  // blocks per partition (0: no split)
   const int blk_begin = p * bpp;
   constexpr int kStride = NW;  // wave w takes blocks first, first + NW, ...
@@ -134,14 +140,15 @@ void decode_mfma_f32_kernel(DecodeParams P) {
   const int ctx = sr.row_ctx((c_end - 1) / P.G);  // last column's row: the longest
   const int nblk = (ctx + kBlock - 1) / kBlock;
   const int blk_end = bpp > 0 ? min(nblk, blk_begin + bpp) : nblk;
-  const int nparts_s = bpp > 0 ? (nblk + bpp - 1) / bpp : (nblk > 0 ? 1 : 0);
+  const int span = nblk - is.start_blk;  // blocks this pass reads (tail pass: past the shared ones)
+  const int nparts_s = bpp > 0 ? (span + bpp - 1) / bpp : (span > 0 ? 1 : 0);
   if (p >= max(nparts_s, 1)) return;  // partition past the tile's longest context
 
   float m = -INFINITY, lsum = 0.0f;
   f32x4_t acc[kTiles];
 #pragma unroll
   for (int e = 0; e < kTiles; ++e) acc[e] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  bool bad = sr.bad;  // the whole tile (wave-uniform)
+  bool bad = sr.bad || is.bad || is.start_blk * kBlock > ctx;  // the whole tile (wave-uniform)
 
   const char* kbase = reinterpret_cast<const char*>(P.k_cache);
   const char* vbase = reinterpret_cast<const char*>(P.v_cache);
@@ -228,9 +235,11 @@ void decode_mfma_f32_kernel(DecodeParams P) {
   // This wave's blocks: first + k * kStride, k < nk, through a ring of DEPTH tiles.
   {
     const int nk = first < blk_end ? (blk_end - first + kStride - 1) / kStride : 0;
+    // tail pass: skip this wave's blocks inside the shared part
+    const int k0 = is.start_blk > first ? (is.start_blk - first + kStride - 1) / kStride : 0;
     uint4 kb[DEPTH][kPieces], vb[DEPTH][kPieces];
     block_pipeline<DEPTH>(
-        bt_row, first, kStride, 0, nk, lane, ids0,
+        bt_row, first, kStride, k0, nk, lane, ids0,
         [&](int d, int b, int k, bool exists) {
           load(kb[d], vb[d], b, first + k * kStride, exists);
         },
@@ -274,7 +283,7 @@ void decode_mfma_f32_kernel(DecodeParams P) {
     const int h = g * P.G + c % P.G;
     // Partitions of this column's own context: with one, partition 0 writes
     // the final row; with several, each writes its partial.
-    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock;
+    const int cblk = (sr.row_ctx(i) + kBlock - 1) / kBlock - is.start_blk;
     const int np = bpp > 0 ? (cblk + bpp - 1) / bpp : 1;
     if (np <= 1 ? p != 0 : p >= np) continue;
     float M = sm_m[0][qq];
@@ -292,8 +301,13 @@ void decode_mfma_f32_kernel(DecodeParams P) {
       for (int e = 0; e < 8; ++e) ov[e] += sm_o[v][qq][8 * ch + e] * sc;
     }
     const size_t row = (size_t)(sr.first + i);
-    // one of several partitions: the unnormalised fp32 row and its (m, l)
-    const bool to_partial = np > 1;
+    // One of several partitions, or the group pass of a shared prefix: the
+    // unnormalised fp32 row and its (m, l). Else the final row (the tail pass
+    // first folds in the group pass's partials of the row).
+    const bool to_partial = np > 1 || P.always_partial;
+    if (!to_partial && P.tail_pass)
+      merge_shared_partials<float, 8>(P, is.bad ? 0 : is.start_blk * kBlock, row, h, 8 * ch, D, M,
+                                      L, ov);
     const float mul = to_partial ? 1.0f : (L > 0.0f ? 1.0f / L : 0.0f);  // empty context: zeros
     float res[8];
 #pragma unroll
@@ -303,9 +317,9 @@ void decode_mfma_f32_kernel(DecodeParams P) {
     const uint4 hi = make_uint4(__float_as_uint(res[4]), __float_as_uint(res[5]),
                                 __float_as_uint(res[6]), __float_as_uint(res[7]));
     if (to_partial) {
-      const size_t part = part_slot(P, row, h, p);
-      store_part16(P, row, h, p, 4, 32 * ch, lo);
-      store_part16(P, row, h, p, 4, 32 * ch + 16, hi);
+      const size_t part = part_slot(P, row, h, P.part_base + p);
+      store_part16(P, row, h, P.part_base + p, 4, 32 * ch, lo);
+      store_part16(P, row, h, P.part_base + p, 4, 32 * ch + 16, hi);
       if (ch == 0) {
         P.ws_ml[2 * part] = any_bad ? 0.0f : M;
         P.ws_ml[2 * part + 1] = any_bad ? nan : L;
@@ -319,10 +333,11 @@ void decode_mfma_f32_kernel(DecodeParams P) {
 }
 
 // fp32 I/O with several columns per kv head (grouped heads, or several query
-// rows): one workgroup per 16-column tile; plain decode and multi-query calls
-// only (the shared-prefix passes are bf16).
+// rows): one workgroup per 16-column tile; decode, multi-query, and the group
+// and tail passes of shared-prefix decode (not its one-pass form, which is
+// bf16 only).
 hipError_t launch_decode_mfma_f32(const DecodeParams& p, hipStream_t stream) {
-  if (p.group_start || p.tail_pass || p.fold_tails || p.always_partial) return hipErrorInvalidValue;
+  if (p.fold_tails) return hipErrorInvalidValue;
   constexpr int DEPTH = PA_MFMA32_DEPTH;
   auto go = [&](auto d, auto nw) {
     constexpr int HD = decltype(d)::value;
@@ -337,8 +352,9 @@ hipError_t launch_decode_mfma_f32(const DecodeParams& p, hipStream_t stream) {
   };
   auto by_waves = [&](auto d) {
     // A whole context per workgroup: more waves, each with a longer share of
-    // its blocks. Split contexts (a partition's few blocks): fewer.
-    if (p.pass_parts == 1)
+    // its blocks. Split contexts (a partition's few blocks) and the tail
+    // pass (a sequence's own blocks): fewer.
+    if (p.pass_parts == 1 && !p.tail_pass)
       go(d, std::integral_constant<int, PA_MFMA32_WAVES_UNSPLIT>{});
     else
       go(d, std::integral_constant<int, PA_MFMA32_WAVES>{});

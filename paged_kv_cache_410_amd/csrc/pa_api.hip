@@ -389,12 +389,13 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   if (max_shared > max_ctx) return PA_EINVAL;
   if (bs != kBs) return bs > 0 ? PA_EUNSUPPORTED : PA_EINVAL;
   if (D != 64 && D != 128) return PA_EUNSUPPORTED;
-  // the group pass runs on the bf16 matrix-core kernels: the decode kernel
-  // for one 16-column tile of (member, query head) pairs per kv head, the
-  // chunk kernel for more; the tail pass takes one tile of a sequence's query
-  // heads (G <= 16)
+  // the group pass runs on the matrix-core kernels: in bf16 the decode kernel
+  // for one 16-column tile of (member, query head) pairs per kv head and the
+  // chunk kernel for more, in fp32 the fp32 kernel (one workgroup per tile);
+  // the tail pass takes one tile of a sequence's query heads (G <= 16)
   const int32_t G = Hq / Hkv;
-  if (dt != PA_BF16 || G > 16) return PA_EUNSUPPORTED;
+  if (G > 16) return PA_EUNSUPPORTED;
+  const bool f32 = dt == PA_F32;
   if (B > kMaxGridYZ || n_groups > kMaxGridYZ || max_group > kMaxGridYZ) return PA_EUNSUPPORTED;
   const int64_t group_tiles = ((int64_t)max_group * G + 15) / 16;
   if ((int64_t)Hkv * group_tiles > INT32_MAX) return PA_EUNSUPPORTED;
@@ -441,8 +442,8 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   // One partition of the shared part and one column tile per kv head: a
   // single pass, each group's workgroup reading its shared blocks and then
   // every member's own blocks, writing the final rows (the workspace goes
-  // unused).
-  if (PA_FOLD_TAILS && nps <= 1 && group_tiles == 1) {
+  // unused). bf16 only.
+  if (PA_FOLD_TAILS && !f32 && nps <= 1 && group_tiles == 1) {
     pa::DecodeParams g = p;
     g.group_start = group_start;
     g.fold_tails = 1;
@@ -463,13 +464,15 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
     g.shared_kv = (flags & PA_KV_SHARED_GROUPS) ? 1 : 0;
     g.max_q = max_group;
     g.n_tiles = (int32_t)group_tiles;
-    g.part_f32 = group_tiles > 1;  // the chunk kernel writes fp32 partials
+    g.part_f32 = f32 || group_tiles > 1;  // fp32 rows: fp32 I/O, or the chunk kernel's
     g.partition = nps > 1 ? partition : 0;
     g.part_base = 0;
     g.always_partial = 1;
     g.pass_parts = (int32_t)nps;
     g.pass_items = n_groups;
-    if (pa::launch_decode_mfma(g, stream) != hipSuccess) return PA_EHIP;
+    if ((f32 ? pa::launch_decode_mfma_f32(g, stream) : pa::launch_decode_mfma(g, stream)) !=
+        hipSuccess)
+      return PA_EHIP;
   }
   // 2. tail pass: each sequence's own tokens past its shared ones, merged
   //    with its row's group-pass partials into the final row
@@ -478,14 +481,14 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   t.shared_partition = nps > 1 ? partition : 0;
   t.max_q = 1;
   t.n_tiles = 1;
-  t.part_f32 = group_tiles > 1;  // as the group pass wrote them
+  t.part_f32 = f32 || group_tiles > 1;  // as the group pass wrote them
   t.partition = 0;
   t.pass_parts = 1;
   t.pass_items = B;
-  const bool mfma = G >= 2;  // bf16 here
-  if ((mfma ? pa::launch_decode_mfma(t, stream) : pa::launch_decode_valu(t, dt, D, stream)) !=
-      hipSuccess)
-    return PA_EHIP;
+  const hipError_t e = G == 1 ? pa::launch_decode_valu(t, dt, D, stream)
+                       : f32  ? pa::launch_decode_mfma_f32(t, stream)
+                              : pa::launch_decode_mfma(t, stream);
+  if (e != hipSuccess) return PA_EHIP;
   return PA_OK;
 }
 

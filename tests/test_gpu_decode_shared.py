@@ -43,7 +43,8 @@ def run_shared(pa, st, gs, sh, mg, partition, context_lens=None):
 
 @pytest.mark.parametrize("name", ["cow_small", "cow_gqa", "prefix_small", "mha_bf16", "gqa8",
                                   "long_mha", "cow_small_d64", "cow_gqa_d64", "prefix_small_d64",
-                                  "mha_bf16_d64"])
+                                  "mha_bf16_d64", "cow_small_f32", "cow_gqa_f32",
+                                  "prefix_small_f32_d64", "gqa_f32", "mha_f32_d128"])
 @pytest.mark.parametrize("partition", [0, 16, 48, 512])
 def test_decode_shared_matches_oracle(pa, name, partition):
     spec = SMALL[name]
@@ -144,7 +145,8 @@ def test_decode_shared_full_config_whole_output(pa, name):
     assert err <= TOL[spec.dtype]
 
 
-@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa", "cow_gqa_d64"])
+@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa", "cow_gqa_d64",
+                                  "cow_gqa_f32"])
 def test_decode_shared_cache_flags_give_identical_bits(pa, name):
     """PA_KV_SHARED and PA_KV_SHARED_GROUPS change how tiles are cached, never
     the result."""
@@ -190,7 +192,7 @@ def test_check_groups_counts_violations(pa):
         assert n == e, (n, e)
 
 
-def fork_tree_batch(seed, Hq, Hkv, NB=600, D=128):
+def fork_tree_batch(seed, Hq, Hkv, NB=600, D=128, dtype="bf16"):
     """Sequences of a random fork tree (roots, children, grandchildren), built
     with the oracle's block manager, in the order they were made: sharing of
     leading blocks at many depths, private tails of random length."""
@@ -218,20 +220,28 @@ def fork_tree_batch(seed, Hq, Hkv, NB=600, D=128):
         bt[i, :len(bm.tables[s])] = bm.tables[s]
     cl = np.array([bm.seq_len(s) for s in seqs], np.int32)
     g = torch.Generator().manual_seed(seed)
-    k = torch.randn(NB, Hkv, 16, D, generator=g).to(torch.bfloat16)
-    v = torch.randn(NB, Hkv, 16, D, generator=g).to(torch.bfloat16)
-    q = torch.randn(len(seqs), Hq, D, generator=g).to(torch.bfloat16)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = torch.randn(NB, Hkv, 16, D, generator=g).to(dt)
+    v = torch.randn(NB, Hkv, 16, D, generator=g).to(dt)
+    q = torch.randn(len(seqs), Hq, D, generator=g).to(dt)
     return q, k, v, bt, cl
 
 
-@pytest.mark.parametrize("D", [128, 64])
+def host_view(t):
+    """A pool or query tensor as the oracle takes it: bf16 as raw uint16
+    bits, fp32 as values."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
 @pytest.mark.parametrize("seed", list(range(8)))
-def test_decode_shared_random_fork_trees(pa, seed, D):
+def test_decode_shared_random_fork_trees(pa, seed, dtype, D):
     Hq, Hkv = (8, 8) if seed % 2 == 0 else (8, 2)
-    q, k, v, bt, cl = fork_tree_batch(seed, Hq, Hkv, D=D)
+    q, k, v, bt, cl = fork_tree_batch(seed, Hq, Hkv, D=D, dtype=dtype)
     B = len(cl)
-    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)   # noqa: E731
-    expect = oracle.decode(bits(q), bits(k), bits(v), bt, cl, 1 / np.sqrt(D))
+    expect = oracle.decode(host_view(q), host_view(k), host_view(v), bt, cl, 1 / np.sqrt(D))
     G = Hq // Hkv
     dev = torch.device("cuda")
     args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
@@ -245,20 +255,21 @@ def test_decode_shared_random_fork_trees(pa, seed, D):
                                groups_overlap=True)
         torch.cuda.synchronize()
         err = max_abs_err(out, expect)
-        say(f"[decode_shared fork tree] seed={seed} B={B} groups={len(gs) - 1} "
+        say(f"[decode_shared fork tree] {dtype} D{D} seed={seed} B={B} groups={len(gs) - 1} "
             f"shared={sorted(set(sh.tolist()))[:6]} max_group={max_group} err={err:.2e}")
-        assert err <= TOL["bf16"]
+        assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("seed", [11, 12, 13])
 @pytest.mark.parametrize("max_group", [3, 4, 8])
-def test_decode_shared_groups_past_one_tile(pa, seed, max_group):
-    """Groups whose members x query heads exceed 16 columns per kv head run
-    their shared part on the chunk kernel (8 query heads per kv head: 24, 32
-    and 64 columns)."""
-    q, k, v, bt, cl = fork_tree_batch(seed, 16, 2)
-    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)   # noqa: E731
-    expect = oracle.decode(bits(q), bits(k), bits(v), bt, cl, 1 / np.sqrt(128))
+def test_decode_shared_groups_past_one_tile(pa, seed, max_group, dtype):
+    """Groups whose members x query heads exceed 16 columns per kv head (8
+    query heads per kv head: 24, 32 and 64 columns) run their shared part on
+    the chunk kernel in bf16, on one fp32 matrix-core workgroup per 16-column
+    tile in fp32."""
+    q, k, v, bt, cl = fork_tree_batch(seed, 16, 2, dtype=dtype)
+    expect = oracle.decode(host_view(q), host_view(k), host_view(v), bt, cl, 1 / np.sqrt(128))
     dev = torch.device("cuda")
     gs, sh = pa.shared_groups(bt, cl, max_group)
     args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
@@ -269,10 +280,10 @@ def test_decode_shared_groups_past_one_tile(pa, seed, max_group):
                                partition=partition)
         torch.cuda.synchronize()
         err = max_abs_err(out, expect)
-        say(f"[decode_shared chunk groups] seed={seed} max_group={max_group} "
+        say(f"[decode_shared wide groups] {dtype} seed={seed} max_group={max_group} "
             f"sizes={np.diff(gs).tolist()} partition={partition} err={err:.2e}")
         assert np.all(np.isfinite(out.float().cpu().numpy()))
-        assert err <= TOL["bf16"]
+        assert err <= TOL[dtype]
 
 
 def test_decode_shared_malformed_groups_stay_in_bounds(pa):

@@ -69,6 +69,18 @@ SMALL = {
                         cow=dict(prompts=2, samples=3, prompt_len=64, r_max=15, tail_lo=1,
                                  tail_hi=30)),
     "gqa32_d64": Spec("gqa32_d64", "bf16", 2, 32, 1, 64, seed=53, lengths=("uniform", 1, 500)),
+    # the sharing workloads in fp32: one query head per kv head (the vector
+    # kernel's tail pass), 4 and 2 heads per kv head (the fp32 matrix-core
+    # kernel's group and tail passes)
+    "cow_small_f32": Spec("cow_small_f32", "f32", 8, 4, 4, 128, seed=54, lengths=("cow",),
+                          cow=dict(prompts=2, samples=4, prompt_len=96, r_max=15, tail_lo=1,
+                                   tail_hi=40)),
+    "cow_gqa_f32": Spec("cow_gqa_f32", "f32", 6, 8, 2, 128, seed=55, lengths=("cow",),
+                        cow=dict(prompts=2, samples=3, prompt_len=64, r_max=15, tail_lo=1,
+                                 tail_hi=30)),
+    "prefix_small_f32_d64": Spec("prefix_small_f32_d64", "f32", 6, 4, 2, 64, seed=56,
+                                 lengths=("prefix",),
+                                 prefix=dict(shared=80, tail_lo=1, tail_hi=40, vocab=50)),
     # fp32 grouped heads on the matrix cores (v_mfma_f32_16x16x4_f32): 8 heads
     # per kv head; a full 16-column tile at head_dim 64; two tiles per kv head
     # (32 heads); unsplit rows longer than one 64-block id chunk per wave
