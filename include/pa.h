@@ -364,8 +364,9 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache,
  * blocks (the workspace goes unused). Otherwise two launches: the shared part
  * of every group (one read of its blocks for all members' query heads, on
  * the matrix cores, into the workspace), then every sequence's own tokens,
- * merged with its shared part into the final row. Supported for bf16 and
- * fp32 with Hq / Hkv <= 16 (else PA_EUNSUPPORTED). A shared length that is
+ * merged with its shared part into the final row (in bf16 with more than 16
+ * query heads per kv head, one query head per workgroup). bf16 and fp32.
+ * A shared length that is
  * negative, not a multiple of bs or beyond the table gives that sequence an
  * all-NaN row (the group pass takes the first member's, so a bad one there gives the
  * whole group NaN rows). Member tables that disagree on the shared entries

@@ -391,10 +391,8 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   if (D != 64 && D != 128) return PA_EUNSUPPORTED;
   // the group pass runs on the matrix-core kernels: in bf16 the decode kernel
   // for one 16-column tile of (member, query head) pairs per kv head and the
-  // chunk kernel for more, in fp32 the fp32 kernel (one workgroup per tile);
-  // the tail pass takes one tile of a sequence's query heads (G <= 16)
+  // chunk kernel for more, in fp32 the fp32 kernel (one workgroup per tile)
   const int32_t G = Hq / Hkv;
-  if (G > 16) return PA_EUNSUPPORTED;
   const bool f32 = dt == PA_F32;
   if (B > kMaxGridYZ || n_groups > kMaxGridYZ || max_group > kMaxGridYZ) return PA_EUNSUPPORTED;
   const int64_t group_tiles = ((int64_t)max_group * G + 15) / 16;
@@ -480,14 +478,19 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   t.tail_pass = 1;
   t.shared_partition = nps > 1 ? partition : 0;
   t.max_q = 1;
-  t.n_tiles = 1;
+  t.n_tiles = (G + 15) / 16;
   t.part_f32 = f32 || group_tiles > 1;  // as the group pass wrote them
   t.partition = 0;
   t.pass_parts = 1;
   t.pass_items = B;
-  const hipError_t e = G == 1 ? pa::launch_decode_valu(t, dt, D, stream)
-                       : f32  ? pa::launch_decode_mfma_f32(t, stream)
-                              : pa::launch_decode_mfma(t, stream);
+  // The tail pass: one query head per workgroup on the vector kernel for one
+  // head per kv head; else a kv head's query heads on the matrix cores, 16
+  // per workgroup in fp32, at most 16 in bf16 (past 16, bf16 goes to the
+  // vector kernel: the decode kernel takes one tile per kv head)
+  const bool valu_tail = G == 1 || (!f32 && G > 16);
+  const hipError_t e = valu_tail ? pa::launch_decode_valu(t, dt, D, stream)
+                       : f32     ? pa::launch_decode_mfma_f32(t, stream)
+                                 : pa::launch_decode_mfma(t, stream);
   if (e != hipSuccess) return PA_EHIP;
   return PA_OK;
 }

@@ -485,8 +485,7 @@ def shared_args(**kw):
     (dict(gs=None), -1), (dict(sh=None), -1), (dict(q=None), -1), (dict(ng=0), -1),
     (dict(mg=0), -1), (dict(max_shared=24), -1), (dict(max_shared=256), -1),
     (dict(partition=8), -1), (dict(Hq=6, Hkv=4), -1), (dict(scale=float("nan")), -1),
-    (dict(dt=7), -1), (dict(D=96), -2), (dict(Hq=32, Hkv=1, mg=1), -2),
-    (dict(Hq=32, Hkv=1, mg=1, dt=0), -2), (dict(bs=32), -2),
+    (dict(dt=7), -1), (dict(D=96), -2), (dict(mg=70000), -2), (dict(bs=32), -2),
     (dict(ws=None), -3), (dict(ws_bytes=100), -3), (dict(ws=FAKE + 16), -1),
     (dict(flags=4), -1), (dict(B=70000), -2),
 ])

@@ -286,6 +286,31 @@ def test_decode_shared_groups_past_one_tile(pa, seed, max_group, dtype):
         assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Hq,D", [(32, 128), (48, 64)])
+@pytest.mark.parametrize("seed", [31, 32])
+def test_decode_shared_more_than_16_heads_per_kv_head(pa, seed, Hq, D, dtype):
+    """One kv head for 32 or 48 query heads (multi-query attention): the
+    group pass takes 2 or 3 column tiles per member; the tail pass takes the
+    vector kernel in bf16 and 2 or 3 fp32 matrix-core tiles in fp32."""
+    q, k, v, bt, cl = fork_tree_batch(seed, Hq, 1, D=D, dtype=dtype)
+    expect = oracle.decode(host_view(q), host_view(k), host_view(v), bt, cl, 1 / np.sqrt(D))
+    dev = torch.device("cuda")
+    args = [t.to(dev) for t in (q, k, v)] + [torch.from_numpy(bt).to(dev),
+                                              torch.from_numpy(cl).to(dev)]
+    for max_group, partition in ((1, 0), (3, 32), (4, None)):
+        gs, sh = pa.shared_groups(bt, cl, max_group)
+        out = pa.decode_shared(*args, torch.from_numpy(gs).to(dev), torch.from_numpy(sh).to(dev),
+                               1 / np.sqrt(D), int(cl.max()), max_group, int(sh.max()),
+                               partition=partition)
+        torch.cuda.synchronize()
+        err = max_abs_err(out, expect)
+        say(f"[decode_shared {Hq}/1 heads] {dtype} D{D} seed={seed} max_group={max_group} "
+            f"partition={partition} err={err:.2e}")
+        assert np.all(np.isfinite(out.float().cpu().numpy()))
+        assert err <= TOL[dtype]
+
+
 def test_decode_shared_malformed_groups_stay_in_bounds(pa):
     """Group bounds outside the batch: the call completes (every read stays
     inside its buffer), and the rows of the intact groups are those of a
