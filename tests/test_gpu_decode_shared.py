@@ -75,10 +75,11 @@ def test_decode_shared_smaller_groups(pa, max_group):
     assert max_abs_err(out, st.expect) <= TOL["bf16"]
 
 
-def test_decode_shared_empty_tails_and_contexts(pa):
+@pytest.mark.parametrize("name", ["cow_small", "cow_small_f32", "cow_gqa_f32"])
+def test_decode_shared_empty_tails_and_contexts(pa, name):
     """A sequence whose whole context is shared (empty own part), and an empty
     sequence in a group of its own."""
-    st = Step(SMALL["cow_small"], poison=True, oracle_full=False)
+    st = Step(SMALL[name], poison=True, oracle_full=False)
     st.run_cache_ops(pa)
     gs, sh, mg = groups_of(pa, st)
     cl = st.tb.context_lens.copy()
@@ -97,11 +98,12 @@ def test_decode_shared_empty_tails_and_contexts(pa):
     o = out.float().cpu().numpy()
     assert np.count_nonzero(o[last]) == 0
     assert np.all(np.isfinite(o))
-    assert float(np.max(np.abs(o - expect))) <= TOL["bf16"]
+    assert float(np.max(np.abs(o - expect))) <= TOL[st.spec.dtype]
 
 
-def test_decode_shared_bad_shared_length_poisons_only_its_row(pa):
-    st = Step(SMALL["cow_small"], oracle_full=False)
+@pytest.mark.parametrize("name", ["cow_small", "cow_small_f32", "cow_gqa_f32"])
+def test_decode_shared_bad_shared_length_poisons_only_its_row(pa, name):
+    st = Step(SMALL[name], oracle_full=False)
     st.run_cache_ops(pa)
     gs, sh, mg = groups_of(pa, st)
     good = run_shared(pa, st, gs, sh, mg, 0).float().cpu()
@@ -311,11 +313,12 @@ def test_decode_shared_more_than_16_heads_per_kv_head(pa, seed, Hq, D, dtype):
         assert err <= TOL[dtype]
 
 
-def test_decode_shared_malformed_groups_stay_in_bounds(pa):
+@pytest.mark.parametrize("dtype,Hkv", [("bf16", 8), ("f32", 8), ("f32", 2)])
+def test_decode_shared_malformed_groups_stay_in_bounds(pa, dtype, Hkv):
     """Group bounds outside the batch: the call completes (every read stays
     inside its buffer), and the rows of the intact groups are those of a
     well-formed call; the affected members' rows are undefined."""
-    q, k, v, bt, cl = fork_tree_batch(5, 8, 8)
+    q, k, v, bt, cl = fork_tree_batch(5, 8, Hkv, dtype=dtype)
     gs, sh = pa.shared_groups(bt, cl, 4)
     assert len(gs) - 1 >= 3
     dev = torch.device("cuda")
@@ -339,7 +342,8 @@ def test_decode_shared_malformed_groups_stay_in_bounds(pa):
     assert torch.equal(out[intact], good[intact])
 
 
-@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa", "prefix_small_d64"])
+@pytest.mark.parametrize("name", ["cow_small", "prefix_small", "cow_gqa", "prefix_small_d64",
+                                  "cow_gqa_f32", "prefix_small_f32_d64"])
 def test_decode_shared_permutation_invariant_and_deterministic(pa, name):
     """The blocks relabelled by a random permutation of the pool (pools and
     tables alike) give bitwise the same outputs, as does a second run:
