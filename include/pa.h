@@ -239,11 +239,11 @@ int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv,
  * max_ctx <= partition, otherwise room for one partial result per (query
  * row, query head, partition): an fp32 (max, sum) pair of the partition's
  * online-softmax state, and a row of D elements. The row is the state's
- * unnormalised output in fp32 for fp32 I/O and from the chunk kernel (bf16,
- * more than 16 query columns per kv head), else an fp16 row of an
+ * unnormalised output in fp32 for fp32 I/O; for bf16 I/O, an fp16 row of an
  * equivalent rescaled state (the row divided by its sum times a power of
- * two, the pair adjusted to match). Sized as (8 + 4 D) bytes per partial, plus alignment,
- * for both dtypes. The contents are scratch: nothing is kept between calls.
+ * two, the pair adjusted to match). Sized as (8 + 4 D) bytes per partial,
+ * plus alignment, for both dtypes. The contents are scratch: nothing is kept
+ * between calls.
  */
 size_t pa_decode_workspace_bytes(int32_t rows, int32_t Hq, int32_t D,
                                  int32_t max_ctx, int32_t partition);

@@ -481,10 +481,21 @@ void chunk_mfma_kernel(DecodeParams P) {
   if (!has_cols) return;
   // Each tile's columns hold their whole state for this partition: lane
   // (rg, col) writes dims 16 et + 4 rg + 0..3 of its column, from acc[t][et].
+  // A partial goes out as an fp16 row of an equivalent rescaled state
+  // (part_scale_f16), as the decode kernels write theirs.
   const float nan = __builtin_nanf("");
+  const bool split = bpp > 0 || P.always_partial;  // some column may write a partial
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const float l_col = rows_sum(lsum[t]);  // per column: sum over the 4 row groups
+    float amax = 0.0f;                      // per column: the largest |o| (partials only)
+    if (split) {
+#pragma unroll
+      for (int et = 0; et < kE; ++et)
+        amax = vmax(amax, vmax(vmax(fabsf(acc[t][et][0]), fabsf(acc[t][et][1])),
+                               vmax(fabsf(acc[t][et][2]), fabsf(acc[t][et][3]))));
+      amax = rows_max(amax);
+    }
     if (!col_ok[t]) continue;
     const int i = gc[t] / P.G;
     const int h = g * P.G + gc[t] % P.G;
@@ -494,15 +505,17 @@ void chunk_mfma_kernel(DecodeParams P) {
     const size_t orow = (size_t)(sr.first + i) * P.Hq + h;
     if (np > 1 || P.always_partial) {
       const size_t part = part_slot(P, sr.first + i, h, P.part_base + p);
-      float* dst = static_cast<float*>(P.ws_o) + part * D;  // fp32 rows (part_f32)
+      const PartScale ps = part_scale_f16(m[t] == kNoRef ? -INFINITY : m[t], l_col, amax);
 #pragma unroll
-      for (int et = 0; et < kE; ++et)
-        *reinterpret_cast<float4*>(dst + 16 * et + 4 * rg) =
-            bad ? make_float4(nan, nan, nan, nan)
-                : make_float4(acc[t][et][0], acc[t][et][1], acc[t][et][2], acc[t][et][3]);
+      for (int et = 0; et < kE; ++et) {
+        uint2 u = make_uint2(pack_f16x2(acc[t][et][0] * ps.mul, acc[t][et][1] * ps.mul),
+                             pack_f16x2(acc[t][et][2] * ps.mul, acc[t][et][3] * ps.mul));
+        if (bad) u = make_uint2(0x7e007e00u, 0x7e007e00u);  // NaN
+        store_part8(P, sr.first + i, h, P.part_base + p, 2, (16 * et + 4 * rg) * 2, u);
+      }
       if (rg == 0) {
-        P.ws_ml[2 * part] = bad ? 0.0f : (m[t] == kNoRef ? -INFINITY : m[t]);
-        P.ws_ml[2 * part + 1] = bad ? nan : l_col;
+        P.ws_ml[2 * part] = bad ? 0.0f : ps.m;
+        P.ws_ml[2 * part + 1] = bad ? nan : ps.l;
       }
     } else {
       const float inv = l_col > 0.0f ? 1.0f / l_col : 0.0f;
@@ -520,10 +533,12 @@ void chunk_mfma_kernel(DecodeParams P) {
 }
 
 // Waves per workgroup and column tiles per wave. Up to 8 tiles per kv
-// head: one tile per wave, as many waves as tiles (a wave without columns
-// still brings its share of every block). More: two tiles per wave on 4
-// waves, so that every K/V operand read from LDS serves 32 columns (with
-// PA_CHUNK_TILES_PER_WAVE 1, one tile per wave on 8 waves).
+// head: one tile per wave, on 4 waves up to 4 tiles, else on 8 (a wave
+// without columns still brings its share of every block: the GQA batch with
+// 3 new tokens per sequence, 2 tiles per kv head in 512-token partitions,
+// took 4.63 TB/s with 4 waves, 4.55 with 2 and with 8). More: two tiles per
+// wave on 4 waves, so that every K/V operand read from LDS serves 32 columns
+// (with PA_CHUNK_TILES_PER_WAVE 1, one tile per wave on 8 waves).
 hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream) {
   constexpr int R = PA_CHUNK_RING;
   auto go = [&](auto d, auto nw, auto tpw) {
@@ -537,7 +552,7 @@ hipError_t launch_chunk_mfma(const DecodeParams& p, hipStream_t stream) {
   };
   auto by_tiles = [&](auto d) {
     using I = std::integral_constant<int, 1>;
-    if (p.n_tiles <= 2 || PA_CHUNK_MAX_WAVES == 2)
+    if (PA_CHUNK_MAX_WAVES == 2)
       go(d, std::integral_constant<int, 2>{}, I{});
     else if (p.n_tiles <= 4 || PA_CHUNK_MAX_WAVES == 4)
       go(d, std::integral_constant<int, 4>{}, I{});

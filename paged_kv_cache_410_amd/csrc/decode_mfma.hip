@@ -75,6 +75,14 @@
 #ifndef PA_MFMA_TAIL_WAVES
 #define PA_MFMA_TAIL_WAVES 4
 #endif
+// Column tiles per kv head from which a call goes to the chunk kernel; with
+// fewer, one workgroup per tile here (the tiles of a kv head on one XCD). On
+// the GQA batch with 3, 4 or 8 new tokens per sequence (2 or 4 tiles per kv
+// head, 512-token partitions): 4.4-4.6 TB/s on the chunk kernel, 3.3-3.4
+// with 2 tiles and 2.1 with 4 here.
+#ifndef PA_CHUNK_MIN_TILES
+#define PA_CHUNK_MIN_TILES 2
+#endif
 // Minimum waves per SIMD the register allocation must allow.
 #ifndef PA_MFMA_MIN_WAVES
 #define PA_MFMA_MIN_WAVES 3
@@ -115,8 +123,9 @@ void decode_mfma_kernel(DecodeParams P) {
   const int col = lane & 15;
   const int rg = lane >> 4;
 
-  // The launcher sends a kv head with several tiles to the chunk kernel; if
-  // one came here, its tiles would read the same K/V, kept on one XCD.
+  // A kv head with several tiles goes to the chunk kernel unless
+  // PA_CHUNK_MIN_TILES is raised; then its tiles run here, one workgroup
+  // each, kept on one XCD (they read the same K/V).
   const GridPos gp = P.n_tiles > 1 ? grid_pos_grouped(P.n_tiles) : grid_pos();
   const int p = gp.y;
   const int g = gp.x / P.n_tiles;    // kv head
@@ -467,7 +476,7 @@ void decode_mfma_kernel(DecodeParams P) {
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
   // several column tiles per kv head: the chunk kernel, whose waves share
   // each block
-  if (p.n_tiles > 1) return launch_chunk_mfma(p, stream);
+  if (p.n_tiles >= PA_CHUNK_MIN_TILES) return launch_chunk_mfma(p, stream);
   constexpr int DEPTH = PA_MFMA_DEPTH;
   if (p.fold_tails) {
     // group pass with the members' own blocks folded in: the shared blocks'

@@ -33,8 +33,8 @@ __device__ __forceinline__ float wave_max(float x) {
   return rows_max(x);
 }
 
-// T: the output's element type; E: the partial rows' (fp16, or fp32 when
-// P.part_f32), chosen at launch.
+// T: the output's element type; E: the partial rows' (fp16 for bf16 output,
+// fp32 for fp32), chosen at launch.
 template <typename T, typename E, int D>
 __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(DecodeParams P) {
   constexpr int RW = kReduceWaves;
@@ -145,15 +145,12 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, int D, hipStream_t stream) {
   const dim3 grid(p.Hq, p.max_q, p.B), block(kReduceWaves * kWave);
-  // bf16 output: fp16 partial rows, or fp32 ones from the chunk kernel
-  if (dtype == 1 && D == 128 && !p.part_f32)
+  // bf16 output: fp16 partial rows; fp32 output: fp32 rows
+  if (p.part_f32 != (dtype == 0)) return hipErrorInvalidValue;
+  if (dtype == 1 && D == 128)
     hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, _Float16, 128>), grid, block, 0, stream, p);
-  else if (dtype == 1 && D == 128)
-    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, float, 128>), grid, block, 0, stream, p);
-  else if (dtype == 1 && D == 64 && !p.part_f32)
-    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, _Float16, 64>), grid, block, 0, stream, p);
   else if (dtype == 1 && D == 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, float, 64>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<uint16_t, _Float16, 64>), grid, block, 0, stream, p);
   else if (dtype == 0 && D == 128)
     hipLaunchKernelGGL((decode_reduce_kernel<float, float, 128>), grid, block, 0, stream, p);
   else if (dtype == 0 && D == 64)

@@ -310,8 +310,8 @@ pa_status attention(void* out, const void* q, const void* k_cache, const void* v
   const bool mfma = dt == PA_BF16 && several;
   const bool mfma32 = dt == PA_F32 && several;
   if ((mfma || mfma32) && (int64_t)Hkv * p.n_tiles > INT32_MAX) return PA_EUNSUPPORTED;
-  // fp32 I/O, or the chunk kernel (bf16, several tiles)
-  p.part_f32 = dt == PA_F32 || (mfma && p.n_tiles > 1);
+  // partial rows: fp32 for fp32 I/O, scaled fp16 for bf16 (every kernel)
+  p.part_f32 = dt == PA_F32;
   hipError_t err = mfma     ? pa::launch_decode_mfma(p, stream)
                    : mfma32 ? pa::launch_decode_mfma_f32(p, stream)
                             : pa::launch_decode_valu(p, dt, D, stream);
@@ -462,7 +462,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
     g.shared_kv = (flags & PA_KV_SHARED_GROUPS) ? 1 : 0;
     g.max_q = max_group;
     g.n_tiles = (int32_t)group_tiles;
-    g.part_f32 = f32 || group_tiles > 1;  // fp32 rows: fp32 I/O, or the chunk kernel's
+    g.part_f32 = f32;
     g.partition = nps > 1 ? partition : 0;
     g.part_base = 0;
     g.always_partial = 1;
@@ -479,7 +479,7 @@ pa_status pa_decode_shared(void* out, const void* q, const void* k_cache, const 
   t.shared_partition = nps > 1 ? partition : 0;
   t.max_q = 1;
   t.n_tiles = (G + 15) / 16;
-  t.part_f32 = f32 || group_tiles > 1;  // as the group pass wrote them
+  t.part_f32 = f32;  // as the group pass wrote them
   t.partition = 0;
   t.pass_parts = 1;
   t.pass_items = B;

@@ -53,8 +53,7 @@ struct DecodeParams {
   int32_t few_items;            // vector kernel: an unsplit grid with at most 8 items per CU
   int32_t pass_parts;           // grid y of this pass (partitions)
   int32_t pass_items;           // grid z of this pass (sequences, or groups)
-  int32_t part_f32;             // partial rows are fp32: fp32 I/O, or written by the chunk
-                                // kernel (whose registers leave no room for the fp16 epilogue)
+  int32_t part_f32;             // partial rows are fp32 (fp32 I/O), else scaled fp16 (bf16 I/O)
 };
 
 // Slot of partial j of query row `row`, query head h (x2 floats in ws_ml, xD in
@@ -99,6 +98,26 @@ __device__ __forceinline__ void store_part16(const DecodeParams& P, size_t row, 
       __builtin_amdgcn_raw_buffer_store_b128(d, r, o, 0, 0);
   } else {
     st16(base + h * row_bytes + off, v);
+  }
+}
+
+// The same for 8 bytes (the chunk kernel's fp16 rows: a lane holds 4
+// consecutive dims of each 16-dim output tile).
+__device__ __forceinline__ void store_part8(const DecodeParams& P, size_t row, int h, int j,
+                                            int eb, int off, const uint2& v) {
+  const int64_t row_bytes = (int64_t)P.D * eb;
+  char* base = static_cast<char*>(P.ws_o) + part_slot(P, row, 0, j) * row_bytes;
+  if ((int64_t)P.Hq * row_bytes <= INT32_MAX) {
+    const rsrc_t r = make_rsrc(base, (int)(P.Hq * row_bytes));
+    typedef unsigned int u32x2_part_t __attribute__((ext_vector_type(2)));
+    const u32x2_part_t d = __builtin_bit_cast(u32x2_part_t, v);
+    const int o = (int)(h * row_bytes) + off;
+    if (row_bytes == 256)
+      __builtin_amdgcn_raw_buffer_store_b64(d, r, o, 0, PA_PART_STORE_AUX);
+    else
+      __builtin_amdgcn_raw_buffer_store_b64(d, r, o, 0, 0);
+  } else {
+    *reinterpret_cast<uint2*>(base + h * row_bytes + off) = v;
   }
 }
 

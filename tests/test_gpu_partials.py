@@ -8,11 +8,10 @@ range both ways (exact in bf16, and the attention output scales by the same
 power): 2^20 and 2^100 need k > 0 to stay finite, 2^-20 needs k < 0 to stay
 out of fp16's subnormals (fixed spacing 2^-24, a 6% error on rows of size
 2^-20). Every fp16 partial is covered: the vector kernel's (one query head
-per kv head; head_dim 128 and 64), the matrix-core kernel's (grouped heads;
-several tiles per kv head at head_dim 64) and the shared-prefix group pass's
-on that kernel. The chunk kernel (several
-query rows, one and two column tiles per wave; shared-prefix groups wider than
-one tile) writes fp32 partials, which the merges read as such. The output
+per kv head; head_dim 128 and 64), the matrix-core kernel's (grouped heads,
+one tile per kv head), the chunk kernel's (several tiles per kv head: two
+per workgroup up to two tiles per wave, head_dim 128 and 64) and the
+shared-prefix group pass's on both (groups of one tile and wider). The output
 divided by the power must match the oracle's unscaled output to the bf16
 tolerance.
 """
@@ -41,8 +40,8 @@ CASES = {
     "mfma_gqa8": Spec("mfma_gqa8", "bf16", 3, 16, 2, 128, seed=33, lengths=("uniform", 300, 3000)),
     "mfma_gqa8_d64": Spec("mfma_gqa8_d64", "bf16", 3, 16, 2, 64, seed=37,
                           lengths=("uniform", 300, 3000)),
-    # head_dim 64, 3 to 5 rows x 8 heads: two or three tiles per kv head, one
-    # workgroup each on the matrix-core decode kernel (fp16 partials)
+    # head_dim 64, 3 to 5 rows x 8 heads: two or three tiles per kv head on
+    # the chunk kernel (2- or 4-wave workgroups)
     "mfma_d64_tiles": Spec("mfma_d64_tiles", "bf16", 2, 16, 2, 64, seed=47,
                            lengths=("uniform", 300, 1200), chunk=("uniform", 3, 5)),
     # 8 rows x 8 heads: 4 column tiles, one per wave
@@ -51,6 +50,11 @@ CASES = {
     # 64 rows x 8 heads: 32 column tiles, two per wave
     "chunk_tpw2": Spec("chunk_tpw2", "bf16", 2, 16, 2, 128, seed=35,
                        lengths=("uniform", 300, 1200), chunk=("uniform", 64, 64)),
+    # the same at head_dim 64, and 3 rows x 8 heads (two tiles, 2-wave workgroups)
+    "chunk_tpw2_d64": Spec("chunk_tpw2_d64", "bf16", 2, 16, 2, 64, seed=38,
+                           lengths=("uniform", 300, 1200), chunk=("uniform", 64, 64)),
+    "chunk_2tiles": Spec("chunk_2tiles", "bf16", 3, 16, 2, 128, seed=39,
+                         lengths=("uniform", 300, 1500), chunk=("uniform", 3, 4)),
 }
 
 
