@@ -38,9 +38,7 @@ CHUNKS = {
                        chunk=("all",)),
     "mq_single": Spec("mq_single", "bf16", 5, 8, 2, 128, seed=35, lengths=("uniform", 1, 400),
                       chunk=("uniform", 1, 1)),
-    # fp32 (the fp32 matrix-core kernel, one query head per kv head), and
-    # bf16 head_dim 64 past one tile (the matrix-core decode kernel, one
-    # workgroup per tile)
+    # fp32 (the fp32 matrix-core kernel, one query head per kv head)
     "mq_f32": Spec("mq_f32", "f32", 3, 4, 4, 64, seed=36, lengths=("uniform", 1, 300),
                    chunk=("uniform", 1, 12)),
     # fp32 on the matrix cores: up to 48 (row, head) columns per kv head, so
@@ -53,7 +51,7 @@ CHUNKS = {
     "mq_bf16_d64": Spec("mq_bf16_d64", "bf16", 3, 4, 2, 64, seed=37, lengths=("uniform", 1, 300),
                         chunk=("uniform", 1, 9)),
     # head_dim 64 past one tile: 160 to 320 columns per kv head, 10 to 20
-    # workgroups per kv head on the matrix-core decode kernel
+    # tiles on the chunk kernel (128-byte rows, two tiles per wave)
     "mq_gqa8_d64": Spec("mq_gqa8_d64", "bf16", 2, 16, 2, 64, seed=48, lengths=("uniform", 100, 900),
                         chunk=("uniform", 20, 40)),
     # head_dim 64 on the matrix cores: at most 16 (row, head) columns per kv head
@@ -62,7 +60,8 @@ CHUNKS = {
     # unsplit rows longer than one 64-block id chunk per wave
     "mq_long": Spec("mq_long", "bf16", 2, 2, 2, 128, seed=38, lengths=("fixed", [9000, 3000]),
                     chunk=("uniform", 2, 6)),
-    # two 16-column tiles per kv head: the chunk kernel's two-wave shape
+    # one or two 16-column tiles per kv head: the matrix-core decode kernel,
+    # and the chunk kernel's 4-wave shape with waves that only load
     "mq_gqa8_short": Spec("mq_gqa8_short", "bf16", 4, 16, 2, 128, seed=39,
                           lengths=("uniform", 1, 900), chunk=("uniform", 2, 4)),
 }
