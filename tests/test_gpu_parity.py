@@ -383,3 +383,19 @@ def test_decode_at_the_batch_limit(pa, dtype, Hq, Hkv, D):
         expect = oracle.decode(q, k, v, bt, cl, scale)
         assert np.all(got[cl == 0] == 0.0)
         assert max_abs_err(out, expect) <= TOL[dtype], part
+
+
+def test_default_partition_policy(pa):
+    """The library's split choice on this device (256 compute units): no split
+    when (sequence, kv head) workgroups fill the GPU eight times over, or the
+    contexts are short: up to 512 tokens, or up to 2048 with grouped heads
+    (matrix-core kernels); else 512-token partitions."""
+    say("[default partition]")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert pa.default_partition(8 * cus, 8, 8, 128, 32768) == 0        # enough workgroups
+    assert pa.default_partition(4, 8, 8, 128, 512) == 0                # short contexts
+    assert pa.default_partition(26, 40, 40, 128, 560) == 512           # one head per kv head
+    assert pa.default_partition(128, 40, 8, 128, 2048) == 0            # grouped, short
+    assert pa.default_partition(16, 32, 8, 64, 2048) == 0
+    assert pa.default_partition(16, 32, 8, 128, 2049) == 512           # grouped, long
+    assert pa.default_partition(16, 64, 8, 128, 32768) == 512
