@@ -227,9 +227,10 @@ pa_status pa_check_groups(const int32_t* group_start, const int32_t* seq_shared,
 /*
  * pa_decode_default_partition — split-context partition size (tokens) the
  * library would pick for this shape on the current device: 0 (no split) when
- * one workgroup per (sequence, kv head) already fills the GPU, when max_ctx
- * is at most 512, or, with grouped query heads (Hq / Hkv >= 2), at most
- * 2048; else a multiple of bs. Never fails; returns 0 for invalid shapes.
+ * the unsplit workgroups already fill the GPU (8 per compute unit with one
+ * query head per kv head, 4 with grouped heads), when max_ctx is at most
+ * 512, or, with grouped query heads (Hq / Hkv >= 2), at most 2048; else a
+ * multiple of bs. Never fails; returns 0 for invalid shapes.
  */
 int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv,
                                     int32_t D, int32_t max_ctx);
