@@ -227,8 +227,8 @@ pa_status pa_check_groups(const int32_t* group_start, const int32_t* seq_shared,
 /*
  * pa_decode_default_partition — split-context partition size (tokens) the
  * library would pick for this shape on the current device: 0 (no split) when
- * the unsplit workgroups already fill the GPU (8 per compute unit with one
- * query head per kv head, 4 with grouped heads), when max_ctx is at most
+ * the unsplit workgroups already fill the GPU (at least 4 per compute
+ * unit, one per sequence and kv head or query head), when max_ctx is at most
  * 512, or, with grouped query heads (Hq / Hkv >= 2), at most 2048; else a
  * multiple of bs. Never fails; returns 0 for invalid shapes.
  */

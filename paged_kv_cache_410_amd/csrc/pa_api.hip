@@ -207,18 +207,20 @@ int32_t pa_decode_default_partition(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
   const int32_t G = Hq / Hkv;
   const int64_t units = (int64_t)B * (G >= 2 ? (int64_t)Hkv * pa::mfma_q_groups(G) : Hq);
   const int64_t cus = device_cus();
-  // Enough (sequence, head) workgroups to keep every CU busy: no split. For
-  // grouped heads (the matrix-core kernels, whose unsplit workgroups stream a
-  // whole context on 8 waves) half as many suffice, and contexts up to 2048
-  // tokens are not split at all: there the partial rows and the merge cost
-  // more than the added workgroups gain. Measured with 8 kv heads: 128
-  // sequences, lognormal lengths up to 2048, 61 us unsplit against 94 at
-  // 512-token partitions; 128 sequences of 512-4096 tokens, 201 against 212;
-  // 16 of up to 2048, 27.5 against 29.9; 16 of 2048-8192, 85.5 against 65.2
-  // (split); 48 of 2048-8192, 186 against 167 (split).
-  const bool grouped = G >= 2;
-  if (units >= (grouped ? 4 : 8) * cus || max_ctx <= 512) return 0;
-  if (grouped && max_ctx <= 2048) return 0;
+  // At least 4 unsplit (sequence, head) workgroups per CU keep every CU
+  // busy: no split. For grouped heads (the matrix-core kernels, whose
+  // unsplit workgroups stream a whole context on 8 waves) contexts up to
+  // 2048 tokens are not split at all: there the partial rows and the merge
+  // cost more than the added workgroups gain. Measured, 32 query heads:
+  // with 8 kv heads, 128 sequences of lognormal lengths up to 2048, 61 us
+  // unsplit against 94 at 512-token partitions; 128 of 512-4096 tokens, 201
+  // against 212; 16 of up to 2048, 27.5 against 29.9; 16 of 2048-8192, 85.5
+  // against 65.2 (split); 48 of 2048-8192, 186 against 167 (split). With 32
+  // kv heads, 32 sequences (1024 workgroups) of 128-2048 tokens, 95.6 against
+  // 102.5; of 512-4096, 195.7 against 200.8; 16 of 512-4096, 106.6 against
+  // 109.3.
+  if (units >= 4 * cus || max_ctx <= 512) return 0;
+  if (G >= 2 && max_ctx <= 2048) return 0;
   return 512;
 }
 

@@ -387,19 +387,19 @@ def test_decode_at_the_batch_limit(pa, dtype, Hq, Hkv, D):
 
 def test_default_partition_policy(pa):
     """The library's split choice on this device: no split when the unsplit
-    workgroups fill the GPU (8 per compute unit for one query head per kv
-    head, 4 for grouped heads on the matrix-core kernels), or the contexts
-    are short: up to 512 tokens, or up to 2048 with grouped heads; else
-    512-token partitions."""
+    workgroups fill the GPU (at least 4 per compute unit), or the contexts
+    are short: up to 512 tokens, or up to 2048 with grouped heads (the
+    matrix-core kernels); else 512-token partitions."""
     say("[default partition]")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert pa.default_partition(8 * cus, 8, 8, 128, 32768) == 0        # enough workgroups
+    assert pa.default_partition(cus // 2, 8, 8, 128, 32768) == 0       # enough workgroups
     assert pa.default_partition(4, 8, 8, 128, 512) == 0                # short contexts
-    assert pa.default_partition(26, 40, 40, 128, 560) == 512           # one head per kv head
+    assert pa.default_partition(4, 40, 40, 128, 560) == 512            # one head per kv head
     assert pa.default_partition(128, 40, 8, 128, 2048) == 0            # grouped, short
     assert pa.default_partition(16, 32, 8, 64, 2048) == 0
     assert pa.default_partition(16, 32, 8, 128, 2049) == 512           # grouped, long
     assert pa.default_partition(16, 64, 8, 128, 32768) == 512
     assert pa.default_partition(cus // 2, 32, 8, 128, 8192) == 0       # grouped, 4 per CU
     assert pa.default_partition(cus // 2 - 1, 32, 8, 128, 8192) == 512
-    assert pa.default_partition(cus // 8, 32, 32, 128, 8192) == 512    # one head per kv head
+    assert pa.default_partition(cus // 8, 32, 32, 128, 8192) == 0      # 4 per CU
+    assert pa.default_partition(cus // 16, 32, 32, 128, 8192) == 512
