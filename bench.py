@@ -188,7 +188,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="13b",
                     choices=["tiny", "7b", "13b", "gqa", "gqa_d64", "gqa_f32", "cow", "cow_gqa8",
-                             "prefix", "13b_verify4", "gqa_chunk512", "gqa_chunk512_d64"])
+                             "prefix", "13b_verify4", "gqa_chunk512", "gqa_chunk512_d64",
+                             "gqa_short"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-context partition in tokens (default: the library's choice, "
                          "or the workload's own)")

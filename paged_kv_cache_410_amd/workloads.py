@@ -32,6 +32,9 @@ Workloads (lengths, seeds and draw order are fixed here):
         U[1024, 8192] whose last 512 tokens are the step's chunk (a prompt
         processed in 512-token chunks).                             seed 6
   gqa_chunk512_d64  the same recipe at head_dim 64.                 seed 11
+  gqa_short  bf16, 128 seqs, 32 q heads / 8 kv heads, head_dim 128, the 13b
+        length mix (a grouped-head layer at short contexts; no split at
+        the library's default partition).                           seed 12
 
 Draw order for a seed: lengths -> free-list permutation -> q -> K pool ->
 V pool -> new K -> new V. Values are N(0, 1) in fp32, rounded to the
@@ -111,6 +114,10 @@ CONFIGS = {
     # 128-byte rows)
     "gqa_chunk512_d64": Spec("gqa_chunk512_d64", "bf16", 16, 64, 8, 64, seed=11,
                              lengths=("uniform", 1024, 8192), chunk=("uniform", 512, 512)),
+    # a grouped-head layer (4 query heads per kv head) over the 13b length mix:
+    # a study workload for short contexts on the matrix-core decode kernel
+    "gqa_short": Spec("gqa_short", "bf16", 128, 32, 8, 128, seed=12,
+                      lengths=("lognormal", 500.0, 0.7, 16, 2048)),
 }
 
 

@@ -60,7 +60,7 @@ def run_step(pa, name):
 
 
 @pytest.mark.parametrize("name", ["7b", "13b", "gqa", "gqa_d64", "gqa_f32", "cow", "prefix",
-                                  "13b_verify4"])
+                                  "13b_verify4", "gqa_short"])
 def test_full_config_whole_output(pa, name):
     st, out = run_step(pa, name)
     say(f"    oracle over the whole output {tuple(out.shape)}")
